@@ -1,0 +1,266 @@
+"""Decode-step benchmark on one MI355X.
+
+One step = slot mapping, then for each of L layers the KV store and the
+split-KV paged decode attention (partial + reduce), then the sampler over
+the logits.  Default workload: the Qwen3-0.6B-shaped decode (64 rows,
+contexts uniform in [128, 4096], GQA 16/8, head_dim 128, block 256,
+28 layers, vocab 151936, T 0.8, top-p 0.95), synthetic seeded inputs
+resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is the paged decode-attention throughput in
+GB/s of algorithmic bytes (each cached K/V element once + Q + O, per layer)
+over the measured time of the attention kernels; decode steps/s and
+sampler tokens/s ride along.  `roofline` covers the dominant kernel (the
+attention partial step) with per-launch HIP-event timing; `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3")
+    ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = automatic)")
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (0 = workload's)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="also run a device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import paged_kv_decode_store_amd as pkv
+    from workloads import config_by_name, host_inputs
+    from workloads.device import device_pool
+    from workloads.generate import sampling_params
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    pkv.lib()  # fail loudly if the HIP library is missing
+
+    cfg = config_by_name(args.config)
+    L = args.layers or cfg.num_layers
+    B, Hq, Hkv, D, bs = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    log(f"[bench] workload {cfg.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} bs={bs} L={L} V={cfg.vocab}")
+
+    inp = host_inputs(cfg, layers=range(L), pools=False, sampler=True)
+    n, tables = inp.context_lens, inp.block_tables
+    dev = torch.device("cuda")
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    nd, td = i32(n), i32(tables)
+    q = [bf16(x) for x in inp.q]
+    kn = [bf16(x) for x in inp.k_new]
+    vn = [bf16(x) for x in inp.v_new]
+    kp, vp = [], []
+    for layer in range(L):
+        kp.append(device_pool(cfg, inp.num_blocks, "kpool", layer))
+        vp.append(device_pool(cfg, inp.num_blocks, "vpool", layer))
+    logits = torch.from_numpy(inp.logits).to(dev)
+    gumbel = torch.from_numpy(inp.gumbel).to(dev)
+    t, p, k = (torch.from_numpy(x).to(dev) for x in sampling_params(cfg))
+    flags = (pkv.PKV_SAMPLE_TOPK if cfg.top_k > 0 else 0) | (pkv.PKV_SAMPLE_TOPP if cfg.top_p < 1 else 0)
+    max_len = int(n.max())
+    split = pkv.decode_split_tokens(B, Hkv, max_len, args.split)
+    ws = torch.empty(pkv.decode_workspace_bytes(B, Hq, Hkv, D, max_len, split), dtype=torch.uint8,
+                     device=dev)
+    sws = torch.empty(pkv.sampler_workspace_bytes(B, cfg.vocab), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    slots = torch.empty(B, dtype=torch.int32, device=dev)
+    ids = torch.empty(B, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident: {sum(x.numel() * 2 for x in kp + vp) / 1e9:.2f} GB of pools, "
+        f"split_tokens={split}")
+
+    def step(ev=None):
+        pkv.slot_mapping(td, nd, bs, out=slots)
+        for layer in range(L):
+            pkv.kv_store(kp[layer], vp[layer], kn[layer], vn[layer], slots)
+            if ev is not None:
+                ev["p0"][layer].record()
+            pkv.decode_attention_partial(q[layer], kp[layer], vp[layer], td, nd, max_len, ws,
+                                         split_tokens=split)
+            if ev is not None:
+                ev["p1"][layer].record()
+            pkv.decode_attention_reduce(out, nd, Hkv, tables.shape[1], bs, max_len, ws,
+                                        split_tokens=split)
+            if ev is not None:
+                ev["r1"][layer].record()
+        if ev is not None:
+            ev["s0"].record()
+        pkv.sample_next_token(logits, gumbel, t, p, k, flags=flags, out=ids, workspace=sws)
+        if ev is not None:
+            ev["s1"].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    def new_events():
+        E = lambda: torch.cuda.Event(enable_timing=True)
+        return {"p0": [E() for _ in range(L)], "p1": [E() for _ in range(L)],
+                "r1": [E() for _ in range(L)], "s0": E(), "s1": E()}
+
+    # timed region: K whole steps, per-kernel events recorded on the same stream
+    evs = [new_events() for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    part_ms = [e["p0"][l].elapsed_time(e["p1"][l]) for e in evs for l in range(L)]
+    red_ms = [e["p1"][l].elapsed_time(e["r1"][l]) for e in evs for l in range(L)]
+    samp_ms = [e["s0"].elapsed_time(e["s1"]) for e in evs]
+    log(f"[bench] timed {args.steps} steps in {total_ms:.2f} ms")
+
+    # algorithmic bytes
+    kv_bytes = int(n.astype(np.int64).sum()) * Hkv * D * 2 * 2   # K and V, each element once
+    q_bytes = B * Hq * D * 2
+    o_bytes = B * Hq * D * 2
+    attn_bytes_layer = kv_bytes + q_bytes + o_bytes
+    part_avg_us = 1e3 * float(np.mean(part_ms))
+    red_avg_us = 1e3 * float(np.mean(red_ms))
+    attn_us_layer = part_avg_us + red_avg_us
+    value = attn_bytes_layer / (attn_us_layer * 1e-6) / 1e9
+    part_gbs = (kv_bytes + q_bytes) / (part_avg_us * 1e-6) / 1e9
+    ms_per_step = total_ms / args.steps
+    samp_avg_us = 1e3 * float(np.mean(samp_ms))
+
+    traffic = read_traffic(cfg.name)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(cfg, inp, kp[0], vp[0], args.cpu_seconds, kv_bytes + q_bytes + o_bytes)
+
+    if args.calibrate_copy > 0:
+        nbytes = args.calibrate_copy << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nbytes} bytes done")
+
+    res = {
+        "metric": "paged decode-attn HBM GB/s (% of peak) + decode steps/s; sampler tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Qwen3-0.6B-shaped paged decode step"
+                   if cfg.name == "qwen3" else cfg.name,
+                   "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "block_size": bs, "layers": L, "vocab": cfg.vocab,
+                   "context_tokens": int(n.sum()), "split_tokens": split,
+                   "temperature": cfg.temperature, "top_p": cfg.top_p, "top_k": cfg.top_k},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_steps_per_s": round(1e3 / ms_per_step, 2),
+        "sampler_tokens_per_s": round(B / (samp_avg_us * 1e-6), 1),
+        "attention_us_per_layer": {"partial": round(part_avg_us, 3), "reduce": round(red_avg_us, 3)},
+        "sampler_us": round(samp_avg_us, 3),
+        "roofline": {"kernel": "decode_partial_kernel<128,2>" if cfg.name == "qwen3" else "decode_partial_kernel",
+                     "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": kv_bytes + q_bytes,
+                     "avg_launch_us": round(part_avg_us, 3),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def read_traffic(name):
+    """Measured HBM bytes per launch of the partial kernel, from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"decode_partial_{name}_counters.txt")
+    src = os.path.join(ROOT, "paged_kv_decode_store_amd", "csrc", "decode_attention.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("kernel_source_sha256_16") != sha or "traffic_bytes_per_launch" not in kv:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
+def cpu_baseline(cfg, inp, kpool, vpool, seconds, layer_bytes):
+    """The oracle as it stands, single-threaded on the host: attention of
+    layer 0 over whole rows (after copying the pools back), repeated until
+    about `seconds` of CPU time, expressed in the same GB/s unit."""
+    import oracle
+    import torch
+
+    kh = kpool.view(torch.int16).cpu().numpy().view(np.uint16)
+    vh = vpool.view(torch.int16).cpu().numpy().view(np.uint16)
+    n, t = inp.context_lens, inp.block_tables
+    q = inp.q[0]
+    rows, done_bytes, elapsed = 0, 0, 0.0
+    per_row = n.astype(np.int64) * cfg.num_kv_heads * cfg.head_dim * 4 + 4 * cfg.num_q_heads * cfg.head_dim
+    t0 = time.perf_counter()
+    b = 0
+    while elapsed < seconds:
+        oracle.decode_attention(q[b:b + 1], kh, vh, t[b:b + 1], n[b:b + 1])
+        done_bytes += int(per_row[b])
+        rows += 1
+        b = (b + 1) % cfg.batch
+        elapsed = time.perf_counter() - t0
+    log(f"[bench] cpu oracle: {rows} rows in {elapsed:.1f} s")
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"layer 0 attention of {rows} rows (cycling over the {cfg.batch} rows, "
+                      f"fp64 two-pass softmax), {elapsed:.1f} s single-threaded"}
+
+
+if __name__ == "__main__":
+    main()

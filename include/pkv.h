@@ -1,0 +1,199 @@
+/*
+ * pkv.h - C ABI of libpkv.so, the paged-KV decode step for AMD MI355X
+ * (gfx950): slot mapping, KV store, split-KV paged GQA decode attention and
+ * the next-token sampler.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers unless stated; the caller owns every
+ *     buffer (pools, inputs, outputs, workspaces).  The library never
+ *     allocates, frees or synchronises: each call only enqueues kernels on
+ *     `stream` (NULL = the default stream) and returns.  Calls on one stream
+ *     run in order, which gives the required store-before-attend order.
+ *   - bf16 tensors are passed as raw 16-bit storage; they must be 16-byte
+ *     aligned, and so must every row start implied by a stride.
+ *   - Paged pool layout (one layer's K or V):
+ *         [num_blocks][block_size][num_kv_heads][head_dim]   bf16
+ *     i.e. the per-layer view of the nano-vllm pool (page "Model Runner",
+ *     section "allocated kv cache").  A flat slot s addresses token row
+ *     (s / block_size, s % block_size).
+ *   - Return value: PKV_OK, or a negative pkv_status.  Argument errors are
+ *     detected on the host before any HIP call and nothing is enqueued.
+ *     PKV_ERR_HIP means a launch failed; pkv_last_error() has the text.
+ *   - Device-side contents (slots, block ids, lengths) are a caller
+ *     contract.  Kernels never access memory outside the buffers described
+ *     by the size arguments: out-of-range slots are skipped, out-of-range
+ *     block ids read block 0, over-long rows are truncated; results for such
+ *     rows are unspecified.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or stride */
+    PKV_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim) */
+    PKV_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+    PKV_ERR_HIP = -4          /* a HIP launch failed */
+} pkv_status;
+
+/* Static text for a status code. */
+const char *pkv_status_string(int status);
+
+/* Text of the last failure on the calling host thread ("" if none). */
+const char *pkv_last_error(void);
+
+/* ---- slot mapping ---------------------------------------------------------
+ * Decode-step slot of each row's new token (nano-vllm "Model Runner" page,
+ * sections "allocated kv cache" and "prefill and decode"): a row whose
+ * context holds n tokens (the new one included) writes position pos = n - 1
+ * at
+ *     slot = block_tables[b][pos / block_size] * block_size + pos % block_size
+ * slot_mapping     int32 [batch]                      (out)
+ * block_tables     int32 [batch][block_table_stride]  physical block ids
+ * context_lens     int32 [batch]                      n per row
+ * n <= 0, a logical block beyond the table, or a negative table entry gives
+ * slot -1 (the store then skips the row).  block_size: power of two >= 1. */
+int pkv_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
+                     int32_t block_table_stride, const int32_t *context_lens,
+                     int32_t batch, int32_t block_size, hipStream_t stream);
+
+/* ---- KV store -------------------------------------------------------------
+ * Writes each token's new K and V head rows into the paged pools at its
+ * slot, in place (nano-vllm page, section "prepare Prefill": the attention
+ * path writes the new K/V at slot_mapping; nanochat engine page, section 2:
+ * the cache is updated in place).  A bit copy.
+ * k_cache, v_cache bf16 pools (layout above), num_blocks blocks each
+ * k_new, v_new     bf16 [num_tokens][num_kv_heads][head_dim] rows; row t
+ *                  starts at element t * new_token_stride (0 = packed)
+ * slot_mapping     int32 [num_tokens]; slot < 0 or >= num_blocks*block_size
+ *                  skips the token.  Slots of one call must be distinct.
+ * head_dim: multiple of 8, <= 256.  block_size: power of two in [16, 4096]. */
+int pkv_kv_store(void *k_cache, void *v_cache, const void *k_new,
+                 const void *v_new, const int32_t *slot_mapping,
+                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                 int64_t new_token_stride, int32_t block_size,
+                 int64_t num_blocks, hipStream_t stream);
+
+/* ---- paged decode attention ----------------------------------------------
+ * Single-query GQA attention of each row over its own n_b cached positions,
+ * gathered through its block table (Grok-1 runners chapter, sections 8.2.3
+ * and 8.5: one new token attends over all cached K/V, 48 query heads share 8
+ * KV heads; nano-vllm page, "prefill and decode": n_b includes the new
+ * token, which must already be stored).  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads).  For each (b, h):
+ *     o = sum_j softmax_j(scale * q . K_j) V_j,   j = 0 .. n_b - 1
+ * and n_b == 0 (an inactive row, chapter 8.2.3) gives o = 0.
+ *
+ * The work is split: positions [s*split_tokens, (s+1)*split_tokens) of each
+ * (row, KV head) form one partial (running max, sum and unnormalised
+ * output, fp32, in the workspace); the reduce step merges a row's partials
+ * with weights exp(m_s - M).  pkv_paged_decode_attention runs both steps;
+ * the two steps are also exported separately.
+ *
+ * out            bf16 [batch][num_q_heads][head_dim], row b at b*out_stride
+ * q              bf16 [batch][num_q_heads][head_dim], row b at b*q_stride
+ *                (strides in elements; 0 = packed)
+ * k_cache,v_cache bf16 pools, num_blocks blocks
+ * block_tables   int32 [batch][block_table_stride]
+ * context_lens   int32 [batch]; each must be <= max_context_len
+ * head_dim       64 or 128;  block_size power of two in [16, 4096]
+ * scale          softmax scale; <= 0 selects 1/sqrt(head_dim)
+ * split_tokens   positions per partial: 0 = automatic, else a multiple of
+ *                64 (see pkv_decode_split_tokens)
+ * workspace      device scratch of at least pkv_decode_workspace_bytes(...)
+ *                bytes, 256-byte aligned; contents on entry are ignored. */
+int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_kv_heads,
+                                int32_t max_context_len, int32_t split_tokens);
+
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_context_len,
+                                  int32_t split_tokens);
+
+int pkv_paged_decode_attention(void *out, int64_t out_stride, const void *q,
+                               int64_t q_stride, const void *k_cache,
+                               const void *v_cache,
+                               const int32_t *block_tables,
+                               int32_t block_table_stride,
+                               const int32_t *context_lens, int32_t batch,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_context_len,
+                               float scale, int32_t split_tokens,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Partial step only: fills the workspace. */
+int pkv_decode_attention_partial(const void *q, int64_t q_stride,
+                                 const void *k_cache, const void *v_cache,
+                                 const int32_t *block_tables,
+                                 int32_t block_table_stride,
+                                 const int32_t *context_lens, int32_t batch,
+                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, int32_t max_context_len,
+                                 float scale, int32_t split_tokens,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Reduce step only: reads a workspace filled by the partial step with the
+ * same shape arguments and writes out. */
+int pkv_decode_attention_reduce(void *out, int64_t out_stride,
+                                const int32_t *context_lens, int32_t batch,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_table_stride,
+                                int32_t block_size, int32_t max_context_len,
+                                int32_t split_tokens, const void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* ---- sampler --------------------------------------------------------------
+ * Next token per row (Grok-1 runners chapter, section 8.3 and 8.3.1;
+ * nanochat engine page, section 3; nano-vllm page, "run model"):
+ *   temperature <= 0 (or NaN): greedy, the lowest index of max logits.
+ *   otherwise, in this order:
+ *     s_i = logits_i / T                      (IEEE fp32 division)
+ *     top-k  if 0 < k < vocab: keep the k largest s, ties to lower index
+ *     top-p  if p < 1: over the kept set, keep every s_i >= tau where tau is
+ *            the smallest value whose strictly-greater mass is <= p of the
+ *            kept mass (the ascending-cumsum rule of the page, exact
+ *            arithmetic); p <= 0 keeps only the maxima
+ *     id = argmax over kept i of fl32(s_i + gumbel_i), ties to lower index
+ * The Gumbel noise is an input (standard Gumbel, fp32), so the draw is
+ * reproducible.  Only the ids are written.
+ * out_ids      int32 [batch]
+ * logits       fp32 [batch][vocab], row b at b*logits_stride (elements)
+ * gumbel       fp32 [batch][vocab], row b at b*gumbel_stride; only read
+ *              where a token is eligible (unused for greedy rows)
+ * temperature, top_p  fp32 [batch];  top_k  int32 [batch]
+ * flags        which filters ANY row may use: PKV_SAMPLE_TOPK and/or
+ *              PKV_SAMPLE_TOPP.  A filter whose flag is clear is off for
+ *              every row whatever its per-row value (its passes are not
+ *              launched).
+ * vocab        1 .. 2^24
+ * workspace    >= pkv_sampler_workspace_bytes(batch, vocab), 256-B aligned */
+#define PKV_SAMPLE_TOPK 1u
+#define PKV_SAMPLE_TOPP 2u
+
+size_t pkv_sampler_workspace_bytes(int32_t batch, int32_t vocab);
+
+int pkv_sample_next_token(int32_t *out_ids, const float *logits,
+                          int64_t logits_stride, const float *gumbel,
+                          int64_t gumbel_stride, const float *temperature,
+                          const float *top_p, const int32_t *top_k,
+                          int32_t batch, int32_t vocab, uint32_t flags,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

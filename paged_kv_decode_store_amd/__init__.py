@@ -1,0 +1,183 @@
+"""paged_kv_decode_store_amd - MI355X-native paged-KV decode step.
+
+A thin Python binding over libpkv.so (include/pkv.h).  Each function checks
+tensor dtypes/devices, passes raw device pointers and the current HIP stream
+to the C ABI, and raises on a non-zero status.  Every step of the path runs
+in the library's HIP kernels; PyTorch only provides device memory and the
+stream.  There is no CPU fallback: importing the package does not need a
+GPU, but every call does.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import PKV_SAMPLE_TOPK, PKV_SAMPLE_TOPP, PkvError, check, lib
+
+__all__ = [
+    "slot_mapping", "kv_store", "paged_decode_attention", "decode_attention_partial",
+    "decode_attention_reduce", "decode_workspace_bytes", "decode_split_tokens",
+    "sample_next_token", "sampler_workspace_bytes", "PkvError",
+    "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
+]
+
+
+def _stream():
+    return ctypes_ptr(torch.cuda.current_stream().cuda_stream)
+
+
+def ctypes_ptr(x: int):
+    return None if x == 0 else x
+
+
+def _dev(t: torch.Tensor, name: str, dtype) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _packed(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def slot_mapping(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int32 [B] slot of each row's new token (position context_len - 1)."""
+    B = context_lens.shape[0]
+    _packed(block_tables, "block_tables")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=context_lens.device)
+    check(lib().pkv_slot_mapping(_dev(out, "out", torch.int32),
+                                 _dev(block_tables, "block_tables", torch.int32),
+                                 block_tables.shape[1],
+                                 _dev(context_lens, "context_lens", torch.int32), B, block_size,
+                                 _stream()), "pkv_slot_mapping")
+    return out
+
+
+def kv_store(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+             v_new: torch.Tensor, slots: torch.Tensor) -> None:
+    """In-place store of k_new/v_new [T, Hkv, D] rows into pools
+    [NB, bs, Hkv, D] at slots [T]."""
+    nb, bs, hkv, d = k_cache.shape
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _packed(t, name)
+    assert v_cache.shape == k_cache.shape
+    T = k_new.shape[0]
+    if k_new.shape[1:] != (hkv, d) or v_new.shape[1:] != (hkv, d):
+        raise ValueError("k_new/v_new must be [T, Hkv, D] matching the pools")
+    if k_new.stride(1) != d or k_new.stride(2) != 1 or v_new.stride() != k_new.stride():
+        raise ValueError("k_new/v_new rows must be packed [Hkv, D] with equal strides")
+    check(lib().pkv_kv_store(_dev(k_cache, "k_cache", torch.bfloat16),
+                             _dev(v_cache, "v_cache", torch.bfloat16),
+                             _dev(k_new, "k_new", torch.bfloat16),
+                             _dev(v_new, "v_new", torch.bfloat16),
+                             _dev(slots, "slots", torch.int32), T, hkv, d, k_new.stride(0), bs, nb,
+                             _stream()), "pkv_kv_store")
+
+
+def decode_split_tokens(batch: int, num_kv_heads: int, max_context_len: int,
+                        split_tokens: int = 0) -> int:
+    return int(lib().pkv_decode_split_tokens(batch, num_kv_heads, max_context_len, split_tokens))
+
+
+def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_context_len: int, split_tokens: int = 0) -> int:
+    return int(lib().pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, split_tokens))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise TypeError("workspace must be a uint8 GPU tensor")
+    return workspace
+
+
+def _attn_shapes(q, k_cache, block_tables):
+    B, Hq, D = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != D:
+        raise ValueError("q and cache head_dim differ")
+    if q.stride(2) != 1 or q.stride(1) != D:
+        raise ValueError("q rows must be packed [Hq, D]")
+    _packed(block_tables, "block_tables")
+    return B, Hq, D, nb, bs, hkv
+
+
+def decode_attention_partial(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                             workspace, scale: float = 0.0, split_tokens: int = 0) -> None:
+    B, Hq, D, nb, bs, hkv = _attn_shapes(q, k_cache, block_tables)
+    check(lib().pkv_decode_attention_partial(
+        _dev(q, "q", torch.bfloat16), q.stride(0), _dev(k_cache, "k_cache", torch.bfloat16),
+        _dev(v_cache, "v_cache", torch.bfloat16), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs,
+        nb, max_context_len, scale, split_tokens, _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream()), "pkv_decode_attention_partial")
+
+
+def decode_attention_reduce(out, context_lens, num_kv_heads, block_table_stride, block_size,
+                            max_context_len, workspace, split_tokens: int = 0) -> None:
+    B, Hq, D = out.shape
+    if out.stride(2) != 1 or out.stride(1) != D:
+        raise ValueError("out rows must be packed [Hq, D]")
+    check(lib().pkv_decode_attention_reduce(
+        _dev(out, "out", torch.bfloat16), out.stride(0),
+        _dev(context_lens, "context_lens", torch.int32), B, Hq, num_kv_heads, D,
+        block_table_stride, block_size, max_context_len, split_tokens,
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream()),
+        "pkv_decode_attention_reduce")
+
+
+def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, scale: float = 0.0, split_tokens: int = 0,
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [B, Hq, D] attention of each row's query over its n_b cached
+    positions (context_lens, new token included)."""
+    B, Hq, D, nb, bs, hkv = _attn_shapes(q, k_cache, block_tables)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    ws = _workspace(decode_workspace_bytes(B, Hq, hkv, D, max_context_len, split_tokens),
+                    q.device, workspace)
+    check(lib().pkv_paged_decode_attention(
+        _dev(out, "out", torch.bfloat16), out.stride(0), _dev(q, "q", torch.bfloat16), q.stride(0),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs, nb, max_context_len,
+        scale, split_tokens, ws.data_ptr(), ws.numel(), _stream()), "pkv_paged_decode_attention")
+    return out
+
+
+def sampler_workspace_bytes(batch: int, vocab: int) -> int:
+    return int(lib().pkv_sampler_workspace_bytes(batch, vocab))
+
+
+def sample_next_token(logits: torch.Tensor, gumbel: torch.Tensor, temperature: torch.Tensor,
+                      top_p: torch.Tensor, top_k: torch.Tensor, flags: Optional[int] = None,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int32 [B] next-token ids.  flags: which filters any row may use
+    (PKV_SAMPLE_TOPK | PKV_SAMPLE_TOPP); None enables both."""
+    B, V = logits.shape
+    if logits.stride(1) != 1 or gumbel.stride(1) != 1 or gumbel.shape != logits.shape:
+        raise ValueError("logits/gumbel must be [B, V] with unit element stride")
+    if flags is None:
+        flags = PKV_SAMPLE_TOPK | PKV_SAMPLE_TOPP
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    ws = _workspace(sampler_workspace_bytes(B, V), logits.device, workspace)
+    check(lib().pkv_sample_next_token(
+        _dev(out, "out", torch.int32), _dev(logits, "logits", torch.float32), logits.stride(0),
+        _dev(gumbel, "gumbel", torch.float32), gumbel.stride(0),
+        _dev(temperature, "temperature", torch.float32), _dev(top_p, "top_p", torch.float32),
+        _dev(top_k, "top_k", torch.int32), B, V, flags, ws.data_ptr(), ws.numel(), _stream()),
+        "pkv_sample_next_token")
+    return out

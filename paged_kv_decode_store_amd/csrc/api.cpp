@@ -1,0 +1,333 @@
+// C ABI entry points of libpkv.so: host-side argument checks, then the
+// launchers.  Every check runs before any HIP call, so argument errors are
+// reported without touching the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/pkv.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return PKV_OK;
+    return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+#define REQUIRE(cond, status, ...)                  \
+    do {                                            \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+int check_split(int32_t split_tokens)
+{
+    REQUIRE(split_tokens >= 0 && split_tokens % 64 == 0 && split_tokens <= (1 << 24),
+            PKV_ERR_INVALID_ARG, "split_tokens must be 0 or a positive multiple of 64");
+    return PKV_OK;
+}
+
+// Shape checks shared by the attention entry points.
+int check_attention_shape(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t block_table_stride,
+                          int32_t max_context_len)
+{
+    REQUIRE(batch >= 0, PKV_ERR_INVALID_ARG, "batch must be >= 0");
+    REQUIRE(num_q_heads > 0 && num_kv_heads > 0, PKV_ERR_INVALID_ARG, "head counts must be > 0");
+    REQUIRE(num_q_heads % num_kv_heads == 0, PKV_ERR_INVALID_ARG,
+            "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", num_q_heads, num_kv_heads);
+    REQUIRE(head_dim == 64 || head_dim == 128, PKV_ERR_UNSUPPORTED,
+            "head_dim %d unsupported (64 or 128)", head_dim);
+    REQUIRE(pow2(block_size) && block_size >= 16 && block_size <= 4096, PKV_ERR_UNSUPPORTED,
+            "block_size %d unsupported (power of two in [16, 4096])", block_size);
+    REQUIRE(block_table_stride > 0, PKV_ERR_INVALID_ARG, "block_table_stride must be > 0");
+    REQUIRE(max_context_len >= 0, PKV_ERR_INVALID_ARG, "max_context_len must be >= 0");
+    return PKV_OK;
+}
+
+// Largest divisor of the group size that is <= 8: query heads per workgroup.
+int32_t heads_per_chunk(int32_t group)
+{
+    for (int g = 8; g >= 1; --g)
+        if (group % g == 0) return g;
+    return 1;
+}
+
+int32_t effective_split(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
+                        int32_t split_tokens)
+{
+    return split_tokens > 0 ? split_tokens
+                            : pkv::auto_split_tokens(batch, num_kv_heads, max_context_len);
+}
+
+int32_t clamp_len(int32_t max_context_len, int32_t block_table_stride, int32_t block_size)
+{
+    const int64_t cap = (int64_t)block_table_stride * block_size;
+    return (int32_t)(max_context_len < cap ? max_context_len : cap);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(int status)
+{
+    switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char *pkv_last_error(void) { return g_last_error; }
+
+int pkv_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
+                     int32_t block_table_stride, const int32_t *context_lens, int32_t batch,
+                     int32_t block_size, hipStream_t stream)
+{
+    REQUIRE(batch >= 0, PKV_ERR_INVALID_ARG, "batch must be >= 0");
+    if (batch == 0) return PKV_OK;
+    REQUIRE(slot_mapping && block_tables && context_lens, PKV_ERR_INVALID_ARG, "null pointer");
+    REQUIRE(aligned(slot_mapping, 4) && aligned(block_tables, 4) && aligned(context_lens, 4),
+            PKV_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+    REQUIRE(block_table_stride > 0, PKV_ERR_INVALID_ARG, "block_table_stride must be > 0");
+    REQUIRE(pow2(block_size) && block_size <= (1 << 20), PKV_ERR_UNSUPPORTED,
+            "block_size %d must be a power of two", block_size);
+    return hip_status(pkv::launch_slot_mapping(slot_mapping, block_tables, block_table_stride,
+                                               context_lens, batch, block_size, stream),
+                      "slot_mapping launch");
+}
+
+int pkv_kv_store(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+                 const int32_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                 int32_t head_dim, int64_t new_token_stride, int32_t block_size,
+                 int64_t num_blocks, hipStream_t stream)
+{
+    REQUIRE(num_tokens >= 0, PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    REQUIRE(num_kv_heads > 0, PKV_ERR_INVALID_ARG, "num_kv_heads must be > 0");
+    REQUIRE(head_dim > 0 && head_dim % 8 == 0 && head_dim <= 256, PKV_ERR_UNSUPPORTED,
+            "head_dim %d unsupported (multiple of 8, <= 256)", head_dim);
+    REQUIRE(pow2(block_size) && block_size >= 16 && block_size <= 4096, PKV_ERR_UNSUPPORTED,
+            "block_size %d unsupported (power of two in [16, 4096])", block_size);
+    REQUIRE(num_blocks > 0, PKV_ERR_INVALID_ARG, "num_blocks must be > 0");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    const int64_t stride = new_token_stride ? new_token_stride : row;
+    REQUIRE(stride >= row && stride % 8 == 0, PKV_ERR_INVALID_ARG,
+            "new_token_stride %lld must be >= %lld and a multiple of 8",
+            (long long)new_token_stride, (long long)row);
+    if (num_tokens == 0) return PKV_OK;
+    REQUIRE(k_cache && v_cache && k_new && v_new && slot_mapping, PKV_ERR_INVALID_ARG,
+            "null pointer");
+    REQUIRE(aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(k_new, 16) &&
+                aligned(v_new, 16),
+            PKV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+    REQUIRE(aligned(slot_mapping, 4), PKV_ERR_INVALID_ARG, "slot_mapping must be 4-byte aligned");
+    return hip_status(pkv::launch_kv_store(static_cast<uint16_t *>(k_cache),
+                                           static_cast<uint16_t *>(v_cache),
+                                           static_cast<const uint16_t *>(k_new),
+                                           static_cast<const uint16_t *>(v_new), slot_mapping,
+                                           num_tokens, num_kv_heads, head_dim, stride,
+                                           num_blocks * block_size, stream),
+                      "kv_store launch");
+}
+
+int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
+                                int32_t split_tokens)
+{
+    if (check_split(split_tokens) != PKV_OK) return 0;
+    return effective_split(batch, num_kv_heads, max_context_len, split_tokens);
+}
+
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_context_len,
+                                  int32_t split_tokens)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || check_split(split_tokens) != PKV_OK)
+        return 0;
+    const int32_t split = effective_split(batch, num_kv_heads, max_context_len, split_tokens);
+    return pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split).total_bytes;
+}
+
+int pkv_decode_attention_partial(const void *q, int64_t q_stride, const void *k_cache,
+                                 const void *v_cache, const int32_t *block_tables,
+                                 int32_t block_table_stride, const int32_t *context_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                 int32_t max_context_len, float scale, int32_t split_tokens,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   block_table_stride, max_context_len);
+    if (rc) return rc;
+    if ((rc = check_split(split_tokens))) return rc;
+    REQUIRE(num_blocks > 0, PKV_ERR_INVALID_ARG, "num_blocks must be > 0");
+    const int64_t qs = q_stride ? q_stride : (int64_t)num_q_heads * head_dim;
+    REQUIRE(qs >= (int64_t)num_q_heads * head_dim && qs % 8 == 0, PKV_ERR_INVALID_ARG,
+            "q_stride must be >= num_q_heads*head_dim and a multiple of 8");
+    REQUIRE(isfinite(scale), PKV_ERR_INVALID_ARG, "scale must be finite");
+    if (batch == 0) return PKV_OK;
+    REQUIRE(q && k_cache && v_cache && block_tables && context_lens, PKV_ERR_INVALID_ARG,
+            "null pointer");
+    REQUIRE(aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16), PKV_ERR_INVALID_ARG,
+            "bf16 tensors must be 16-byte aligned");
+    REQUIRE(aligned(block_tables, 4) && aligned(context_lens, 4), PKV_ERR_INVALID_ARG,
+            "int32 arrays must be 4-byte aligned");
+    const int32_t split = effective_split(batch, num_kv_heads, max_context_len, split_tokens);
+    const pkv::SplitGeometry g =
+        pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split);
+    REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,
+            "workspace must be non-null and 256-byte aligned");
+    REQUIRE(workspace_bytes >= g.total_bytes, PKV_ERR_WORKSPACE,
+            "workspace too small: %zu < %zu bytes", workspace_bytes, g.total_bytes);
+
+    pkv::PartialArgs a;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + g.part_o_bytes);
+    a.q = static_cast<const uint16_t *>(q);
+    a.q_stride = qs;
+    a.k_cache = static_cast<const uint16_t *>(k_cache);
+    a.v_cache = static_cast<const uint16_t *>(v_cache);
+    a.block_tables = block_tables;
+    a.table_stride = block_table_stride;
+    a.context_lens = context_lens;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.head_chunks = a.group / heads_per_chunk(a.group);
+    a.bs_log2 = __builtin_ctz((unsigned)block_size);
+    a.num_blocks = num_blocks;
+    a.max_len = clamp_len(max_context_len, block_table_stride, block_size);
+    a.split_tokens = split;
+    a.num_splits = g.num_splits;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
+    a.c = sc * 1.4426950408889634f;
+    return hip_status(pkv::launch_decode_partial(a, head_dim, stream), "decode partial launch");
+}
+
+int pkv_decode_attention_reduce(void *out, int64_t out_stride, const int32_t *context_lens,
+                                int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_table_stride, int32_t block_size,
+                                int32_t max_context_len, int32_t split_tokens,
+                                const void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   block_table_stride, max_context_len);
+    if (rc) return rc;
+    if ((rc = check_split(split_tokens))) return rc;
+    const int64_t os = out_stride ? out_stride : (int64_t)num_q_heads * head_dim;
+    REQUIRE(os >= (int64_t)num_q_heads * head_dim && os % 8 == 0, PKV_ERR_INVALID_ARG,
+            "out_stride must be >= num_q_heads*head_dim and a multiple of 8");
+    if (batch == 0) return PKV_OK;
+    REQUIRE(out && context_lens, PKV_ERR_INVALID_ARG, "null pointer");
+    REQUIRE(aligned(out, 16), PKV_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    REQUIRE(aligned(context_lens, 4), PKV_ERR_INVALID_ARG, "context_lens must be 4-byte aligned");
+    const int32_t split = effective_split(batch, num_kv_heads, max_context_len, split_tokens);
+    const pkv::SplitGeometry g =
+        pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split);
+    REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,
+            "workspace must be non-null and 256-byte aligned");
+    REQUIRE(workspace_bytes >= g.total_bytes, PKV_ERR_WORKSPACE,
+            "workspace too small: %zu < %zu bytes", workspace_bytes, g.total_bytes);
+    pkv::ReduceArgs a;
+    a.out = static_cast<uint16_t *>(out);
+    a.out_stride = os;
+    a.part_o = static_cast<const float *>(workspace);
+    a.part_ml = reinterpret_cast<const float *>(static_cast<const char *>(workspace) +
+                                                g.part_o_bytes);
+    a.context_lens = context_lens;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.max_len = clamp_len(max_context_len, block_table_stride, block_size);
+    a.split_tokens = split;
+    a.num_splits = g.num_splits;
+    return hip_status(pkv::launch_decode_reduce(a, head_dim, stream), "decode reduce launch");
+}
+
+int pkv_paged_decode_attention(void *out, int64_t out_stride, const void *q, int64_t q_stride,
+                               const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, int32_t block_table_stride,
+                               const int32_t *context_lens, int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_context_len, float scale,
+                               int32_t split_tokens, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream)
+{
+    // validate the reduce's own arguments first so that nothing is enqueued
+    // when either step would be refused
+    const int64_t os = out_stride ? out_stride : (int64_t)num_q_heads * head_dim;
+    if (batch > 0) {
+        REQUIRE(out && aligned(out, 16), PKV_ERR_INVALID_ARG,
+                "out must be non-null and 16-byte aligned");
+    }
+    REQUIRE(num_q_heads > 0 && (os >= (int64_t)num_q_heads * head_dim) && os % 8 == 0,
+            PKV_ERR_INVALID_ARG, "out_stride must be >= num_q_heads*head_dim and a multiple of 8");
+    int rc = pkv_decode_attention_partial(q, q_stride, k_cache, v_cache, block_tables,
+                                          block_table_stride, context_lens, batch, num_q_heads,
+                                          num_kv_heads, head_dim, block_size, num_blocks,
+                                          max_context_len, scale, split_tokens, workspace,
+                                          workspace_bytes, stream);
+    if (rc) return rc;
+    return pkv_decode_attention_reduce(out, out_stride, context_lens, batch, num_q_heads,
+                                       num_kv_heads, head_dim, block_table_stride, block_size,
+                                       max_context_len, split_tokens, workspace, workspace_bytes,
+                                       stream);
+}
+
+size_t pkv_sampler_workspace_bytes(int32_t batch, int32_t vocab)
+{
+    if (batch < 0 || vocab <= 0 || vocab > (1 << 24)) return 0;
+    return pkv::sampler_workspace_bytes(batch, vocab);
+}
+
+int pkv_sample_next_token(int32_t *out_ids, const float *logits, int64_t logits_stride,
+                          const float *gumbel, int64_t gumbel_stride, const float *temperature,
+                          const float *top_p, const int32_t *top_k, int32_t batch, int32_t vocab,
+                          uint32_t flags, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream)
+{
+    REQUIRE(batch >= 0 && batch <= 65535, PKV_ERR_INVALID_ARG, "batch must be in [0, 65535]");
+    REQUIRE(vocab > 0 && vocab <= (1 << 24), PKV_ERR_UNSUPPORTED,
+            "vocab %d unsupported (1 .. 2^24)", vocab);
+    REQUIRE((flags & ~(PKV_SAMPLE_TOPK | PKV_SAMPLE_TOPP)) == 0, PKV_ERR_INVALID_ARG,
+            "unknown flag bits 0x%x", flags);
+    const int64_t ls = logits_stride ? logits_stride : vocab;
+    const int64_t gs = gumbel_stride ? gumbel_stride : vocab;
+    REQUIRE(ls >= vocab && gs >= vocab, PKV_ERR_INVALID_ARG, "row strides must be >= vocab");
+    if (batch == 0) return PKV_OK;
+    REQUIRE(out_ids && logits && gumbel && temperature && top_p && top_k, PKV_ERR_INVALID_ARG,
+            "null pointer");
+    REQUIRE(aligned(out_ids, 4) && aligned(logits, 4) && aligned(gumbel, 4) &&
+                aligned(temperature, 4) && aligned(top_p, 4) && aligned(top_k, 4),
+            PKV_ERR_INVALID_ARG, "arrays must be 4-byte aligned");
+    const size_t need = pkv::sampler_workspace_bytes(batch, vocab);
+    REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,
+            "workspace must be non-null and 256-byte aligned");
+    REQUIRE(workspace_bytes >= need, PKV_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes",
+            workspace_bytes, need);
+    return hip_status(pkv::launch_sampler(out_ids, logits, ls, gumbel, gs, temperature, top_p,
+                                          top_k, batch, vocab, flags, workspace, stream),
+                      "sampler launch");
+}
+
+}  // extern "C"

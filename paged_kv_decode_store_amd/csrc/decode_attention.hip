@@ -1,0 +1,322 @@
+// Split-KV paged decode attention for gfx950.
+//
+// Partial step: one workgroup per (split, row, KV head, query-head chunk).
+// Its four waves stream the split's cached positions in 16-position chunks
+// (a chunk never straddles a block because block_size is a power of two
+// >= 16).  Inside a wave, a lane group of D/8 lanes owns one position at a
+// time and each lane holds 8 of its head dims (one 16-byte load of K and one
+// of V), so every K/V byte is fetched from HBM exactly once and shared by
+// all G query heads of the KV head.  q.k uses v_dot2_f32_bf16 on the packed
+// bf16 pairs and a DPP butterfly inside the 16-lane row; each lane group
+// keeps its own online-softmax state (max, sum, 8 output dims per lane),
+// merged across groups with shuffles and across waves through LDS at the
+// end.  The partial (max in log2 units, sum, unnormalised output) goes to
+// the fp32 workspace.
+//
+// Reduce step: one wave per (row, query head) merges the row's partials,
+// O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, and writes bf16.
+#include <math.h>
+
+#include "launch.hpp"
+#include "pkv_device.hpp"
+
+namespace pkv {
+
+constexpr int kWaves = 4;                 // waves per partial workgroup
+constexpr int kChunk = 16;                // positions per wave iteration
+constexpr int kRound = kWaves * kChunk;   // positions per workgroup iteration
+
+template <int D, int G>
+__global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const PartialArgs a)
+{
+    constexpr int LPT = D / 8;        // lanes per position
+    constexpr int GPW = 64 / LPT;     // lane groups per wave
+    constexpr int U = kChunk / GPW;   // positions per lane group per iteration
+    static_assert(GPW * U == kChunk, "chunk geometry");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int gi = lane / LPT;
+    const int li = lane % LPT;
+
+    int x = blockIdx.x;
+    const int hc = x % a.head_chunks;
+    x /= a.head_chunks;
+    const int kvh = x % a.num_kv_heads;
+    x /= a.num_kv_heads;
+    const int b = x % a.batch;
+    const int s = x / a.batch;
+
+    const int n = min(max(a.context_lens[b], 0), a.max_len);
+    const int t_begin = s * a.split_tokens;
+    if (t_begin >= n) return;
+    const int t_end = min(n, t_begin + a.split_tokens);
+    const int h0 = kvh * a.group + hc * G;
+    const float c = a.c;
+
+    uint4 qv[G];
+    {
+        const uint16_t *qrow = a.q + (int64_t)b * a.q_stride + (int64_t)h0 * D + li * 8;
+#pragma unroll
+        for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const uint4 *>(qrow + h * D);
+    }
+
+    float m[G], l[G], o[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[h][d] = 0.f;
+    }
+
+    const int64_t tok_stride = (int64_t)a.num_kv_heads * D;
+    const int64_t lane_off = (int64_t)kvh * D + li * 8 + (int64_t)(gi * U) * tok_stride;
+    const int bs_mask = (1 << a.bs_log2) - 1;
+    const int32_t *table = a.block_tables + (int64_t)b * a.table_stride;
+
+    for (int t0 = t_begin + wave * kChunk; t0 < t_end; t0 += kRound) {
+        int blk = table[t0 >> a.bs_log2];
+        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+        const int64_t base =
+            (((int64_t)blk << a.bs_log2) + (t0 & bs_mask)) * tok_stride + lane_off;
+        uint4 kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            kr[u] = *reinterpret_cast<const uint4 *>(a.k_cache + base + u * tok_stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            vr[u] = *reinterpret_cast<const uint4 *>(a.v_cache + base + u * tok_stride);
+
+        const int tg = t0 + gi * U;
+        float vf[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            vf[u][0] = bf16_lo(vr[u].x);
+            vf[u][1] = bf16_hi(vr[u].x);
+            vf[u][2] = bf16_lo(vr[u].y);
+            vf[u][3] = bf16_hi(vr[u].y);
+            vf[u][4] = bf16_lo(vr[u].z);
+            vf[u][5] = bf16_hi(vr[u].z);
+            vf[u][6] = bf16_lo(vr[u].w);
+            vf[u][7] = bf16_hi(vr[u].w);
+        }
+
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float sc[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float acc = dot2_bf16(qv[h].x, kr[u].x, 0.f);
+                acc = dot2_bf16(qv[h].y, kr[u].y, acc);
+                acc = dot2_bf16(qv[h].z, kr[u].z, acc);
+                acc = dot2_bf16(qv[h].w, kr[u].w, acc);
+                acc = group_sum<LPT>(acc);
+                sc[u] = (tg + u < t_end) ? acc : -INFINITY;
+            }
+            float mx = m[h];
+#pragma unroll
+            for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u]);
+            const float ref = (mx == -INFINITY) ? 0.f : mx;
+            const float alpha = __builtin_amdgcn_exp2f((m[h] - ref) * c);
+            float p[U], psum = 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                p[u] = __builtin_amdgcn_exp2f((sc[u] - ref) * c);
+                psum += p[u];
+            }
+            l[h] = l[h] * alpha + psum;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                float acc = o[h][d] * alpha;
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc += p[u] * vf[u][d];
+                o[h][d] = acc;
+            }
+            m[h] = mx;
+        }
+    }
+
+    // merge the lane groups of this wave
+#pragma unroll
+    for (int xo = LPT; xo < 64; xo <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float m2 = __shfl_xor(m[h], xo);
+            const float l2 = __shfl_xor(l[h], xo);
+            const float mn = fmaxf(m[h], m2);
+            const float ref = (mn == -INFINITY) ? 0.f : mn;
+            const float a1 = __builtin_amdgcn_exp2f((m[h] - ref) * c);
+            const float a2 = __builtin_amdgcn_exp2f((m2 - ref) * c);
+            l[h] = l[h] * a1 + l2 * a2;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) o[h][d] = o[h][d] * a1 + __shfl_xor(o[h][d], xo) * a2;
+            m[h] = mn;
+        }
+    }
+
+    // merge the waves through LDS and write the partial
+    __shared__ float s_o[kWaves][G][D];
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+    if (gi == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float4 *dst = reinterpret_cast<float4 *>(&s_o[wave][h][li * 8]);
+            dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+            dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+            if (li == 0) {
+                s_m[wave][h] = m[h];
+                s_l[wave][h] = l[h];
+            }
+        }
+    }
+    __syncthreads();
+    const int64_t pbase = ((int64_t)b * a.num_q_heads + h0) * a.num_splits + s;
+    for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float e = __builtin_amdgcn_exp2f((s_m[w][h] - M) * c);
+            L += s_l[w][h] * e;
+            O += s_o[w][h][d] * e;
+        }
+        const int64_t pidx = pbase + (int64_t)h * a.num_splits;
+        a.part_o[pidx * D + d] = O;
+        if (d == 0) {
+            a.part_ml[2 * pidx] = M * c;
+            a.part_ml[2 * pidx + 1] = L;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
+{
+    constexpr int DPL = D / 64;  // output dims per lane
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gw >= a.batch * a.num_q_heads) return;
+    const int b = gw / a.num_q_heads;
+    const int h = gw - b * a.num_q_heads;
+    const int n = min(max(a.context_lens[b], 0), a.max_len);
+    const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+    uint16_t *orow = a.out + (int64_t)b * a.out_stride + (int64_t)h * D + lane * DPL;
+    if (ns == 0) {
+        // an inactive row attends over nothing: the output is the zero vector
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) orow[j] = 0;
+        return;
+    }
+    const int64_t base = ((int64_t)b * a.num_q_heads + h) * a.num_splits;
+    const float *ml = a.part_ml + 2 * base;
+    float M = -INFINITY;
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int s = lane; s < ns; s += 64) L += ml[2 * s + 1] * __builtin_amdgcn_exp2f(ml[2 * s] - M);
+    L = wave_sum(L);
+    float acc[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
+    const float *po = a.part_o + base * D + lane * DPL;
+    for (int s = 0; s < ns; ++s) {
+        const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[j] += w * po[(int64_t)s * D + j];
+    }
+    if constexpr (DPL == 2) {
+        const uint32_t lo = bf16_round(acc[0] / L), hi = bf16_round(acc[1] / L);
+        *reinterpret_cast<uint32_t *>(orow) = lo | (hi << 16);
+    } else {
+        orow[0] = (uint16_t)bf16_round(acc[0] / L);
+    }
+}
+
+// ---- host side ------------------------------------------------------------
+
+int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len)
+{
+    // Aim for about 2048 non-empty workgroups (8 per CU on 256 CUs) when
+    // the longest row fills the grid; 64-position granularity.
+    if (max_context_len <= 0 || batch <= 0 || num_kv_heads <= 0) return kRound;
+    const int64_t units = (int64_t)batch * num_kv_heads;
+    const int64_t splits = (2048 + units - 1) / units;
+    int64_t split = ((int64_t)max_context_len + splits - 1) / splits;
+    split = ((split + kRound - 1) / kRound) * kRound;
+    if (split < kRound) split = kRound;
+    if (split > 16384) split = 16384;
+    return (int32_t)split;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+SplitGeometry split_geometry(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                             int32_t max_context_len, int32_t split_tokens)
+{
+    SplitGeometry g;
+    g.split_tokens = split_tokens;
+    const int64_t ml = max_context_len > 0 ? max_context_len : 0;
+    g.num_splits = (int32_t)((ml + split_tokens - 1) / split_tokens);
+    if (g.num_splits < 1) g.num_splits = 1;
+    const size_t units = (size_t)batch * num_q_heads * g.num_splits;
+    g.part_o_bytes = align256(units * head_dim * sizeof(float));
+    g.part_ml_bytes = align256(units * 2 * sizeof(float));
+    g.total_bytes = g.part_o_bytes + g.part_ml_bytes;
+    return g;
+}
+
+template <int D, int G>
+static void launch_partial_g(const PartialArgs &a, hipStream_t stream)
+{
+    const int64_t grid =
+        (int64_t)a.num_splits * a.batch * a.num_kv_heads * a.head_chunks;
+    decode_partial_kernel<D, G><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
+}
+
+template <int D>
+static hipError_t launch_partial_d(const PartialArgs &a, int G, hipStream_t stream)
+{
+    switch (G) {
+    case 1: launch_partial_g<D, 1>(a, stream); break;
+    case 2: launch_partial_g<D, 2>(a, stream); break;
+    case 3: launch_partial_g<D, 3>(a, stream); break;
+    case 4: launch_partial_g<D, 4>(a, stream); break;
+    case 5: launch_partial_g<D, 5>(a, stream); break;
+    case 6: launch_partial_g<D, 6>(a, stream); break;
+    case 7: launch_partial_g<D, 7>(a, stream); break;
+    case 8: launch_partial_g<D, 8>(a, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_partial(const PartialArgs &a, int32_t head_dim, hipStream_t stream)
+{
+    if (a.batch == 0) return hipSuccess;
+    const int G = a.group / a.head_chunks;
+    if (head_dim == 128) return launch_partial_d<128>(a, G, stream);
+    if (head_dim == 64) return launch_partial_d<64>(a, G, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_reduce(const ReduceArgs &a, int32_t head_dim, hipStream_t stream)
+{
+    if (a.batch == 0) return hipSuccess;
+    const int64_t waves = (int64_t)a.batch * a.num_q_heads;
+    const unsigned grid = (unsigned)((waves + 3) / 4);
+    if (head_dim == 128)
+        decode_reduce_kernel<128><<<grid, 256, 0, stream>>>(a);
+    else if (head_dim == 64)
+        decode_reduce_kernel<64><<<grid, 256, 0, stream>>>(a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace pkv

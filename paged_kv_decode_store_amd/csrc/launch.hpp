@@ -1,0 +1,79 @@
+// Internal launchers behind the C ABI.  Arguments are already validated by
+// the entry points in api.cpp; each launcher only enqueues kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
+                               int32_t table_stride, const int32_t *context_lens,
+                               int32_t batch, int32_t block_size, hipStream_t stream);
+
+hipError_t launch_kv_store(uint16_t *k_cache, uint16_t *v_cache, const uint16_t *k_new,
+                           const uint16_t *v_new, const int32_t *slots, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int64_t new_stride,
+                           int64_t total_slots, hipStream_t stream);
+
+// Split-KV geometry shared by the partial and reduce steps.
+struct SplitGeometry {
+    int32_t split_tokens;  // positions per partial (multiple of 64)
+    int32_t num_splits;    // partials per (row, query head)
+    size_t part_o_bytes;   // fp32 [B][Hq][S][D]
+    size_t part_ml_bytes;  // fp32 [B][Hq][S][2]
+    size_t total_bytes;
+};
+
+int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len);
+SplitGeometry split_geometry(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                             int32_t max_context_len, int32_t split_tokens);
+
+struct PartialArgs {
+    float *part_o;
+    float *part_ml;
+    const uint16_t *q;
+    int64_t q_stride;
+    const uint16_t *k_cache;
+    const uint16_t *v_cache;
+    const int32_t *block_tables;
+    int32_t table_stride;
+    const int32_t *context_lens;
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;          // num_q_heads / num_kv_heads
+    int32_t head_chunks;    // query-head chunks per KV head
+    int32_t bs_log2;
+    int64_t num_blocks;
+    int32_t max_len;        // clamp of context_lens: min(max_context_len, stride*bs)
+    int32_t split_tokens;
+    int32_t num_splits;
+    float c;                // softmax scale * log2(e)
+};
+
+struct ReduceArgs {
+    uint16_t *out;
+    int64_t out_stride;
+    const float *part_o;
+    const float *part_ml;
+    const int32_t *context_lens;
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t max_len;
+    int32_t split_tokens;
+    int32_t num_splits;
+};
+
+hipError_t launch_decode_partial(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_decode_reduce(const ReduceArgs &a, int32_t head_dim, hipStream_t stream);
+
+// Sampler
+size_t sampler_workspace_bytes(int32_t batch, int32_t vocab);
+hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_stride,
+                          const float *gumbel, int64_t gumbel_stride, const float *temperature,
+                          const float *top_p, const int32_t *top_k, int32_t batch, int32_t vocab,
+                          uint32_t flags, void *workspace, hipStream_t stream);
+
+}  // namespace pkv

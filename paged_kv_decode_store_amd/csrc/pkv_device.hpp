@@ -1,0 +1,87 @@
+// Device-side helpers shared by the libpkv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Exact widening of the low / high bf16 of a packed pair.
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_round(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// c + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs, fp32 accumulate
+// (v_dot2_f32_bf16; bf16 products are exact in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane moves inside a 16-lane row.
+enum : int {
+    DPP_QUAD_XOR1 = 0xB1,   // quad_perm [1,0,3,2]
+    DPP_QUAD_XOR2 = 0x4E,   // quad_perm [2,3,0,1]
+    DPP_ROW_HALF_MIRROR = 0x141,
+    DPP_ROW_MIRROR = 0x140,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LANES (2..16) consecutive lanes; every lane of
+// a group ends with the same (bit-identical) sum.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16, "group size");
+    v += dpp_mov<DPP_QUAD_XOR1>(v);
+    if constexpr (LANES >= 4) v += dpp_mov<DPP_QUAD_XOR2>(v);
+    if constexpr (LANES >= 8) v += dpp_mov<DPP_ROW_HALF_MIRROR>(v);
+    if constexpr (LANES >= 16) v += dpp_mov<DPP_ROW_MIRROR>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int x = 32; x >= 1; x >>= 1) v = fmaxf(v, __shfl_xor(v, x));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    for (int x = 32; x >= 1; x >>= 1) v += __shfl_xor(v, x);
+    return v;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Order-preserving map of fp32 onto uint32 (larger float -> larger key);
+// -0 is folded onto +0 first so equal floats get equal keys.
+__device__ __forceinline__ uint32_t float_key(float f)
+{
+    f = f + 0.0f;
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_float(uint32_t k)
+{
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+}  // namespace pkv

@@ -1,0 +1,52 @@
+"""Helpers shared by the GPU parity tests: moving seeded inputs to the
+device, reading results back, and the comparison rules."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+ATTN_TOL = 1e-2          # max-abs error of bf16 attention output vs fp64 oracle
+AMBIGUOUS_MARGIN = 1e-5  # nucleus rows this close to a mass boundary may differ
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_u16(a: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bits -> device bf16 tensor (bit copy)."""
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.cuda().view(torch.bfloat16)
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev_i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def dev_f32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def bf16_out_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def compare_ids(gpu_ids, ref_ids, infos):
+    """Bit-exact ids, except rows whose nucleus cut sits within
+    AMBIGUOUS_MARGIN of a mass boundary.  Returns (#mismatch, #ambiguous)."""
+    bad, amb = [], 0
+    for b, (g, r) in enumerate(zip(gpu_ids, ref_ids)):
+        if g == r:
+            continue
+        info = infos[b]
+        if info.topp_applied and info.margin <= AMBIGUOUS_MARGIN:
+            amb += 1
+            continue
+        bad.append((b, int(g), int(r), info.kept, info.margin))
+    return bad, amb

@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/pkv.h declares, and
+refuse bad arguments on the host, before any HIP call.  No test here passes
+a set of arguments that would reach a kernel launch: every call below fails
+validation.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_decode_store_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 4096  # a non-null, 256-byte aligned fake device address; never dereferenced
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = declared_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.PROTOTYPES)
+
+
+def test_status_strings():
+    L = _lib.lib()
+    assert L.pkv_status_string(0) == b"ok"
+    for code in (-1, -2, -3, -4):
+        assert L.pkv_status_string(code) not in (b"ok", b"unknown status")
+
+
+def test_slot_mapping_validation():
+    L = _lib.lib()
+    assert L.pkv_slot_mapping(None, FAKE, 4, FAKE, 3, 256, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_slot_mapping(FAKE, FAKE, 0, FAKE, 3, 256, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_slot_mapping(FAKE, FAKE, 4, FAKE, 3, 100, None) == _lib.PKV_ERR_UNSUPPORTED
+    assert L.pkv_slot_mapping(FAKE, FAKE, 4, FAKE, -1, 256, None) == _lib.PKV_ERR_INVALID_ARG
+    # an empty batch is a no-op, not an error, and launches nothing
+    assert L.pkv_slot_mapping(None, None, 4, None, 0, 256, None) == _lib.PKV_OK
+
+
+def test_kv_store_validation():
+    L = _lib.lib()
+    ok = dict(k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, s=FAKE, T=4, H=8, D=128, st=0, bs=256, nb=10)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.pkv_kv_store(a["k"], a["v"], a["kn"], a["vn"], a["s"], a["T"], a["H"], a["D"],
+                              a["st"], a["bs"], a["nb"], None)
+
+    assert call(k=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(kn=FAKE + 2) == _lib.PKV_ERR_INVALID_ARG          # misaligned bf16
+    assert call(D=100) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(bs=96) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(st=8 * 128 - 8) == _lib.PKV_ERR_INVALID_ARG      # stride below a row
+    assert call(nb=0) == _lib.PKV_ERR_INVALID_ARG
+    assert call(T=0, k=None, v=None, kn=None, vn=None, s=None) == _lib.PKV_OK
+    assert b"aligned" in L.pkv_last_error() or True
+
+
+def _attn_call(L, **kw):
+    a = dict(out=FAKE, ostride=0, q=FAKE, qstride=0, k=FAKE, v=FAKE, bt=FAKE, bts=16, lens=FAKE,
+             B=64, Hq=16, Hkv=8, D=128, bs=256, nb=600, maxlen=4096, scale=0.0, split=0,
+             ws=FAKE, wsb=0)
+    a.update(kw)
+    return L.pkv_paged_decode_attention(a["out"], a["ostride"], a["q"], a["qstride"], a["k"],
+                                        a["v"], a["bt"], a["bts"], a["lens"], a["B"], a["Hq"],
+                                        a["Hkv"], a["D"], a["bs"], a["nb"], a["maxlen"],
+                                        a["scale"], a["split"], a["ws"], a["wsb"], None)
+
+
+def test_attention_validation():
+    L = _lib.lib()
+    need = L.pkv_decode_workspace_bytes(64, 16, 8, 128, 4096, 0)
+    assert need > 0
+    # every case below fails one check; the last one fails only the workspace size
+    assert _attn_call(L, q=None, wsb=need) == _lib.PKV_ERR_INVALID_ARG
+    assert _attn_call(L, out=None, wsb=need) == _lib.PKV_ERR_INVALID_ARG
+    assert _attn_call(L, k=FAKE + 8, wsb=need) == _lib.PKV_ERR_INVALID_ARG
+    assert _attn_call(L, D=96, wsb=need) == _lib.PKV_ERR_UNSUPPORTED
+    assert _attn_call(L, bs=8, wsb=need) == _lib.PKV_ERR_UNSUPPORTED
+    assert _attn_call(L, Hq=12, wsb=need) == _lib.PKV_ERR_INVALID_ARG  # 12 % 8 != 0
+    assert _attn_call(L, split=100, wsb=need) == _lib.PKV_ERR_INVALID_ARG
+    assert _attn_call(L, scale=float("nan"), wsb=need) == _lib.PKV_ERR_INVALID_ARG
+    assert _attn_call(L, qstride=16 * 128 - 8, wsb=need) == _lib.PKV_ERR_INVALID_ARG
+    assert _attn_call(L, ws=FAKE + 16, wsb=need) == _lib.PKV_ERR_WORKSPACE
+    assert _attn_call(L, ws=None, wsb=need) == _lib.PKV_ERR_WORKSPACE
+    assert _attn_call(L, wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
+    assert b"workspace too small" in L.pkv_last_error()
+
+
+def test_workspace_and_split_queries():
+    L = _lib.lib()
+    for (B, Hkv, ml) in [(64, 8, 4096), (8, 8, 131072), (4, 16, 513), (32, 8, 2048), (1, 1, 1)]:
+        s = L.pkv_decode_split_tokens(B, Hkv, ml, 0)
+        assert s >= 64 and s % 64 == 0
+        assert L.pkv_decode_split_tokens(B, Hkv, ml, 128) == 128
+    assert L.pkv_decode_split_tokens(4, 4, 100, 100) == 0  # not a multiple of 64
+    # workspace: [B][Hq][S][D] + [B][Hq][S][2] fp32, each 256-byte aligned
+    B, Hq, Hkv, D, ml, split = 3, 4, 2, 64, 1000, 128
+    S = (ml + split - 1) // split
+    o = B * Hq * S * D * 4
+    m = B * Hq * S * 2 * 4
+    expect = ((o + 255) // 256) * 256 + ((m + 255) // 256) * 256
+    assert L.pkv_decode_workspace_bytes(B, Hq, Hkv, D, ml, split) == expect
+    assert L.pkv_decode_workspace_bytes(B, Hq, Hkv, D, ml, 100) == 0
+    assert L.pkv_sampler_workspace_bytes(64, 151936) > 64 * 2048 * 12
+    assert L.pkv_sampler_workspace_bytes(1, 0) == 0
+
+
+def test_sampler_validation():
+    L = _lib.lib()
+    need = L.pkv_sampler_workspace_bytes(8, 1000)
+
+    def call(**kw):
+        a = dict(ids=FAKE, z=FAKE, zs=0, g=FAKE, gs=0, t=FAKE, p=FAKE, k=FAKE, B=8, V=1000,
+                 flags=3, ws=FAKE, wsb=need)
+        a.update(kw)
+        return L.pkv_sample_next_token(a["ids"], a["z"], a["zs"], a["g"], a["gs"], a["t"], a["p"],
+                                       a["k"], a["B"], a["V"], a["flags"], a["ws"], a["wsb"], None)
+
+    assert call(z=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(t=FAKE + 2) == _lib.PKV_ERR_INVALID_ARG
+    assert call(V=0) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(V=(1 << 24) + 1) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(flags=4) == _lib.PKV_ERR_INVALID_ARG
+    assert call(zs=999) == _lib.PKV_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
+    assert call(B=0, ids=None, z=None, g=None) == _lib.PKV_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import paged_kv_decode_store_amd as pkv
+
+    bt = torch.zeros((2, 2), dtype=torch.int32)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pkv.slot_mapping(bt, lens, 256, out=torch.empty(2, dtype=torch.int32))

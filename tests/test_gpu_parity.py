@@ -1,0 +1,339 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: slot writes and sampled ids bit-exact; attention within max-abs 1e-2
+of the fp64 oracle.  Sizes: the five workloads in the launch configuration
+the benchmark times, plus small ragged cases that span several 16-position
+chunks, several splits and a ragged tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_store_amd as pkv
+from workloads import CONFIGS, config_by_name, host_inputs
+from workloads.device import device_pool
+from workloads.generate import block_tables, bf16_bits_from_f32, context_lengths, sampling_params
+
+from gpu_util import (ATTN_TOL, bf16_out_to_f64, compare_ids, dev_f32, dev_i32, dev_u16,
+                      host_u16, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def _normal_bf16(rng, shape):
+    return bf16_bits_from_f32(rng.standard_normal(size=shape, dtype=np.float32))
+
+
+# ------------------------------------------------------------ slot mapping --
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_slot_mapping_workloads(cfg):
+    n = context_lengths(cfg)
+    t, _ = block_tables(cfg, n)
+    say(f"slot_mapping {cfg.name}")
+    got = pkv.slot_mapping(dev_i32(t), dev_i32(n), cfg.block_size).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.array_equal(got, oracle.slot_mapping(t, n, cfg.block_size))
+
+
+def test_slot_mapping_edges():
+    t = np.array([[5, 10], [3, -1], [7, 8]], np.int32)
+    n = np.array([300, 257, 0], np.int32)  # row 1's position 256 hits the -1 entry
+    for bs in (16, 256):
+        got = pkv.slot_mapping(dev_i32(t), dev_i32(n), bs).cpu().numpy()
+        assert np.array_equal(got, oracle.slot_mapping(t, n, bs)), bs
+    # past the end of the table
+    got = pkv.slot_mapping(dev_i32(t), dev_i32(np.array([600, 1, 1], np.int32)), 256).cpu().numpy()
+    assert got.tolist() == oracle.slot_mapping(t, np.array([600, 1, 1], np.int32), 256).tolist()
+    assert got[0] == -1
+
+
+# --------------------------------------------------------------- kv store --
+
+@pytest.mark.parametrize("name", ["tiny", "grok", "clone"])
+def test_kv_store_host_pools(name):
+    cfg = config_by_name(name)
+    inp = host_inputs(cfg, layers=(0,), sampler=False)
+    slots = oracle.slot_mapping(inp.block_tables, inp.context_lens, cfg.block_size)
+    kc, vc = dev_u16(inp.k_pool[0]), dev_u16(inp.v_pool[0])
+    say(f"kv_store {name}")
+    pkv.kv_store(kc, vc, dev_u16(inp.k_new[0]), dev_u16(inp.v_new[0]), dev_i32(slots))
+    torch.cuda.synchronize()
+    kref, vref = inp.k_pool[0].copy(), inp.v_pool[0].copy()
+    assert oracle.kv_store(kref, vref, inp.k_new[0], inp.v_new[0], slots, cfg.block_size) == 0
+    assert np.array_equal(host_u16(kc), kref)
+    assert np.array_equal(host_u16(vc), vref)
+
+
+@pytest.mark.parametrize("name", ["qwen3", "long"])
+def test_kv_store_device_pools(name):
+    """Pools filled on the device: the rows at the slots must equal the new
+    K/V bit for bit, and no other pool byte may change."""
+    cfg = config_by_name(name)
+    inp = host_inputs(cfg, layers=(0,), pools=False, sampler=False)
+    slots = oracle.slot_mapping(inp.block_tables, inp.context_lens, cfg.block_size)
+    kc = device_pool(cfg, inp.num_blocks, "kpool", 0)
+    vc = device_pool(cfg, inp.num_blocks, "vpool", 0)
+    k0, v0 = kc.clone(), vc.clone()
+    say(f"kv_store {name}")
+    pkv.kv_store(kc, vc, dev_u16(inp.k_new[0]), dev_u16(inp.v_new[0]), dev_i32(slots))
+    torch.cuda.synchronize()
+    rows = kc.shape[0] * kc.shape[1]
+    sl = torch.from_numpy(slots.astype(np.int64)).cuda()
+    for pool, before, new in ((kc, k0, inp.k_new[0]), (vc, v0, inp.v_new[0])):
+        flat = pool.view(rows, -1)
+        assert np.array_equal(host_u16(flat[sl]).reshape(new.shape), new)
+        keep = torch.ones(rows, dtype=torch.bool, device="cuda")
+        keep[sl] = False
+        assert torch.equal(flat[keep].view(torch.int16), before.view(rows, -1)[keep].view(torch.int16))
+
+
+def test_kv_store_skips_negative_and_out_of_range_slots():
+    rng = np.random.default_rng(3)
+    nb, bs, hkv, d = 3, 16, 2, 64
+    kp, vp = _normal_bf16(rng, (nb, bs, hkv, d)), _normal_bf16(rng, (nb, bs, hkv, d))
+    kn, vn = _normal_bf16(rng, (4, hkv, d)), _normal_bf16(rng, (4, hkv, d))
+    slots = np.array([-1, 47, nb * bs, 0], np.int32)
+    kc, vc = dev_u16(kp), dev_u16(vp)
+    pkv.kv_store(kc, vc, dev_u16(kn), dev_u16(vn), dev_i32(slots))
+    torch.cuda.synchronize()
+    kref, vref = kp.copy(), vp.copy()
+    oracle.kv_store(kref, vref, kn, vn, slots, bs)
+    assert np.array_equal(host_u16(kc), kref) and np.array_equal(host_u16(vc), vref)
+
+
+# -------------------------------------------------------------- attention --
+
+def _attention_case(rng, B, Hq, Hkv, D, bs, lens, split, spare=3, scale=0.0):
+    lens = np.asarray(lens, np.int32)
+    need = [(int(n) + bs - 1) // bs for n in lens]
+    W = max(1, max(need))
+    nb = sum(need) + spare
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((B, W), -1, np.int32)
+    pos = 0
+    for b in range(B):
+        tables[b, :need[b]] = perm[pos:pos + need[b]]
+        pos += need[b]
+    kp, vp = _normal_bf16(rng, (nb, bs, Hkv, D)), _normal_bf16(rng, (nb, bs, Hkv, D))
+    q = _normal_bf16(rng, (B, Hq, D))
+    maxlen = int(max(1, lens.max()))
+    say(f"attention B={B} Hq={Hq} Hkv={Hkv} D={D} bs={bs} split={split} lens={lens.tolist()}")
+    out = pkv.paged_decode_attention(dev_u16(q), dev_u16(kp), dev_u16(vp), dev_i32(tables),
+                                     dev_i32(lens), maxlen, scale=scale, split_tokens=split)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(q, kp, vp, tables, lens, scale)
+    return bf16_out_to_f64(out), ref
+
+
+RAGGED = [1, 15, 16, 17, 63, 64, 65, 200, 255, 256, 257, 700]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (6, 2), (12, 3), (10, 2), (14, 2), (8, 1),
+                                    (16, 1), (22, 2)])
+def test_attention_ragged_group_sizes(D, Hq, Hkv):
+    rng = np.random.default_rng(1000 + D + 7 * Hq + Hkv)
+    got, ref = _attention_case(rng, len(RAGGED), Hq, Hkv, D, 16, RAGGED, split=128)
+    err = np.abs(got - ref).max()
+    assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 256])
+@pytest.mark.parametrize("split", [0, 64, 192, 1024])
+def test_attention_block_sizes_and_splits(bs, split):
+    rng = np.random.default_rng(2000 + bs + split)
+    lens = [0, 1, 31, 33, 100, 513, 1300, 64]
+    got, ref = _attention_case(rng, len(lens), 8, 2, 128, bs, lens, split=split)
+    assert np.abs(got - ref).max() <= ATTN_TOL
+    assert np.all(got[0] == 0.0)  # inactive row -> zero vector
+
+
+def test_attention_explicit_scale_and_peaky_scores():
+    rng = np.random.default_rng(77)
+    got, ref = _attention_case(rng, 3, 4, 2, 128, 16, [5, 300, 2000], split=64, scale=0.5)
+    assert np.abs(got - ref).max() <= ATTN_TOL
+
+
+def _decode_step_host(cfg, inp, layer=0):
+    """Slot mapping + store + attention on the GPU for one layer of host
+    pools; returns (gpu out fp64, oracle out fp64)."""
+    n, t = inp.context_lens, inp.block_tables
+    kc, vc = dev_u16(inp.k_pool[layer]), dev_u16(inp.v_pool[layer])
+    nd, td = dev_i32(n), dev_i32(t)
+    slots = pkv.slot_mapping(td, nd, cfg.block_size)
+    pkv.kv_store(kc, vc, dev_u16(inp.k_new[layer]), dev_u16(inp.v_new[layer]), slots)
+    out = pkv.paged_decode_attention(dev_u16(inp.q[layer]), kc, vc, td, nd, int(n.max()))
+    torch.cuda.synchronize()
+    kref, vref = inp.k_pool[layer].copy(), inp.v_pool[layer].copy()
+    s_ref = oracle.slot_mapping(t, n, cfg.block_size)
+    oracle.kv_store(kref, vref, inp.k_new[layer], inp.v_new[layer], s_ref, cfg.block_size)
+    ref = oracle.decode_attention(inp.q[layer], kref, vref, t, n)
+    return bf16_out_to_f64(out), ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "grok", "clone"])
+def test_decode_step_workloads_full(name):
+    cfg = config_by_name(name)
+    inp = host_inputs(cfg, layers=(0,), sampler=False)
+    say(f"decode step {name}")
+    got, ref = _decode_step_host(cfg, inp)
+    err = np.abs(got - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+def _device_layer(cfg, inp, layer):
+    kc = device_pool(cfg, inp.num_blocks, "kpool", layer)
+    vc = device_pool(cfg, inp.num_blocks, "vpool", layer)
+    return kc, vc
+
+
+def test_decode_step_qwen3_full_layers():
+    """The headline workload: two layers of device-filled pools, every
+    (row, head) output checked against the oracle."""
+    cfg = config_by_name("qwen3")
+    inp = host_inputs(cfg, layers=(0, 27), pools=False, sampler=False)
+    n, t = inp.context_lens, inp.block_tables
+    nd, td = dev_i32(n), dev_i32(t)
+    slots = pkv.slot_mapping(td, nd, cfg.block_size)
+    for li, layer in enumerate(inp.layers):
+        say(f"decode step qwen3 layer {layer}")
+        kc, vc = _device_layer(cfg, inp, layer)
+        pkv.kv_store(kc, vc, dev_u16(inp.k_new[li]), dev_u16(inp.v_new[li]), slots)
+        out = pkv.paged_decode_attention(dev_u16(inp.q[li]), kc, vc, td, nd, int(n.max()))
+        torch.cuda.synchronize()
+        kh, vh = host_u16(kc), host_u16(vc)  # pools after the store
+        ref = oracle.decode_attention(inp.q[li], kh, vh, t, n)
+        err = np.abs(bf16_out_to_f64(out) - ref).max()
+        say(f"  max abs err {err:.3e}")
+        assert err <= ATTN_TOL
+        del kc, vc, kh, vh
+
+
+def test_decode_step_long_sampled_heads():
+    """Long-context split-KV workload at full size; the oracle checks three
+    query heads (first, middle, last) of every row, which covers all
+    splits of every row."""
+    cfg = config_by_name("long")
+    inp = host_inputs(cfg, layers=(0,), pools=False, sampler=False)
+    n, t = inp.context_lens, inp.block_tables
+    nd, td = dev_i32(n), dev_i32(t)
+    kc, vc = _device_layer(cfg, inp, 0)
+    say("decode step long")
+    slots = pkv.slot_mapping(td, nd, cfg.block_size)
+    pkv.kv_store(kc, vc, dev_u16(inp.k_new[0]), dev_u16(inp.v_new[0]), slots)
+    out = pkv.paged_decode_attention(dev_u16(inp.q[0]), kc, vc, td, nd, int(n.max()))
+    torch.cuda.synchronize()
+    got = bf16_out_to_f64(out)
+    kh, vh = host_u16(kc), host_u16(vc)
+    g = cfg.group
+    scale = 1.0 / np.sqrt(cfg.head_dim)
+    worst = 0.0
+    for b in range(cfg.batch):
+        for h in (0, cfg.num_q_heads // 2 + 1, cfg.num_q_heads - 1):
+            ref = oracle.decode_attention_head(inp.q[0][b, h], kh, vh, t[b], n[b], h // g, scale)
+            worst = max(worst, float(np.abs(got[b, h] - ref).max()))
+    say(f"  max abs err {worst:.3e}")
+    assert worst <= ATTN_TOL
+
+
+# ---------------------------------------------------------------- sampler --
+
+def _flags(t, p, k, V):
+    f = 0
+    if np.any((k > 0) & (k < V)):
+        f |= pkv.PKV_SAMPLE_TOPK
+    if np.any(p < 1):
+        f |= pkv.PKV_SAMPLE_TOPP
+    return f
+
+
+def _sample_and_compare(z, g, t, p, k, flags=None):
+    B, V = z.shape
+    if flags is None:
+        flags = _flags(t, p, k, V)
+    ids = pkv.sample_next_token(dev_f32(z), dev_f32(g), dev_f32(t), dev_f32(p), dev_i32(k),
+                                flags=flags).cpu().numpy()
+    torch.cuda.synchronize()
+    # the oracle sees the filters that the flags leave on
+    p_eff = p if flags & pkv.PKV_SAMPLE_TOPP else np.ones_like(p)
+    k_eff = k if flags & pkv.PKV_SAMPLE_TOPK else np.zeros_like(k)
+    ref, infos = oracle.sample(z, g, t, p_eff, k_eff)
+    bad, amb = compare_ids(ids, ref, infos)
+    return bad, amb, infos
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_sampler_workloads(cfg):
+    inp = host_inputs(cfg, layers=(), pools=False)
+    t, p, k = sampling_params(cfg)
+    say(f"sampler {cfg.name}")
+    bad, amb, infos = _sample_and_compare(inp.logits, inp.gumbel, t, p, k)
+    say(f"  ambiguous rows {amb}, kept sizes {[i.kept for i in infos[:8]]}")
+    assert not bad, bad
+    assert amb <= 1
+
+
+def test_sampler_mixed_rows_and_edges():
+    rng = np.random.default_rng(55)
+    B, V = 24, 50000  # V not a multiple of any chunk size
+    z = (rng.standard_normal((B, V), dtype=np.float32) * 3).astype(np.float32)
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = np.array([0.0, 0.7, 1.0, 1.3, -1.0, 0.01] * 4, np.float32)
+    p = np.array([1.0, 0.9, 0.5, 0.0, 0.95, 0.3, 1.0, 0.99] * 3, np.float32)
+    k = np.array([0, 0, 50, 1, V, 3, 1000, 0, 20, 0, 0, 7] * 2, np.int32)
+    # exact ties: row 2 and 8 get repeated values around their k-th value
+    z[2, :200] = 5.0
+    z[8, 1000:1100] = 4.0
+    z[8, 10] = 9.0
+    bad, amb, _ = _sample_and_compare(z, g, t, p, k)
+    assert not bad, bad
+    assert amb == 0
+
+
+def test_sampler_flags_turn_filters_off():
+    rng = np.random.default_rng(56)
+    B, V = 8, 9000
+    z = (rng.standard_normal((B, V), dtype=np.float32) * 2).astype(np.float32)
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = np.full(B, 0.9, np.float32)
+    p = np.full(B, 0.5, np.float32)
+    k = np.full(B, 10, np.int32)
+    for flags in (0, pkv.PKV_SAMPLE_TOPK, pkv.PKV_SAMPLE_TOPP, 3):
+        bad, amb, _ = _sample_and_compare(z, g, t, p, k, flags=flags)
+        assert not bad and amb == 0, flags
+
+
+def test_sampler_tiny_vocab_and_single_row():
+    rng = np.random.default_rng(57)
+    for V in (1, 2, 7, 1024, 1025):
+        z = rng.standard_normal((1, V), dtype=np.float32)
+        g = rng.gumbel(size=(1, V)).astype(np.float32)
+        for (t, p, k) in ((1.0, 1.0, 0), (0.5, 0.6, 0), (1.0, 1.0, 2), (0.0, 1.0, 0)):
+            bad, amb, _ = _sample_and_compare(z, g, np.array([t], np.float32),
+                                              np.array([p], np.float32), np.array([k], np.int32))
+            assert not bad, (V, t, p, k, bad)
+
+
+def test_sampler_top_k_ties_across_chunks():
+    """Many equal logits spread over several chunks: the kept ties must be
+    the lowest indices, across chunk boundaries."""
+    B, V = 4, 40000
+    z = np.zeros((B, V), np.float32)
+    z[:, ::7] = 1.0            # 5715 equal maxima per row
+    g = np.random.default_rng(58).gumbel(size=(B, V)).astype(np.float32)
+    t = np.ones(B, np.float32)
+    p = np.ones(B, np.float32)
+    k = np.array([1, 100, 3000, 5715], np.int32)
+    bad, amb, infos = _sample_and_compare(z, g, t, p, k)
+    assert not bad
+    assert [i.kept for i in infos] == k.tolist()
