@@ -95,7 +95,7 @@ def main():
     t, p, k = (torch.from_numpy(x).to(dev) for x in sampling_params(cfg))
     flags = (pkv.PKV_SAMPLE_TOPK if cfg.top_k > 0 else 0) | (pkv.PKV_SAMPLE_TOPP if cfg.top_p < 1 else 0)
     max_len = int(n.max())
-    split = pkv.decode_split_tokens(B, Hkv, max_len, args.split)
+    split = pkv.decode_split_tokens(B, Hq, Hkv, max_len, args.split)
     ws = torch.empty(pkv.decode_workspace_bytes(B, Hq, Hkv, D, max_len, split), dtype=torch.uint8,
                      device=dev)
     sws = torch.empty(pkv.sampler_workspace_bytes(B, cfg.vocab), dtype=torch.uint8, device=dev)

@@ -108,11 +108,14 @@ int pkv_kv_store(void *k_cache, void *v_cache, const void *k_new,
  * head_dim       64 or 128;  block_size power of two in [16, 4096]
  * scale          softmax scale; <= 0 selects 1/sqrt(head_dim)
  * split_tokens   positions per partial: 0 = automatic, else a multiple of
- *                64 (see pkv_decode_split_tokens)
+ *                64 (see pkv_decode_split_tokens: the automatic choice
+ *                depends on batch, heads and max_context_len only, never on
+ *                device data, so a query and the launch always agree)
  * workspace      device scratch of at least pkv_decode_workspace_bytes(...)
  *                bytes, 256-byte aligned; contents on entry are ignored. */
-int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_kv_heads,
-                                int32_t max_context_len, int32_t split_tokens);
+int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t max_context_len,
+                                int32_t split_tokens);
 
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,

@@ -81,9 +81,10 @@ def kv_store(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
                              _stream()), "pkv_kv_store")
 
 
-def decode_split_tokens(batch: int, num_kv_heads: int, max_context_len: int,
+def decode_split_tokens(batch: int, num_q_heads: int, num_kv_heads: int, max_context_len: int,
                         split_tokens: int = 0) -> int:
-    return int(lib().pkv_decode_split_tokens(batch, num_kv_heads, max_context_len, split_tokens))
+    return int(lib().pkv_decode_split_tokens(batch, num_q_heads, num_kv_heads, max_context_len,
+                                             split_tokens))
 
 
 def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

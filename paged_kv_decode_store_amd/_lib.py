@@ -31,7 +31,7 @@ PROTOTYPES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_slot_mapping": (ctypes.c_int, [_P, _P, _I32, _P, _I32, _I32, _P]),
     "pkv_kv_store": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I64, _P]),
-    "pkv_decode_split_tokens": (_I32, [_I32, _I32, _I32, _I32]),
+    "pkv_decode_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "pkv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_paged_decode_attention": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _P, _I32, _P, _I32,
                                                   _I32, _I32, _I32, _I32, _I64, _I32, _F, _I32,

@@ -69,11 +69,12 @@ int32_t heads_per_chunk(int32_t group)
     return 1;
 }
 
-int32_t effective_split(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
-                        int32_t split_tokens)
+int32_t effective_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t max_context_len, int32_t split_tokens)
 {
-    return split_tokens > 0 ? split_tokens
-                            : pkv::auto_split_tokens(batch, num_kv_heads, max_context_len);
+    if (split_tokens > 0) return split_tokens;
+    const int32_t group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
+    return pkv::auto_split_tokens(batch, num_kv_heads, max_context_len, group);
 }
 
 int32_t clamp_len(int32_t max_context_len, int32_t block_table_stride, int32_t block_size)
@@ -150,11 +151,11 @@ int pkv_kv_store(void *k_cache, void *v_cache, const void *k_new, const void *v_
                       "kv_store launch");
 }
 
-int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
-                                int32_t split_tokens)
+int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t max_context_len, int32_t split_tokens)
 {
     if (check_split(split_tokens) != PKV_OK) return 0;
-    return effective_split(batch, num_kv_heads, max_context_len, split_tokens);
+    return effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -164,7 +165,7 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
     if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         max_context_len < 0 || check_split(split_tokens) != PKV_OK)
         return 0;
-    const int32_t split = effective_split(batch, num_kv_heads, max_context_len, split_tokens);
+    const int32_t split = effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
     return pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split).total_bytes;
 }
 
@@ -192,7 +193,7 @@ int pkv_decode_attention_partial(const void *q, int64_t q_stride, const void *k_
             "bf16 tensors must be 16-byte aligned");
     REQUIRE(aligned(block_tables, 4) && aligned(context_lens, 4), PKV_ERR_INVALID_ARG,
             "int32 arrays must be 4-byte aligned");
-    const int32_t split = effective_split(batch, num_kv_heads, max_context_len, split_tokens);
+    const int32_t split = effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
     const pkv::SplitGeometry g =
         pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split);
     REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,
@@ -242,7 +243,7 @@ int pkv_decode_attention_reduce(void *out, int64_t out_stride, const int32_t *co
     REQUIRE(out && context_lens, PKV_ERR_INVALID_ARG, "null pointer");
     REQUIRE(aligned(out, 16), PKV_ERR_INVALID_ARG, "out must be 16-byte aligned");
     REQUIRE(aligned(context_lens, 4), PKV_ERR_INVALID_ARG, "context_lens must be 4-byte aligned");
-    const int32_t split = effective_split(batch, num_kv_heads, max_context_len, split_tokens);
+    const int32_t split = effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
     const pkv::SplitGeometry g =
         pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split);
     REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,

@@ -75,19 +75,25 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     const int bs_mask = (1 << a.bs_log2) - 1;
     const int32_t *table = a.block_tables + (int64_t)b * a.table_stride;
 
-    for (int t0 = t_begin + wave * kChunk; t0 < t_end; t0 += kRound) {
+    // Issue the K/V loads of the chunk starting at t0 (one block, U positions
+    // per lane group, one 16-byte piece per lane and position).
+    auto load_chunk = [&](int t0, uint4 (&kr)[U], uint4 (&vr)[U]) {
         int blk = table[t0 >> a.bs_log2];
         blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
         const int64_t base =
             (((int64_t)blk << a.bs_log2) + (t0 & bs_mask)) * tok_stride + lane_off;
-        uint4 kr[U], vr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            kr[u] = *reinterpret_cast<const uint4 *>(a.k_cache + base + u * tok_stride);
+            kr[u] = load_stream16(a.k_cache + base + u * tok_stride);
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            vr[u] = *reinterpret_cast<const uint4 *>(a.v_cache + base + u * tok_stride);
+            vr[u] = load_stream16(a.v_cache + base + u * tok_stride);
+    };
 
+    // Online softmax over one chunk.  The running max of a lane group only
+    // moves when one of its scores exceeds it; the rescale of (l, o) is done
+    // only in waves where some group's max moved (a wave-uniform branch).
+    auto compute_chunk = [&](int t0, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
         const int tg = t0 + gi * U;
         float vf[U][8];
 #pragma unroll
@@ -101,7 +107,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
             vf[u][6] = bf16_lo(vr[u].w);
             vf[u][7] = bf16_hi(vr[u].w);
         }
-
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float sc[U];
@@ -117,24 +122,38 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
             float mx = m[h];
 #pragma unroll
             for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u]);
-            const float ref = (mx == -INFINITY) ? 0.f : mx;
-            const float alpha = __builtin_amdgcn_exp2f((m[h] - ref) * c);
+            if (__any(mx > m[h])) {
+                const float ref = (mx == -INFINITY) ? 0.f : mx;
+                const float alpha = __builtin_amdgcn_exp2f((m[h] - ref) * c);
+                l[h] *= alpha;
+#pragma unroll
+                for (int d = 0; d < 8; ++d) o[h][d] *= alpha;
+                m[h] = mx;
+            }
+            const float mc = (m[h] == -INFINITY) ? 0.f : m[h] * c;
             float p[U], psum = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                p[u] = __builtin_amdgcn_exp2f((sc[u] - ref) * c);
+                p[u] = __builtin_amdgcn_exp2f(fmaf(sc[u], c, -mc));
                 psum += p[u];
             }
-            l[h] = l[h] * alpha + psum;
+            l[h] += psum;
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
-                float acc = o[h][d] * alpha;
+                float acc = o[h][d];
 #pragma unroll
-                for (int u = 0; u < U; ++u) acc += p[u] * vf[u][d];
+                for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][d], acc);
                 o[h][d] = acc;
             }
-            m[h] = mx;
         }
+    };
+
+    // Double-buffered stream: the next chunk's loads are in flight while the
+    // current chunk is computed.
+    for (int t0 = t_begin + wave * kChunk; t0 < t_end; t0 += kRound) {
+        uint4 ka[U], va[U];
+        load_chunk(t0, ka, va);
+        compute_chunk(t0, ka, va);
     }
 
     // merge the lane groups of this wave
@@ -240,17 +259,23 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
 
 // ---- host side ------------------------------------------------------------
 
-int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len)
+int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
+                          int32_t group)
 {
-    // Aim for about 2048 non-empty workgroups (8 per CU on 256 CUs) when
-    // the longest row fills the grid; 64-position granularity.
+    // Measured on MI355X: the partial kernel runs best with roughly 1-2k
+    // non-empty workgroups.  Rows are assumed half full on average, so the
+    // split aims at B * Hkv * max_len / 2 positions spread over ~2048
+    // workgroups; groups >= 4 get at least 512 positions per split so the
+    // per-workgroup merge of G heads stays small next to the streaming.
     if (max_context_len <= 0 || batch <= 0 || num_kv_heads <= 0) return kRound;
-    const int64_t units = (int64_t)batch * num_kv_heads;
-    const int64_t splits = (2048 + units - 1) / units;
-    int64_t split = ((int64_t)max_context_len + splits - 1) / splits;
+    int64_t split = (int64_t)batch * num_kv_heads * max_context_len / 4096;
+    const int64_t lo = group >= 4 ? 512 : 128;
+    if (split < lo) split = lo;
+    if (split > 8192) split = 8192;
     split = ((split + kRound - 1) / kRound) * kRound;
-    if (split < kRound) split = kRound;
-    if (split > 16384) split = 16384;
+    // no longer than the longest row needs
+    const int64_t cap = ((int64_t)max_context_len + kRound - 1) / kRound * kRound;
+    if (split > cap) split = cap;
     return (int32_t)split;
 }
 

@@ -26,7 +26,8 @@ struct SplitGeometry {
     size_t total_bytes;
 };
 
-int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len);
+int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
+                          int32_t group);
 SplitGeometry split_geometry(int32_t batch, int32_t num_q_heads, int32_t head_dim,
                              int32_t max_context_len, int32_t split_tokens);
 

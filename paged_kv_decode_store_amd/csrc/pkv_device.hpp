@@ -12,6 +12,15 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+// 16-byte load with the non-temporal (streaming) cache policy: for data
+// read once per launch, like cached K/V rows.
+__device__ __forceinline__ uint4 load_stream16(const void *p)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 // fp32 -> bf16, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_round(float f)
 {

@@ -1,18 +1,23 @@
 // Next-token sampler: temperature, top-k, nucleus (top-p) and a Gumbel-max
 // draw, on fp32 logits [B][V].
 //
-// Every pass splits each row into chunks of `chunk` logits, one 256-thread
-// workgroup per (chunk, row), and recomputes s = z / T (IEEE division) and
-// its order-preserving 32-bit key.  Thresholds are found by a three-level
-// radix select on the key (11 + 11 + 10 bits): each level histograms the
-// keys that match the prefix chosen so far into 2048 digits, and the last
-// workgroup of the row to finish (counted with an atomic ticket) scans the
-// histogram and fixes the next digit.  Top-k ranks by count; top-p
-// accumulates mass exp(s - max) in 40-bit fixed point, so the sums are
-// exact, order independent and identical from run to run.  A top-k tie at
-// the k-th key is cut by index with one more pass.  The final pass takes the
-// argmax of fl32(s + g) over the eligible logits as one 64-bit atomic max of
+// Row-parallel passes split each row into chunks of `chunk` logits, one
+// 256-thread workgroup per (chunk, row).  Each thread first loads its whole
+// share of the chunk into registers (float4 when rows are 16-byte aligned)
+// and then recomputes s = z / T (IEEE division) and the order-preserving
+// 32-bit key of s.  Thresholds come from a three-level radix select on the
+// key (11 + 11 + 10 bits): a histogram pass counts the keys that match the
+// prefix chosen so far into 2048 digits (global atomics), and a per-row
+// select kernel (one workgroup per row) scans the histogram and fixes the
+// next digit.  Top-k ranks by count; top-p accumulates the mass exp(s - max)
+// in 2^-40 fixed point, so the sums are exact, independent of order and
+// identical from run to run.  A top-k tie at the k-th key is cut by index
+// with one more count pass.  The final pass takes the argmax of
+// fl32(s + g) over the eligible logits as a 64-bit atomic max of
 // (key, ~index), which resolves ties to the lowest index.
+//
+// Passes communicate only through kernel boundaries: no workgroup waits for
+// or fences against another one inside a kernel.
 #include <math.h>
 
 #include "launch.hpp"
@@ -25,6 +30,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kDigits = 2048;
 constexpr int kDigitsPerThread = kDigits / kThreads;
+constexpr int kMaxPer = 32;  // logits per thread per chunk (chunk <= 8192)
 
 enum : uint32_t { MODE_GREEDY = 1, MODE_TOPK = 2, MODE_TOPP = 4, MODE_TOPP_MAX = 8 };
 enum : int { WHICH_K = 0, WHICH_P = 1 };
@@ -34,7 +40,7 @@ struct alignas(64) SampCtl {
     unsigned long long Z;     // kept mass, 2^-40 units
     unsigned long long A;     // mass strictly above the current top-p bucket
     uint32_t max_key;         // key of max s
-    uint32_t done;            // last-workgroup ticket
+    uint32_t pad;
     uint32_t mode;
     uint32_t k_prefix;        // top-k: digits fixed so far
     uint32_t k_rank;          // rank still needed inside the prefix bucket
@@ -159,17 +165,44 @@ __device__ T block_scan_inclusive(T v, T *scratch)
     return r;
 }
 
-// True in every thread of the one workgroup of row b that finishes last.
-__device__ bool last_of_row(SampCtl *ctl, int *s_flag)
-{
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) *s_flag = (atomicAdd(&ctl->done, 1u) == gridDim.x - 1) ? 1 : 0;
-    __syncthreads();
-    const bool last = *s_flag != 0;
-    if (last) __threadfence();
-    return last;
-}
+// Each thread's share of one chunk (chunk / 256 <= 32 logits), loaded into
+// registers before any of it is used so that all loads of a pass are in
+// flight together.  VEC4: consecutive threads read consecutive float4s
+// (rows 16-byte aligned, vocab a multiple of 4); otherwise single floats.
+template <bool VEC4>
+struct Tile {
+    float v[kMaxPer];
+
+    __device__ __forceinline__ static int index(int i0, int j)
+    {
+        if constexpr (VEC4)
+            return i0 + ((j >> 2) * kThreads + (int)threadIdx.x) * 4 + (j & 3);
+        else
+            return i0 + j * kThreads + (int)threadIdx.x;
+    }
+
+    __device__ __forceinline__ void load(const float *__restrict__ row, int i0, int i1, int per)
+    {
+        if constexpr (VEC4) {
+#pragma unroll
+            for (int q = 0; q < kMaxPer / 4; ++q) {
+                const int i = index(i0, 4 * q);
+                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (4 * q < per && i < i1) f = *reinterpret_cast<const float4 *>(row + i);
+                v[4 * q] = f.x;
+                v[4 * q + 1] = f.y;
+                v[4 * q + 2] = f.z;
+                v[4 * q + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j) {
+                const int i = index(i0, j);
+                v[j] = (j < per && i < i1) ? row[i] : 0.f;
+            }
+        }
+    }
+};
 
 __global__ __launch_bounds__(kThreads) void samp_init_kernel(const SampArgs a)
 {
@@ -178,7 +211,6 @@ __global__ __launch_bounds__(kThreads) void samp_init_kernel(const SampArgs a)
         a.cnt[(int64_t)b * kDigits + d] = 0;
         a.mass[(int64_t)b * kDigits + d] = 0;
     }
-    for (int c = threadIdx.x; c < a.nchunks; c += kThreads) a.chunk_cnt[(int64_t)b * a.nchunks + c] = 0;
     if (threadIdx.x == 0) {
         SampCtl c = {};
         const float T = a.temperature[b];
@@ -199,6 +231,7 @@ __global__ __launch_bounds__(kThreads) void samp_init_kernel(const SampArgs a)
 }
 
 // max key of s over the row (needed for top-p masses and the p <= 0 case)
+template <bool VEC4>
 __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
@@ -206,16 +239,22 @@ __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
     if (!(ctl->mode & (MODE_TOPP | MODE_TOPP_MAX))) return;
     __shared__ uint32_t s_red[kThreads];
     const float T = a.temperature[b];
-    const float *z = a.logits + (int64_t)b * a.lstride;
     const int i0 = blockIdx.x * a.chunk;
     const int i1 = min(a.vocab, i0 + a.chunk);
+    const int per = a.chunk / kThreads;
+    Tile<VEC4> t;
+    t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
     uint32_t kmax = 0;
-    for (int i = i0 + threadIdx.x; i < i1; i += kThreads) kmax = max(kmax, float_key(z[i] / T));
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j)
+        if (j < per && Tile<VEC4>::index(i0, j) < i1) kmax = max(kmax, float_key(t.v[j] / T));
     kmax = block_max(kmax, s_red);
     if (threadIdx.x == 0) atomicMax(&ctl->max_key, kmax);
 }
 
-template <int WHICH>
+// One radix level: histogram of the digit (key >> shift) & mask over the
+// keys that match the prefix fixed so far.
+template <int WHICH, bool VEC4>
 __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a, int level)
 {
     const int b = blockIdx.y;
@@ -227,8 +266,13 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a, i
     __shared__ uint32_t s_cnt[kDigits];
     __shared__ unsigned long long s_mass[WHICH == WHICH_P ? kDigits : 1];
     __shared__ unsigned long long s_red[kThreads];
-    __shared__ int s_flag;
-    __shared__ int s_dstar;
+
+    const float T = a.temperature[b];
+    const int i0 = blockIdx.x * a.chunk;
+    const int i1 = min(a.vocab, i0 + a.chunk);
+    const int per = a.chunk / kThreads;
+    Tile<VEC4> t;
+    t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
 
     for (int d = threadIdx.x; d < kDigits; d += kThreads) {
         s_cnt[d] = 0;
@@ -241,17 +285,16 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a, i
     const int hi = shift + width;
     const uint32_t dmask = (1u << width) - 1u;
     const uint32_t prefix = WHICH == WHICH_K ? ctl->k_prefix : ctl->p_prefix;
-    const float T = a.temperature[b];
     const float M = key_float(ctl->max_key);
     const uint32_t kkey = ctl->k_key, kcut = ctl->k_cut;
     const bool topk = (mode & MODE_TOPK) != 0;
-    const float *z = a.logits + (int64_t)b * a.lstride;
-    const int i0 = blockIdx.x * a.chunk;
-    const int i1 = min(a.vocab, i0 + a.chunk);
 
     unsigned long long zloc = 0;
-    for (int i = i0 + threadIdx.x; i < i1; i += kThreads) {
-        const float s = z[i] / T;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+        const int i = Tile<VEC4>::index(i0, j);
+        if (j >= per || i >= i1) continue;
+        const float s = t.v[j] / T;
         const uint32_t key = float_key(s);
         if (hi < 32 && (key >> hi) != (prefix >> hi)) continue;
         if (WHICH == WHICH_P && topk && !(key > kkey || (key == kkey && (uint32_t)i <= kcut)))
@@ -275,34 +318,52 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a, i
         const unsigned long long zs = block_sum(zloc, s_red);
         if (threadIdx.x == 0 && zs) atomicAdd(&ctl->Z, zs);
     }
-    if (!last_of_row(ctl, &s_flag)) return;
+}
 
-    // ---- last workgroup of the row: choose the digit ----
-    for (int d = threadIdx.x; d < kDigits; d += kThreads) {
-        uint32_t *gc = &a.cnt[(int64_t)b * kDigits + d];
-        s_cnt[d] = __hip_atomic_load(gc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// One workgroup per row: pick the digit of the current level from the
+// completed histogram, update the row's prefix, clear the histogram.
+template <int WHICH>
+__global__ __launch_bounds__(kThreads) void samp_select_kernel(const SampArgs a, int level)
+{
+    const int b = blockIdx.x;
+    SampCtl *ctl = a.ctl + b;
+    const uint32_t mode = ctl->mode;
+    if (WHICH == WHICH_K && !(mode & MODE_TOPK)) return;
+    if (WHICH == WHICH_P && !(mode & MODE_TOPP)) return;
+    __shared__ unsigned long long s_red[kThreads];
+    __shared__ int s_dstar;
+
+    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
+    const int d_lo = (int)threadIdx.x * kDigitsPerThread;
+    uint32_t cnt[kDigitsPerThread];
+    unsigned long long mass[kDigitsPerThread];
+#pragma unroll
+    for (int j = 0; j < kDigitsPerThread; ++j) {
+        uint32_t *gc = &a.cnt[(int64_t)b * kDigits + d_lo + j];
+        cnt[j] = *gc;
+        *gc = 0;
+        mass[j] = 0;
         if (WHICH == WHICH_P) {
-            unsigned long long *gm = &a.mass[(int64_t)b * kDigits + d];
-            s_mass[d] = __hip_atomic_load(gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(gm, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            unsigned long long *gm = &a.mass[(int64_t)b * kDigits + d_lo + j];
+            mass[j] = *gm;
+            *gm = 0;
         }
     }
     if (threadIdx.x == 0) s_dstar = kDigits;
-    __syncthreads();
 
-    const int d_hi = (int)threadIdx.x * kDigitsPerThread + kDigitsPerThread - 1;
     if (WHICH == WHICH_K) {
         unsigned long long own = 0;
-        for (int j = 0; j < kDigitsPerThread; ++j) own += s_cnt[d_hi - j];
-        // count in digits above this thread's range
+#pragma unroll
+        for (int j = 0; j < kDigitsPerThread; ++j) own += cnt[j];
+        // count in the digits above this thread's range
         unsigned long long above = block_scan_inclusive<unsigned long long, true>(own, s_red) - own;
         const unsigned long long r = ctl->k_rank;
-        for (int j = 0; j < kDigitsPerThread; ++j) {
-            const int d = d_hi - j;
-            const unsigned long long cd = s_cnt[d];
+#pragma unroll
+        for (int j = kDigitsPerThread - 1; j >= 0; --j) {
+            const unsigned long long cd = cnt[j];
             if (above < r && r <= above + cd) {
-                // unique digit holding the rank-th largest key
+                // the unique digit holding the rank-th largest key
+                const int d = d_lo + j;
                 const uint32_t pre = ctl->k_prefix | ((uint32_t)d << shift);
                 const uint32_t rank = (uint32_t)(r - above);
                 ctl->k_prefix = pre;
@@ -316,21 +377,22 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a, i
         }
     } else {
         unsigned long long own = 0;
-        for (int j = 0; j < kDigitsPerThread; ++j) own += s_mass[d_hi - j];
+#pragma unroll
+        for (int j = 0; j < kDigitsPerThread; ++j) own += mass[j];
         unsigned long long above = block_scan_inclusive<unsigned long long, true>(own, s_red) - own;
         const unsigned long long A = ctl->A;
         const double limit = (double)a.top_p[b] * (double)ctl->Z;
         int cand = kDigits;
         unsigned long long cand_above = 0;
-        for (int j = 0; j < kDigitsPerThread; ++j) {
-            const int d = d_hi - j;
-            // mass strictly above every key of digit d; grows as d falls
-            if ((double)(A + above) > limit) break;
-            if (s_cnt[d]) {
-                cand = d;
+        // the lowest non-empty digit whose strictly-greater mass is within
+        // the limit (that mass only grows as the digit falls)
+#pragma unroll
+        for (int j = kDigitsPerThread - 1; j >= 0; --j) {
+            if ((double)(A + above) <= limit && cnt[j]) {
+                cand = d_lo + j;
                 cand_above = above;
             }
-            above += s_mass[d];
+            above += mass[j];
         }
         if (cand < kDigits) atomicMin(&s_dstar, cand);
         __syncthreads();
@@ -341,41 +403,51 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a, i
             if (level == 2) ctl->p_key = pre;
         }
     }
-    if (threadIdx.x == 0) ctl->done = 0;
 }
 
-// top-k ties: keep only the k_tie lowest-index logits whose key equals k_key
-__global__ __launch_bounds__(kThreads) void samp_tie_kernel(const SampArgs a)
+// top-k ties, count step: logits per chunk whose key equals k_key
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads) void samp_tie_count_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
     SampCtl *ctl = a.ctl + b;
     if (!(ctl->mode & MODE_TOPK) || ctl->k_tie == 0) return;
     __shared__ uint32_t s_red[kThreads];
-    __shared__ int s_flag;
+    const float T = a.temperature[b];
+    const uint32_t kkey = ctl->k_key;
+    const int i0 = blockIdx.x * a.chunk;
+    const int i1 = min(a.vocab, i0 + a.chunk);
+    const int per = a.chunk / kThreads;
+    Tile<VEC4> t;
+    t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
+    uint32_t eq = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j)
+        if (j < per && Tile<VEC4>::index(i0, j) < i1) eq += float_key(t.v[j] / T) == kkey;
+    eq = block_sum(eq, s_red);
+    if (threadIdx.x == 0) a.chunk_cnt[(int64_t)b * a.nchunks + blockIdx.x] = eq;
+}
+
+// top-k ties, cut step (one workgroup per row): keep only the k_tie
+// lowest-index logits whose key equals k_key
+__global__ __launch_bounds__(kThreads) void samp_tie_cut_kernel(const SampArgs a)
+{
+    const int b = blockIdx.x;
+    SampCtl *ctl = a.ctl + b;
+    if (!(ctl->mode & MODE_TOPK) || ctl->k_tie == 0) return;
+    __shared__ uint32_t s_red[kThreads];
     __shared__ int s_chunk;
     __shared__ uint32_t s_rem;
-
     const float T = a.temperature[b];
     const uint32_t kkey = ctl->k_key;
     const float *z = a.logits + (int64_t)b * a.lstride;
-    int i0 = blockIdx.x * a.chunk;
-    int i1 = min(a.vocab, i0 + a.chunk);
-    uint32_t eq = 0;
-    for (int i = i0 + threadIdx.x; i < i1; i += kThreads) eq += float_key(z[i] / T) == kkey;
-    eq = block_sum(eq, s_red);
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&a.chunk_cnt[(int64_t)b * a.nchunks + blockIdx.x], eq, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    if (!last_of_row(ctl, &s_flag)) return;
-
     if (threadIdx.x == 0) {
         const uint32_t need = ctl->k_tie;
         uint32_t run = 0;
         int cstar = a.nchunks - 1;
         uint32_t rem = 1;
         for (int c = 0; c < a.nchunks; ++c) {
-            const uint32_t v = __hip_atomic_load(&a.chunk_cnt[(int64_t)b * a.nchunks + c],
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t v = a.chunk_cnt[(int64_t)b * a.nchunks + c];
             if (run + v >= need) {
                 cstar = c;
                 rem = need - run;
@@ -389,8 +461,8 @@ __global__ __launch_bounds__(kThreads) void samp_tie_kernel(const SampArgs a)
     __syncthreads();
     // ordered scan of the chosen chunk: thread t owns a contiguous range
     const int per = a.chunk / kThreads;
-    i0 = s_chunk * a.chunk + (int)threadIdx.x * per;
-    i1 = min(a.vocab, i0 + per);
+    const int i0 = s_chunk * a.chunk + (int)threadIdx.x * per;
+    const int i1 = min(a.vocab, i0 + per);
     uint32_t own = 0;
     for (int i = i0; i < i1; ++i) own += float_key(z[i] / T) == kkey;
     const uint32_t incl = block_scan_inclusive<uint32_t, false>(own, s_red);
@@ -405,48 +477,102 @@ __global__ __launch_bounds__(kThreads) void samp_tie_kernel(const SampArgs a)
             }
         }
     }
-    if (threadIdx.x == 0) ctl->done = 0;
 }
 
+template <bool VEC4>
 __global__ __launch_bounds__(kThreads) void samp_final_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
     SampCtl *ctl = a.ctl + b;
     __shared__ unsigned long long s_red[kThreads];
-    __shared__ int s_flag;
     const uint32_t mode = ctl->mode;
-    const float *z = a.logits + (int64_t)b * a.lstride;
-    const float *g = a.gumbel + (int64_t)b * a.gstride;
     const int i0 = blockIdx.x * a.chunk;
     const int i1 = min(a.vocab, i0 + a.chunk);
+    const int per = a.chunk / kThreads;
+    Tile<VEC4> t;
+    t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
     unsigned long long best = 0;
     if (mode & MODE_GREEDY) {
-        for (int i = i0 + threadIdx.x; i < i1; i += kThreads)
-            best = max(best, pack_key_index(float_key(z[i]), (uint32_t)i));
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) {
+            const int i = Tile<VEC4>::index(i0, j);
+            if (j < per && i < i1) best = max(best, pack_key_index(float_key(t.v[j]), (uint32_t)i));
+        }
     } else {
         const float T = a.temperature[b];
+        const float *g = a.gumbel + (int64_t)b * a.gstride;
         const bool topk = (mode & MODE_TOPK) != 0;
         const bool topp = (mode & (MODE_TOPP | MODE_TOPP_MAX)) != 0;
-        const uint32_t kkey = ctl->k_key, kcut = ctl->k_cut;
-        const uint32_t pkey = (mode & MODE_TOPP) ? ctl->p_key : ctl->max_key;
-        for (int i = i0 + threadIdx.x; i < i1; i += kThreads) {
-            const float s = z[i] / T;
-            const uint32_t key = float_key(s);
-            if (topk && !(key > kkey || (key == kkey && (uint32_t)i <= kcut))) continue;
-            if (topp && key < pkey) continue;
-            const float kappa = s + g[i];
-            best = max(best, pack_key_index(float_key(kappa), (uint32_t)i));
+        if (!topk && !topp) {
+            // every logit is eligible: stream the noise as a tile too
+            Tile<VEC4> gt;
+            gt.load(g, i0, i1, per);
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j) {
+                const int i = Tile<VEC4>::index(i0, j);
+                if (j < per && i < i1) {
+                    const float kappa = t.v[j] / T + gt.v[j];
+                    best = max(best, pack_key_index(float_key(kappa), (uint32_t)i));
+                }
+            }
+        } else {
+            const uint32_t kkey = ctl->k_key, kcut = ctl->k_cut;
+            const uint32_t pkey = (mode & MODE_TOPP) ? ctl->p_key : ctl->max_key;
+            uint32_t kept = 0;
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j) {
+                const int i = Tile<VEC4>::index(i0, j);
+                const float s = t.v[j] / T;
+                const uint32_t key = float_key(s);
+                bool ok = j < per && i < i1;
+                if (topk) ok = ok && (key > kkey || (key == kkey && (uint32_t)i <= kcut));
+                if (topp) ok = ok && key >= pkey;
+                t.v[j] = s;
+                kept |= (ok ? 1u : 0u) << j;
+            }
+            // noise only for the eligible logits, all loads issued together
+            float gv[kMaxPer];
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j)
+                gv[j] = ((kept >> j) & 1u) ? g[Tile<VEC4>::index(i0, j)] : 0.f;
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j)
+                if ((kept >> j) & 1u)
+                    best = max(best, pack_key_index(float_key(t.v[j] + gv[j]),
+                                                    (uint32_t)Tile<VEC4>::index(i0, j)));
         }
     }
     best = block_max(best, s_red);
-    if (threadIdx.x == 0) atomicMax(&ctl->best, best);
-    if (!last_of_row(ctl, &s_flag)) return;
-    if (threadIdx.x == 0) {
-        const unsigned long long v =
-            __hip_atomic_load(&ctl->best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.out_ids[b] = (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffull));
-        ctl->done = 0;
+    if (threadIdx.x == 0 && best) atomicMax(&ctl->best, best);
+}
+
+__global__ __launch_bounds__(kThreads) void samp_write_ids_kernel(const SampArgs a)
+{
+    const int b = blockIdx.x * kThreads + threadIdx.x;
+    if (b >= a.batch) return;
+    const unsigned long long v = a.ctl[b].best;
+    a.out_ids[b] = (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffull));
+}
+
+template <bool VEC4>
+void launch_passes(const SampArgs &a, const dim3 grid, uint32_t flags, hipStream_t stream)
+{
+    if (flags & 2u) samp_max_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
+    if (flags & 1u) {
+        for (int level = 0; level < 3; ++level) {
+            samp_hist_kernel<WHICH_K, VEC4><<<grid, kThreads, 0, stream>>>(a, level);
+            samp_select_kernel<WHICH_K><<<a.batch, kThreads, 0, stream>>>(a, level);
+        }
+        samp_tie_count_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
+        samp_tie_cut_kernel<<<a.batch, kThreads, 0, stream>>>(a);
     }
+    if (flags & 2u)
+        for (int level = 0; level < 3; ++level) {
+            samp_hist_kernel<WHICH_P, VEC4><<<grid, kThreads, 0, stream>>>(a, level);
+            samp_select_kernel<WHICH_P><<<a.batch, kThreads, 0, stream>>>(a, level);
+        }
+    samp_final_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
+    samp_write_ids_kernel<<<(a.batch + kThreads - 1) / kThreads, kThreads, 0, stream>>>(a);
 }
 
 }  // namespace
@@ -485,16 +611,13 @@ hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_
 
     const dim3 grid(L.nchunks, batch);
     samp_init_kernel<<<batch, kThreads, 0, stream>>>(a);
-    if (flags & 2u) samp_max_kernel<<<grid, kThreads, 0, stream>>>(a);
-    if (flags & 1u) {
-        for (int level = 0; level < 3; ++level)
-            samp_hist_kernel<WHICH_K><<<grid, kThreads, 0, stream>>>(a, level);
-        samp_tie_kernel<<<grid, kThreads, 0, stream>>>(a);
-    }
-    if (flags & 2u)
-        for (int level = 0; level < 3; ++level)
-            samp_hist_kernel<WHICH_P><<<grid, kThreads, 0, stream>>>(a, level);
-    samp_final_kernel<<<grid, kThreads, 0, stream>>>(a);
+    const bool vec4 = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && logits_stride % 4 == 0 &&
+                      (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0) && gumbel_stride % 4 == 0 &&
+                      vocab % 4 == 0;
+    if (vec4)
+        launch_passes<true>(a, grid, flags, stream);
+    else
+        launch_passes<false>(a, grid, flags, stream);
     return hipGetLastError();
 }
 

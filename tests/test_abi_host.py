@@ -101,11 +101,12 @@ def test_attention_validation():
 
 def test_workspace_and_split_queries():
     L = _lib.lib()
-    for (B, Hkv, ml) in [(64, 8, 4096), (8, 8, 131072), (4, 16, 513), (32, 8, 2048), (1, 1, 1)]:
-        s = L.pkv_decode_split_tokens(B, Hkv, ml, 0)
+    for (B, Hq, Hkv, ml) in [(64, 16, 8, 4096), (8, 64, 8, 131072), (4, 16, 16, 513),
+                             (32, 48, 8, 2048), (1, 1, 1, 1)]:
+        s = L.pkv_decode_split_tokens(B, Hq, Hkv, ml, 0)
         assert s >= 64 and s % 64 == 0
-        assert L.pkv_decode_split_tokens(B, Hkv, ml, 128) == 128
-    assert L.pkv_decode_split_tokens(4, 4, 100, 100) == 0  # not a multiple of 64
+        assert L.pkv_decode_split_tokens(B, Hq, Hkv, ml, 128) == 128
+    assert L.pkv_decode_split_tokens(4, 4, 4, 100, 100) == 0  # not a multiple of 64
     # workspace: [B][Hq][S][D] + [B][Hq][S][2] fp32, each 256-byte aligned
     B, Hq, Hkv, D, ml, split = 3, 4, 2, 64, 1000, 128
     S = (ml + split - 1) // split
