@@ -42,6 +42,11 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override layer count (0 = workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate slot-mapping and store launches instead of the fused "
+                         "store + attention partial")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (no HIP-graph replay of the step)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run a device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -106,14 +111,24 @@ def main():
     log(f"[bench] inputs resident: {sum(x.numel() * 2 for x in kp + vp) / 1e9:.2f} GB of pools, "
         f"split_tokens={split}")
 
+    fused = not args.unfused
+
     def step(ev=None):
-        pkv.slot_mapping(td, nd, bs, out=slots)
+        if not fused:
+            pkv.slot_mapping(td, nd, bs, out=slots)
         for layer in range(L):
-            pkv.kv_store(kp[layer], vp[layer], kn[layer], vn[layer], slots)
+            if not fused:
+                pkv.kv_store(kp[layer], vp[layer], kn[layer], vn[layer], slots)
             if ev is not None:
                 ev["p0"][layer].record()
-            pkv.decode_attention_partial(q[layer], kp[layer], vp[layer], td, nd, max_len, ws,
-                                         split_tokens=split)
+            if fused:
+                # store of the new K/V fused into the attention partial step
+                pkv.decode_attention_partial_store(q[layer], kp[layer], vp[layer], kn[layer],
+                                                   vn[layer], td, nd, max_len, ws,
+                                                   split_tokens=split)
+            else:
+                pkv.decode_attention_partial(q[layer], kp[layer], vp[layer], td, nd, max_len, ws,
+                                             split_tokens=split)
             if ev is not None:
                 ev["p1"][layer].record()
             pkv.decode_attention_reduce(out, nd, Hkv, tables.shape[1], bs, max_len, ws,
@@ -149,7 +164,33 @@ def main():
     part_ms = [e["p0"][l].elapsed_time(e["p1"][l]) for e in evs for l in range(L)]
     red_ms = [e["p1"][l].elapsed_time(e["r1"][l]) for e in evs for l in range(L)]
     samp_ms = [e["s0"].elapsed_time(e["s1"]) for e in evs]
-    log(f"[bench] timed {args.steps} steps in {total_ms:.2f} ms")
+    log(f"[bench] timed {args.steps} eager steps in {total_ms:.2f} ms")
+    eager_ms_per_step = total_ms / args.steps
+
+    # the same step captured once as a HIP graph and replayed: removes the
+    # host launch gaps between the ~3L+10 kernels of a step
+    graph_ms_per_step = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms_per_step = g0.elapsed_time(g1) / args.steps
+        log(f"[bench] timed {args.steps} graph replays: {graph_ms_per_step:.4f} ms per step")
 
     # algorithmic bytes
     kv_bytes = int(n.astype(np.int64).sum()) * Hkv * D * 2 * 2   # K and V, each element once
@@ -160,11 +201,13 @@ def main():
     red_avg_us = 1e3 * float(np.mean(red_ms))
     attn_us_layer = part_avg_us + red_avg_us
     value = attn_bytes_layer / (attn_us_layer * 1e-6) / 1e9
-    part_gbs = (kv_bytes + q_bytes) / (part_avg_us * 1e-6) / 1e9
-    ms_per_step = total_ms / args.steps
+    store_bytes = 2 * B * Hkv * D * 2 if fused else 0   # new K and V rows written
+    part_bytes = kv_bytes + q_bytes + store_bytes
+    part_gbs = part_bytes / (part_avg_us * 1e-6) / 1e9
+    ms_per_step = graph_ms_per_step if graph_ms_per_step is not None else eager_ms_per_step
     samp_avg_us = 1e3 * float(np.mean(samp_ms))
 
-    traffic = read_traffic(cfg.name)
+    traffic = read_traffic(cfg.name, fused)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -200,13 +243,16 @@ def main():
                    "temperature": cfg.temperature, "top_p": cfg.top_p, "top_k": cfg.top_k},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_steps_per_s": round(1e3 / ms_per_step, 2),
+        "step_timing": "hip_graph_replay" if graph_ms_per_step is not None else "eager",
+        "ms_per_step_eager": round(eager_ms_per_step, 4),
         "sampler_tokens_per_s": round(B / (samp_avg_us * 1e-6), 1),
         "attention_us_per_layer": {"partial": round(part_avg_us, 3), "reduce": round(red_avg_us, 3)},
         "sampler_us": round(samp_avg_us, 3),
-        "roofline": {"kernel": "decode_partial_kernel<128,2>" if cfg.name == "qwen3" else "decode_partial_kernel",
+        "step": "fused store + attention" if fused else "slot mapping, store, attention",
+        "roofline": {"kernel": f"decode_partial_kernel<{D},{min(cfg.group, 8)},{'true' if fused else 'false'}>",
                      "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": kv_bytes + q_bytes,
+                     "bytes_per_launch": part_bytes,
                      "avg_launch_us": round(part_avg_us, 3),
                      "traffic": traffic},
         "cpu_baseline": cpu,
@@ -214,12 +260,13 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def read_traffic(name):
+def read_traffic(name, fused):
     """Measured HBM bytes per launch of the partial kernel, from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"decode_partial_{name}_counters.txt")
+    tag = "fused" if fused else "plain"
+    path = os.path.join(ROOT, "profiles", f"decode_partial_{tag}_{name}_counters.txt")
     src = os.path.join(ROOT, "paged_kv_decode_store_amd", "csrc", "decode_attention.hip")
     if not os.path.exists(path):
         return None

@@ -158,6 +158,52 @@ int pkv_decode_attention_reduce(void *out, int64_t out_stride,
                                 int32_t split_tokens, const void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* ---- fused store + attention ---------------------------------------------
+ * The decode step's store and attention in one pass, the way the pages'
+ * attention kernels write the new K/V into the cache while attending
+ * (nanochat engine page, section 2: the cache is written in place inside the
+ * attention call; nano-vllm page, "prepare Prefill": the attention path
+ * writes the new K/V at slot_mapping).  For each row b with
+ * 1 <= n_b <= max_context_len, position n_b - 1 is the new token: its K/V
+ * rows are taken from k_new/v_new (bf16 [batch][num_kv_heads][head_dim],
+ * row b at b*new_token_stride elements, 0 = packed), written into the pools
+ * at slot block_tables[b][(n_b-1)/block_size]*block_size + (n_b-1)%block_size
+ * (skipped if that block id is outside [0, num_blocks)), and attended from
+ * registers.  The result equals pkv_slot_mapping + pkv_kv_store +
+ * pkv_paged_decode_attention on the same arguments.  Other arguments and the
+ * workspace are as for pkv_paged_decode_attention. */
+int pkv_paged_decode_attention_store(void *out, int64_t out_stride,
+                                     const void *q, int64_t q_stride,
+                                     void *k_cache, void *v_cache,
+                                     const void *k_new, const void *v_new,
+                                     int64_t new_token_stride,
+                                     const int32_t *block_tables,
+                                     int32_t block_table_stride,
+                                     const int32_t *context_lens,
+                                     int32_t batch, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int64_t num_blocks,
+                                     int32_t max_context_len, float scale,
+                                     int32_t split_tokens, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* Partial step of the fused path only (store + partials); finish with
+ * pkv_decode_attention_reduce. */
+int pkv_decode_attention_partial_store(const void *q, int64_t q_stride,
+                                       void *k_cache, void *v_cache,
+                                       const void *k_new, const void *v_new,
+                                       int64_t new_token_stride,
+                                       const int32_t *block_tables,
+                                       int32_t block_table_stride,
+                                       const int32_t *context_lens,
+                                       int32_t batch, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int64_t num_blocks,
+                                       int32_t max_context_len, float scale,
+                                       int32_t split_tokens, void *workspace,
+                                       size_t workspace_bytes,
+                                       hipStream_t stream);
+
 /* ---- sampler --------------------------------------------------------------
  * Next token per row (Grok-1 runners chapter, section 8.3 and 8.3.1;
  * nanochat engine page, section 3; nano-vllm page, "run model"):

@@ -19,6 +19,7 @@ from ._lib import PKV_SAMPLE_TOPK, PKV_SAMPLE_TOPP, PkvError, check, lib
 __all__ = [
     "slot_mapping", "kv_store", "paged_decode_attention", "decode_attention_partial",
     "decode_attention_reduce", "decode_workspace_bytes", "decode_split_tokens",
+    "paged_decode_attention_store", "decode_attention_partial_store",
     "sample_next_token", "sampler_workspace_bytes", "PkvError",
     "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
 ]
@@ -154,6 +155,56 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs, nb, max_context_len,
         scale, split_tokens, ws.data_ptr(), ws.numel(), _stream()), "pkv_paged_decode_attention")
+    return out
+
+
+def _new_rows(k_new, v_new, hkv, D):
+    if k_new.shape[1:] != (hkv, D) or v_new.shape[1:] != (hkv, D):
+        raise ValueError("k_new/v_new must be [B, Hkv, D] matching the pools")
+    if k_new.stride(1) != D or k_new.stride(2) != 1 or v_new.stride() != k_new.stride():
+        raise ValueError("k_new/v_new rows must be packed [Hkv, D] with equal strides")
+    return k_new.stride(0)
+
+
+def decode_attention_partial_store(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+                                   max_context_len, workspace, scale: float = 0.0,
+                                   split_tokens: int = 0) -> None:
+    """Fused store + partial step: row b's new position (context_lens[b]-1)
+    takes its K/V from k_new/v_new [B, Hkv, D] and is written to the pools."""
+    B, Hq, D, nb, bs, hkv = _attn_shapes(q, k_cache, block_tables)
+    ns = _new_rows(k_new, v_new, hkv, D)
+    check(lib().pkv_decode_attention_partial_store(
+        _dev(q, "q", torch.bfloat16), q.stride(0), _dev(k_cache, "k_cache", torch.bfloat16),
+        _dev(v_cache, "v_cache", torch.bfloat16), _dev(k_new, "k_new", torch.bfloat16),
+        _dev(v_new, "v_new", torch.bfloat16), ns, _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs,
+        nb, max_context_len, scale, split_tokens, _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream()), "pkv_decode_attention_partial_store")
+
+
+def paged_decode_attention_store(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 k_new: torch.Tensor, v_new: torch.Tensor,
+                                 block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                 max_context_len: int, scale: float = 0.0, split_tokens: int = 0,
+                                 out: Optional[torch.Tensor] = None,
+                                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fused decode step for one layer: store each row's new K/V at its slot
+    and attend over the n_b positions; equals slot_mapping + kv_store +
+    paged_decode_attention."""
+    B, Hq, D, nb, bs, hkv = _attn_shapes(q, k_cache, block_tables)
+    ns = _new_rows(k_new, v_new, hkv, D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    ws = _workspace(decode_workspace_bytes(B, Hq, hkv, D, max_context_len, split_tokens),
+                    q.device, workspace)
+    check(lib().pkv_paged_decode_attention_store(
+        _dev(out, "out", torch.bfloat16), out.stride(0), _dev(q, "q", torch.bfloat16), q.stride(0),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16), ns,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs, nb, max_context_len,
+        scale, split_tokens, ws.data_ptr(), ws.numel(), _stream()),
+        "pkv_paged_decode_attention_store")
     return out
 
 

@@ -169,13 +169,19 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
     return pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split).total_bytes;
 }
 
-int pkv_decode_attention_partial(const void *q, int64_t q_stride, const void *k_cache,
-                                 const void *v_cache, const int32_t *block_tables,
-                                 int32_t block_table_stride, const int32_t *context_lens,
-                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                 int32_t max_context_len, float scale, int32_t split_tokens,
-                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Checks and fills the partial step's launch arguments; k_new == NULL selects
+// the plain partial, otherwise the fused store + partial.
+int setup_partial(pkv::PartialArgs &a, const void *q, int64_t q_stride, const void *k_cache,
+                  const void *v_cache, const void *k_new, const void *v_new,
+                  int64_t new_token_stride, const int32_t *block_tables,
+                  int32_t block_table_stride, const int32_t *context_lens, int32_t batch,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int64_t num_blocks, int32_t max_context_len, float scale, int32_t split_tokens,
+                  void *workspace, size_t workspace_bytes, bool fused)
 {
     int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                    block_table_stride, max_context_len);
@@ -185,15 +191,27 @@ int pkv_decode_attention_partial(const void *q, int64_t q_stride, const void *k_
     const int64_t qs = q_stride ? q_stride : (int64_t)num_q_heads * head_dim;
     REQUIRE(qs >= (int64_t)num_q_heads * head_dim && qs % 8 == 0, PKV_ERR_INVALID_ARG,
             "q_stride must be >= num_q_heads*head_dim and a multiple of 8");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    const int64_t ns = new_token_stride ? new_token_stride : row;
+    if (fused) {
+        REQUIRE(ns >= row && ns % 8 == 0, PKV_ERR_INVALID_ARG,
+                "new_token_stride must be >= num_kv_heads*head_dim and a multiple of 8");
+    }
     REQUIRE(isfinite(scale), PKV_ERR_INVALID_ARG, "scale must be finite");
     if (batch == 0) return PKV_OK;
     REQUIRE(q && k_cache && v_cache && block_tables && context_lens, PKV_ERR_INVALID_ARG,
             "null pointer");
     REQUIRE(aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16), PKV_ERR_INVALID_ARG,
             "bf16 tensors must be 16-byte aligned");
+    if (fused) {
+        REQUIRE(k_new && v_new, PKV_ERR_INVALID_ARG, "null pointer");
+        REQUIRE(aligned(k_new, 16) && aligned(v_new, 16), PKV_ERR_INVALID_ARG,
+                "bf16 tensors must be 16-byte aligned");
+    }
     REQUIRE(aligned(block_tables, 4) && aligned(context_lens, 4), PKV_ERR_INVALID_ARG,
             "int32 arrays must be 4-byte aligned");
-    const int32_t split = effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
+    const int32_t split =
+        effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
     const pkv::SplitGeometry g =
         pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split);
     REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,
@@ -201,7 +219,6 @@ int pkv_decode_attention_partial(const void *q, int64_t q_stride, const void *k_
     REQUIRE(workspace_bytes >= g.total_bytes, PKV_ERR_WORKSPACE,
             "workspace too small: %zu < %zu bytes", workspace_bytes, g.total_bytes);
 
-    pkv::PartialArgs a;
     a.part_o = static_cast<float *>(workspace);
     a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + g.part_o_bytes);
     a.q = static_cast<const uint16_t *>(q);
@@ -223,7 +240,53 @@ int pkv_decode_attention_partial(const void *q, int64_t q_stride, const void *k_
     a.num_splits = g.num_splits;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
     a.c = sc * 1.4426950408889634f;
+    a.k_new = fused ? static_cast<const uint16_t *>(k_new) : nullptr;
+    a.v_new = fused ? static_cast<const uint16_t *>(v_new) : nullptr;
+    a.new_stride = ns;
+    a.k_cache_w = fused ? static_cast<uint16_t *>(const_cast<void *>(k_cache)) : nullptr;
+    a.v_cache_w = fused ? static_cast<uint16_t *>(const_cast<void *>(v_cache)) : nullptr;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_attention_partial(const void *q, int64_t q_stride, const void *k_cache,
+                                 const void *v_cache, const int32_t *block_tables,
+                                 int32_t block_table_stride, const int32_t *context_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                 int32_t max_context_len, float scale, int32_t split_tokens,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    pkv::PartialArgs a;
+    int rc = setup_partial(a, q, q_stride, k_cache, v_cache, nullptr, nullptr, 0, block_tables,
+                           block_table_stride, context_lens, batch, num_q_heads, num_kv_heads,
+                           head_dim, block_size, num_blocks, max_context_len, scale,
+                           split_tokens, workspace, workspace_bytes, false);
+    if (rc || batch == 0) return rc;
     return hip_status(pkv::launch_decode_partial(a, head_dim, stream), "decode partial launch");
+}
+
+int pkv_decode_attention_partial_store(const void *q, int64_t q_stride, void *k_cache,
+                                       void *v_cache, const void *k_new, const void *v_new,
+                                       int64_t new_token_stride, const int32_t *block_tables,
+                                       int32_t block_table_stride, const int32_t *context_lens,
+                                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                       int32_t max_context_len, float scale,
+                                       int32_t split_tokens, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream)
+{
+    pkv::PartialArgs a;
+    int rc = setup_partial(a, q, q_stride, k_cache, v_cache, k_new, v_new, new_token_stride,
+                           block_tables, block_table_stride, context_lens, batch, num_q_heads,
+                           num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                           scale, split_tokens, workspace, workspace_bytes, true);
+    if (rc || batch == 0) return rc;
+    return hip_status(pkv::launch_decode_partial(a, head_dim, stream),
+                      "decode partial (store) launch");
 }
 
 int pkv_decode_attention_reduce(void *out, int64_t out_stride, const int32_t *context_lens,
@@ -288,6 +351,34 @@ int pkv_paged_decode_attention(void *out, int64_t out_stride, const void *q, int
                                           num_kv_heads, head_dim, block_size, num_blocks,
                                           max_context_len, scale, split_tokens, workspace,
                                           workspace_bytes, stream);
+    if (rc) return rc;
+    return pkv_decode_attention_reduce(out, out_stride, context_lens, batch, num_q_heads,
+                                       num_kv_heads, head_dim, block_table_stride, block_size,
+                                       max_context_len, split_tokens, workspace, workspace_bytes,
+                                       stream);
+}
+
+int pkv_paged_decode_attention_store(void *out, int64_t out_stride, const void *q,
+                                     int64_t q_stride, void *k_cache, void *v_cache,
+                                     const void *k_new, const void *v_new,
+                                     int64_t new_token_stride, const int32_t *block_tables,
+                                     int32_t block_table_stride, const int32_t *context_lens,
+                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                     int32_t max_context_len, float scale, int32_t split_tokens,
+                                     void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const int64_t os = out_stride ? out_stride : (int64_t)num_q_heads * head_dim;
+    if (batch > 0) {
+        REQUIRE(out && aligned(out, 16), PKV_ERR_INVALID_ARG,
+                "out must be non-null and 16-byte aligned");
+    }
+    REQUIRE(num_q_heads > 0 && (os >= (int64_t)num_q_heads * head_dim) && os % 8 == 0,
+            PKV_ERR_INVALID_ARG, "out_stride must be >= num_q_heads*head_dim and a multiple of 8");
+    int rc = pkv_decode_attention_partial_store(
+        q, q_stride, k_cache, v_cache, k_new, v_new, new_token_stride, block_tables,
+        block_table_stride, context_lens, batch, num_q_heads, num_kv_heads, head_dim, block_size,
+        num_blocks, max_context_len, scale, split_tokens, workspace, workspace_bytes, stream);
     if (rc) return rc;
     return pkv_decode_attention_reduce(out, out_stride, context_lens, batch, num_q_heads,
                                        num_kv_heads, head_dim, block_table_stride, block_size,

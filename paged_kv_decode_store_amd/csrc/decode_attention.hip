@@ -26,7 +26,7 @@ constexpr int kWaves = 4;                 // waves per partial workgroup
 constexpr int kChunk = 16;                // positions per wave iteration
 constexpr int kRound = kWaves * kChunk;   // positions per workgroup iteration
 
-template <int D, int G>
+template <int D, int G, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const PartialArgs a)
 {
     constexpr int LPT = D / 8;        // lanes per position
@@ -47,9 +47,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     const int b = x % a.batch;
     const int s = x / a.batch;
 
-    const int n = min(max(a.context_lens[b], 0), a.max_len);
+    const int n_row = a.context_lens[b];
+    const int n = min(max(n_row, 0), a.max_len);
     const int t_begin = s * a.split_tokens;
     if (t_begin >= n) return;
+    // fused store: the row's new position, if it lies inside the attended range
+    const int pos_new = (FUSED && n_row >= 1 && n_row <= n) ? n_row - 1 : -1;
     const int t_end = min(n, t_begin + a.split_tokens);
     const int h0 = kvh * a.group + hc * G;
     const float c = a.c;
@@ -78,10 +81,32 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     // Issue the K/V loads of the chunk starting at t0 (one block, U positions
     // per lane group, one 16-byte piece per lane and position).
     auto load_chunk = [&](int t0, uint4 (&kr)[U], uint4 (&vr)[U]) {
-        int blk = table[t0 >> a.bs_log2];
-        blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+        const int raw = table[t0 >> a.bs_log2];
+        const bool blk_ok = raw >= 0 && raw < a.num_blocks;
+        const int blk = blk_ok ? raw : 0;
         const int64_t base =
             (((int64_t)blk << a.bs_log2) + (t0 & bs_mask)) * tok_stride + lane_off;
+        if (FUSED && pos_new >= t0 && pos_new < t0 + kChunk) {
+            // this chunk holds the new position: its K/V come from k_new/v_new,
+            // and the first query-head chunk stores them in the pools
+            const int64_t noff = (int64_t)b * a.new_stride + (int64_t)kvh * D + li * 8;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t off = base + u * tok_stride;
+                if (t0 + gi * U + u == pos_new) {
+                    kr[u] = *reinterpret_cast<const uint4 *>(a.k_new + noff);
+                    vr[u] = *reinterpret_cast<const uint4 *>(a.v_new + noff);
+                    if (hc == 0 && blk_ok) {
+                        *reinterpret_cast<uint4 *>(a.k_cache_w + off) = kr[u];
+                        *reinterpret_cast<uint4 *>(a.v_cache_w + off) = vr[u];
+                    }
+                } else {
+                    kr[u] = load_stream16(a.k_cache + off);
+                    vr[u] = load_stream16(a.v_cache + off);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
             kr[u] = load_stream16(a.k_cache + base + u * tok_stride);
@@ -244,7 +269,22 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
 #pragma unroll
     for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
     const float *po = a.part_o + base * D + lane * DPL;
-    for (int s = 0; s < ns; ++s) {
+    // four splits per step so that their loads are in flight together
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+        float w[4], v[4][DPL];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            w[k] = __builtin_amdgcn_exp2f(ml[2 * (s + k)] - M);
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) v[k][j] = po[(int64_t)(s + k) * D + j];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) acc[j] += w[k] * v[k][j];
+    }
+    for (; s < ns; ++s) {
         const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
 #pragma unroll
         for (int j = 0; j < DPL; ++j) acc[j] += w * po[(int64_t)s * D + j];
@@ -301,7 +341,10 @@ static void launch_partial_g(const PartialArgs &a, hipStream_t stream)
 {
     const int64_t grid =
         (int64_t)a.num_splits * a.batch * a.num_kv_heads * a.head_chunks;
-    decode_partial_kernel<D, G><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
+    if (a.k_new)
+        decode_partial_kernel<D, G, true><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
+    else
+        decode_partial_kernel<D, G, false><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
 }
 
 template <int D>

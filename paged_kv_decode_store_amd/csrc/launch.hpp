@@ -52,6 +52,14 @@ struct PartialArgs {
     int32_t split_tokens;
     int32_t num_splits;
     float c;                // softmax scale * log2(e)
+    // fused store: when k_new is non-null, each row's new position
+    // (context_lens[b] - 1) takes its K/V from k_new/v_new and the first
+    // query-head chunk writes them into the pools
+    const uint16_t *k_new;
+    const uint16_t *v_new;
+    int64_t new_stride;     // elements between consecutive rows of k_new/v_new
+    uint16_t *k_cache_w;    // same pools as k_cache/v_cache, written by the fused store
+    uint16_t *v_cache_w;
 };
 
 struct ReduceArgs {

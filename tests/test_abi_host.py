@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.PROTOTYPES)
@@ -148,3 +148,23 @@ def test_binding_refuses_cpu_tensors():
     lens = torch.ones(2, dtype=torch.int32)
     with pytest.raises(ValueError):
         pkv.slot_mapping(bt, lens, 256, out=torch.empty(2, dtype=torch.int32))
+
+
+def test_fused_attention_validation():
+    L = _lib.lib()
+    need = L.pkv_decode_workspace_bytes(64, 16, 8, 128, 4096, 0)
+
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, ns=0, bt=FAKE, lens=FAKE,
+                 ws=FAKE, wsb=need)
+        a.update(kw)
+        return L.pkv_paged_decode_attention_store(a["out"], 0, a["q"], 0, a["k"], a["v"], a["kn"],
+                                                  a["vn"], a["ns"], a["bt"], 16, a["lens"], 64, 16,
+                                                  8, 128, 256, 600, 4096, 0.0, 0, a["ws"], a["wsb"],
+                                                  None)
+
+    assert call(kn=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(vn=FAKE + 4) == _lib.PKV_ERR_INVALID_ARG
+    assert call(ns=8 * 128 - 8) == _lib.PKV_ERR_INVALID_ARG
+    assert call(out=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE

@@ -337,3 +337,90 @@ def test_sampler_top_k_ties_across_chunks():
     bad, amb, infos = _sample_and_compare(z, g, t, p, k)
     assert not bad
     assert [i.kept for i in infos] == k.tolist()
+
+
+# ------------------------------------------------ fused store + attention --
+
+def _fused_case(rng, B, Hq, Hkv, D, bs, lens, split, spare=3):
+    lens = np.asarray(lens, np.int32)
+    need = [(int(n) + bs - 1) // bs for n in lens]
+    W = max(1, max(need))
+    nb = sum(need) + spare
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((B, W), -1, np.int32)
+    pos = 0
+    for b in range(B):
+        tables[b, :need[b]] = perm[pos:pos + need[b]]
+        pos += need[b]
+    kp, vp = _normal_bf16(rng, (nb, bs, Hkv, D)), _normal_bf16(rng, (nb, bs, Hkv, D))
+    kn, vn = _normal_bf16(rng, (B, Hkv, D)), _normal_bf16(rng, (B, Hkv, D))
+    q = _normal_bf16(rng, (B, Hq, D))
+    maxlen = int(max(1, lens.max()))
+    say(f"fused B={B} Hq={Hq} Hkv={Hkv} D={D} bs={bs} split={split} lens={lens.tolist()}")
+    kc, vc = dev_u16(kp), dev_u16(vp)
+    out = pkv.paged_decode_attention_store(dev_u16(q), kc, vc, dev_u16(kn), dev_u16(vn),
+                                           dev_i32(tables), dev_i32(lens), maxlen,
+                                           split_tokens=split)
+    torch.cuda.synchronize()
+    kref, vref = kp.copy(), vp.copy()
+    slots = oracle.slot_mapping(tables, lens, bs)
+    oracle.kv_store(kref, vref, kn, vn, slots, bs)
+    ref = oracle.decode_attention(q, kref, vref, tables, lens)
+    return bf16_out_to_f64(out), ref, host_u16(kc), host_u16(vc), kref, vref
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,bs,split", [
+    (128, 16, 8, 256, 0), (128, 8, 2, 16, 64), (64, 16, 16, 32, 128), (128, 16, 1, 16, 64),
+    (128, 22, 2, 64, 192), (64, 12, 4, 16, 0), (128, 48, 8, 256, 512)])
+def test_fused_store_attention_matches_store_then_attend(D, Hq, Hkv, bs, split):
+    """Ragged rows including n = 0, n = 1, new tokens at the first and last
+    position of a block and of a 16-position chunk."""
+    rng = np.random.default_rng(3000 + D + Hq + bs + split)
+    lens = [0, 1, 2, 16, 17, 32, 33, bs, bs + 1, 2 * bs - 1, 700, 1025]
+    got, ref, kh, vh, kref, vref = _fused_case(rng, len(lens), Hq, Hkv, D, bs, lens, split)
+    assert np.array_equal(kh, kref) and np.array_equal(vh, vref)
+    err = np.abs(got - ref).max()
+    assert err <= ATTN_TOL, err
+    assert np.all(got[0] == 0.0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "grok", "clone"])
+def test_fused_decode_step_workloads_full(name):
+    cfg = config_by_name(name)
+    inp = host_inputs(cfg, layers=(0,), sampler=False)
+    n, t = inp.context_lens, inp.block_tables
+    kc, vc = dev_u16(inp.k_pool[0]), dev_u16(inp.v_pool[0])
+    say(f"fused decode step {name}")
+    out = pkv.paged_decode_attention_store(dev_u16(inp.q[0]), kc, vc, dev_u16(inp.k_new[0]),
+                                           dev_u16(inp.v_new[0]), dev_i32(t), dev_i32(n),
+                                           int(n.max()))
+    torch.cuda.synchronize()
+    kref, vref = inp.k_pool[0].copy(), inp.v_pool[0].copy()
+    oracle.kv_store(kref, vref, inp.k_new[0], inp.v_new[0],
+                    oracle.slot_mapping(t, n, cfg.block_size), cfg.block_size)
+    assert np.array_equal(host_u16(kc), kref) and np.array_equal(host_u16(vc), vref)
+    ref = oracle.decode_attention(inp.q[0], kref, vref, t, n)
+    err = np.abs(bf16_out_to_f64(out) - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+def test_fused_decode_step_qwen3_layer():
+    cfg = config_by_name("qwen3")
+    inp = host_inputs(cfg, layers=(5,), pools=False, sampler=False)
+    n, t = inp.context_lens, inp.block_tables
+    kc, vc = _device_layer(cfg, inp, 5)
+    k0, v0 = host_u16(kc), host_u16(vc)
+    say("fused decode step qwen3 layer 5")
+    out = pkv.paged_decode_attention_store(dev_u16(inp.q[0]), kc, vc, dev_u16(inp.k_new[0]),
+                                           dev_u16(inp.v_new[0]), dev_i32(t), dev_i32(n),
+                                           int(n.max()))
+    torch.cuda.synchronize()
+    kref, vref = k0, v0
+    oracle.kv_store(kref, vref, inp.k_new[0], inp.v_new[0],
+                    oracle.slot_mapping(t, n, cfg.block_size), cfg.block_size)
+    assert np.array_equal(host_u16(kc), kref) and np.array_equal(host_u16(vc), vref)
+    ref = oracle.decode_attention(inp.q[0], kref, vref, t, n)
+    err = np.abs(bf16_out_to_f64(out) - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_TOL
