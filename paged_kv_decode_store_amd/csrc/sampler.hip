@@ -4,20 +4,35 @@
 // Row-parallel passes split each row into chunks of `chunk` logits, one
 // 256-thread workgroup per (chunk, row).  Each thread first loads its whole
 // share of the chunk into registers (float4 when rows are 16-byte aligned)
-// and then recomputes s = z / T (IEEE division) and the order-preserving
-// 32-bit key of s.  Thresholds come from a three-level radix select on the
-// key (11 + 11 + 10 bits): a histogram pass counts the keys that match the
-// prefix chosen so far into 2048 digits (global atomics), and a per-row
-// select kernel (one workgroup per row) scans the histogram and fixes the
-// next digit.  Top-k ranks by count; top-p accumulates the mass exp(s - max)
-// in 2^-40 fixed point, so the sums are exact, independent of order and
-// identical from run to run.  A top-k tie at the k-th key is cut by index
-// with one more count pass.  The final pass takes the argmax of
-// fl32(s + g) over the eligible logits as a 64-bit atomic max of
-// (key, ~index), which resolves ties to the lowest index.
+// and recomputes s = z / T (IEEE division) and the order-preserving 32-bit
+// key of s.
 //
+// Rows with a top-k or nucleus filter take three passes over their logits:
+//   max     the row max M of s
+//   bins    a histogram over 2048 value bins of width 1/32 below M
+//           (bin = floor(fl(M - s) * 32), the last bin catching everything
+//           >= 64 below M), with counts and the mass exp(s - M) in 2^-40
+//           fixed point: exact, order independent and identical from run
+//           to run
+//   collect every logit in a bin above the threshold bin is eligible: its
+//           Gumbel key fl32(s + g) joins a max of the packed 64-bit
+//           (key, ~index) (ties to the lowest index); the logits of the
+//           threshold bin itself are appended to a per-row candidate list
+// and two per-row kernels: `select` finds the threshold bin from the
+// histogram, `resolve` ranks the candidates (by counting when there are at
+// most 512, else by a bitonic sort in LDS) and fixes the exact cut inside
+// that bin (by rank for top-k, by strictly-greater mass for the nucleus),
+// then writes the id.  Top-k followed by the nucleus may need one more
+// collect/resolve round when the nucleus cut lies above the top-k bin.  If a
+// threshold bin holds more candidates than the list, `resolve` finds the cut
+// exactly by scanning the row itself (radix select on the key).
+//
+// Greedy rows (T <= 0) and rows without a filter need only the collect pass.
 // Passes communicate only through kernel boundaries: no workgroup waits for
-// or fences against another one inside a kernel.
+// or fences against another one inside a kernel.  Per-chunk results (row
+// max, best Gumbel key) go to per-chunk slots that the next kernel reduces,
+// so no pass needs memory cleared beforehand except the histograms, which
+// the max pass clears.
 #include <math.h>
 
 #include "launch.hpp"
@@ -27,35 +42,45 @@ namespace pkv {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kDigits = 2048;
-constexpr int kDigitsPerThread = kDigits / kThreads;
-constexpr int kMaxPer = 32;  // logits per thread per chunk (chunk <= 8192)
+constexpr int kThreads = 256;           // row-parallel passes
+constexpr int kRThreads = 512;          // per-row select / resolve
+constexpr int kBins = 2048;             // value bins below the row max
+constexpr float kBinsPerUnit = 32.f;    // bin width: 1/32 of a logit unit
+constexpr int kCap = 4096;              // threshold-bin candidates kept per row
+constexpr int kMaxPer = 32;             // logits per thread per chunk (bit masks: <= 32)
+constexpr int kDigits = 2048;           // radix digits of the exact in-row fallback
+constexpr int kMinGroups = 256;         // row-parallel workgroups wanted (one per CU)
+constexpr int kList = 1024;             // compacted noise reads per collect workgroup
+constexpr uint32_t kCandBit = 0x80000000u;
+constexpr uint32_t kKeptBit = 0x40000000u;
+constexpr uint32_t kIndexMask = 0x3fffffffu;  // vocab < 2^30
 
-enum : uint32_t { MODE_GREEDY = 1, MODE_TOPK = 2, MODE_TOPP = 4, MODE_TOPP_MAX = 8 };
-enum : int { WHICH_K = 0, WHICH_P = 1 };
+enum : uint32_t {
+    MODE_GREEDY = 1,     // T <= 0: lowest index of the max raw logit
+    MODE_PLAIN = 2,      // T > 0 and no filter: every token eligible
+    MODE_TOPK = 4,
+    MODE_TOPP = 8,
+    MODE_TOPP_MAX = 16,  // p <= 0: only the maxima are eligible
+    MODE_DONE = 32,      // id written
+};
 
 struct alignas(64) SampCtl {
-    unsigned long long best;  // packed (key, ~index) of the draw
-    unsigned long long Z;     // kept mass, 2^-40 units
-    unsigned long long A;     // mass strictly above the current top-p bucket
+    unsigned long long Z;     // eligible mass, 2^-40 units
+    unsigned long long A;     // mass of the bins above the threshold bin
     uint32_t max_key;         // key of max s
-    uint32_t pad;
     uint32_t mode;
-    uint32_t k_prefix;        // top-k: digits fixed so far
-    uint32_t k_rank;          // rank still needed inside the prefix bucket
-    uint32_t k_key;           // key of the k-th largest s
-    uint32_t k_cut;           // last kept index among keys == k_key
-    uint32_t k_tie;           // equal keys still to keep, when a cut is needed
-    uint32_t p_prefix;        // top-p: digits fixed so far
-    uint32_t p_key;           // key of tau
+    uint32_t k;               // top-k
+    uint32_t jstar;           // threshold bin
+    uint32_t rank;            // top-k: logits of the threshold bin to keep
+    uint32_t ncand;           // logits of the threshold bin appended
+    uint32_t round2;          // 1 while a second collect round is pending
 };
 static_assert(sizeof(SampCtl) == 64, "control block");
 
 struct SampLayout {
     int32_t chunk;
     int32_t nchunks;
-    size_t ctl_off, cnt_off, mass_off, chunk_off, total;
+    size_t ctl_off, cnt_off, mass_off, cand_off, kap_off, pmax_off, pbest_off, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -63,20 +88,26 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 SampLayout sampler_layout(int32_t batch, int32_t vocab)
 {
     SampLayout L;
-    // the largest chunk that still gives >= 1024 workgroups per pass
-    int32_t chunk = 8192;
-    while (chunk > 1024 && (int64_t)batch * ((vocab + chunk - 1) / chunk) < 1024) chunk >>= 1;
+    // the largest chunk that still gives kMinGroups workgroups per pass
+    int32_t chunk = kMaxPer * kThreads;
+    while (chunk > 4 * kThreads && (int64_t)batch * ((vocab + chunk - 1) / chunk) < kMinGroups) chunk >>= 1;
     L.chunk = chunk;
     L.nchunks = (vocab + chunk - 1) / chunk;
     size_t off = 0;
     L.ctl_off = off;
     off = align256(off + (size_t)batch * sizeof(SampCtl));
     L.cnt_off = off;
-    off = align256(off + (size_t)batch * kDigits * sizeof(uint32_t));
+    off = align256(off + (size_t)batch * kBins * sizeof(uint32_t));
     L.mass_off = off;
-    off = align256(off + (size_t)batch * kDigits * sizeof(unsigned long long));
-    L.chunk_off = off;
+    off = align256(off + (size_t)batch * kBins * sizeof(unsigned long long));
+    L.cand_off = off;
+    off = align256(off + (size_t)batch * kCap * sizeof(unsigned long long));
+    L.kap_off = off;
+    off = align256(off + (size_t)batch * kCap * sizeof(uint32_t));
+    L.pmax_off = off;
     off = align256(off + (size_t)batch * L.nchunks * sizeof(uint32_t));
+    L.pbest_off = off;
+    off = align256(off + (size_t)batch * L.nchunks * sizeof(unsigned long long));
     L.total = off;
     return L;
 }
@@ -93,9 +124,12 @@ struct SampArgs {
     int32_t batch, vocab, chunk, nchunks;
     uint32_t flags;
     SampCtl *ctl;
-    uint32_t *cnt;
-    unsigned long long *mass;
-    uint32_t *chunk_cnt;
+    uint32_t *cnt;                 // [B][kBins]
+    unsigned long long *mass;      // [B][kBins]
+    unsigned long long *cand;      // [B][kCap]  (key << 32) | ~index
+    uint32_t *kap;                 // [B][kCap]  key of fl32(s + g)
+    uint32_t *part_max;            // [B][nchunks] key of the chunk max of s
+    unsigned long long *part_best; // [B][nchunks] best packed Gumbel key of the chunk
 };
 
 __device__ __forceinline__ unsigned long long pack_key_index(uint32_t key, uint32_t i)
@@ -103,66 +137,111 @@ __device__ __forceinline__ unsigned long long pack_key_index(uint32_t key, uint3
     return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - i);
 }
 
-// exp(s - M) in 2^-40 fixed point; the fp32 rounding error of s - M is
-// recovered exactly (TwoSum) and folded in to first order.
+__device__ __forceinline__ uint32_t unpack_index(unsigned long long v)
+{
+    return 0xffffffffu - (uint32_t)(v & 0xffffffffull);
+}
+
+// exp(s - M) in 2^-40 fixed point, by the hardware base-2 exponential.  The
+// rounding errors of d = s - M (TwoSum) and of d * log2(e) (FMA residual)
+// are recovered exactly and folded in to first order.  The fixed-point value
+// is assembled from two 20-bit halves (w < 2, so w * 2^40 < 2^41).
 __device__ __forceinline__ unsigned long long mass_fixed(float s, float M)
 {
+    constexpr float kLog2e = 1.44269504088896341f;
+    constexpr float kLn2 = 0.693147180559945309f;
     const float d = s - M;
     const float bb = d - s;
     const float e = (s - (d - bb)) + (-M - bb);
-    float w = expf(d);
-    w = fmaf(w, e, w);
-    return (unsigned long long)(w * 1099511627776.0f);
+    const float x = d * kLog2e;
+    const float xe = fmaf(d, kLog2e, -x);
+    float w = __builtin_amdgcn_exp2f(x);
+    w = fmaf(w, fmaf(xe, kLn2, e), w);
+    const float hi = floorf(w * 1048576.0f);             // w * 2^20, integer part
+    const float lo = (w * 1048576.0f - hi) * 1048576.0f; // exact remainder, * 2^20
+    return ((unsigned long long)(uint32_t)hi << 20) + (uint32_t)lo;
+}
+
+// Value bin below the row max M: monotone non-increasing in s (rounding of
+// M - s is monotone, the scale is a power of two).
+__device__ __forceinline__ int bin_of(float s, float M)
+{
+    const float d = (M - s) * kBinsPerUnit;
+    return d < (float)(kBins - 1) ? (int)d : kBins - 1;
+}
+
+// Block-wide reductions and scans: within each wave by lane shuffles, then
+// one exchange of the per-wave results through `scratch` (>= NT / 64
+// entries).  Every thread gets the result; `scratch` is free again on return.
+template <typename T>
+__device__ __forceinline__ T wave_sum_t(T v)
+{
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m);
+    return v;
 }
 
 template <typename T>
+__device__ __forceinline__ T wave_max_t(T v)
+{
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) v = max(v, __shfl_xor(v, m));
+    return v;
+}
+
+// Sum over aligned groups of q consecutive lanes (q a power of two <= 64).
+template <typename T>
+__device__ __forceinline__ T group_sum_lanes(T v, int q)
+{
+    for (int m = 1; m < q; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+template <typename T, int NT>
 __device__ T block_sum(T v, T *scratch)
 {
+    v = wave_sum_t(v);
     __syncthreads();
-    scratch[threadIdx.x] = v;
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
     __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off) scratch[threadIdx.x] += scratch[threadIdx.x + off];
-        __syncthreads();
-    }
-    const T r = scratch[0];
+    T r = scratch[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) r += scratch[w];
     __syncthreads();
     return r;
 }
 
-template <typename T>
+template <typename T, int NT>
 __device__ T block_max(T v, T *scratch)
 {
+    v = wave_max_t(v);
     __syncthreads();
-    scratch[threadIdx.x] = v;
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
     __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off)
-            scratch[threadIdx.x] = max(scratch[threadIdx.x], scratch[threadIdx.x + off]);
-        __syncthreads();
-    }
-    const T r = scratch[0];
+    T r = scratch[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) r = max(r, scratch[w]);
     __syncthreads();
     return r;
 }
 
-// Inclusive scan over threads, ascending (REVERSE = false) or descending.
-template <typename T, bool REVERSE>
+// Inclusive scan over the threads in ascending order.
+template <typename T, int NT>
 __device__ T block_scan_inclusive(T v, T *scratch)
 {
-    __syncthreads();
-    const int t = REVERSE ? kThreads - 1 - (int)threadIdx.x : (int)threadIdx.x;
-    scratch[t] = v;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const T add = (t >= off) ? scratch[t - off] : T(0);
-        __syncthreads();
-        scratch[t] += add;
-        __syncthreads();
+    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const T u = __shfl_up(v, (unsigned)off);
+        if (lane >= off) v += u;
     }
-    const T r = scratch[t];
     __syncthreads();
-    return r;
+    if (lane == 63) scratch[wave] = v;
+    __syncthreads();
+    T base = 0;
+    for (int w = 0; w < wave; ++w) base += scratch[w];
+    __syncthreads();
+    return v + base;
 }
 
 // Each thread's share of one chunk (chunk / 256 <= 32 logits), loaded into
@@ -204,291 +283,208 @@ struct Tile {
     }
 };
 
-__global__ __launch_bounds__(kThreads) void samp_init_kernel(const SampArgs a)
+// What a row needs, from its own settings and the enabled filters.
+__device__ __forceinline__ uint32_t row_mode(const SampArgs &a, int b)
 {
-    const int b = blockIdx.x;
-    for (int d = threadIdx.x; d < kDigits; d += kThreads) {
-        a.cnt[(int64_t)b * kDigits + d] = 0;
-        a.mass[(int64_t)b * kDigits + d] = 0;
+    const float T = a.temperature[b];
+    if (!(T > 0.f)) return MODE_GREEDY;
+    const int32_t k = a.top_k[b];
+    const float p = a.top_p[b];
+    uint32_t mode = 0;
+    if ((a.flags & 1u) && k > 0 && k < a.vocab) mode |= MODE_TOPK;
+    if ((a.flags & 2u) && p < 1.f) {
+        if (!(p > 0.f)) return MODE_TOPP_MAX;  // the maxima are always in the top k
+        mode |= MODE_TOPP;
     }
-    if (threadIdx.x == 0) {
-        SampCtl c = {};
-        const float T = a.temperature[b];
-        if (!(T > 0.f)) {
-            c.mode = MODE_GREEDY;
-        } else {
-            const int32_t k = a.top_k[b];
-            if ((a.flags & 1u) && k > 0 && k < a.vocab) {
-                c.mode |= MODE_TOPK;
-                c.k_rank = (uint32_t)k;
-            }
-            const float p = a.top_p[b];
-            if ((a.flags & 2u) && p < 1.f) c.mode |= (p > 0.f) ? MODE_TOPP : MODE_TOPP_MAX;
-        }
-        c.k_cut = 0xffffffffu;
-        a.ctl[b] = c;
-    }
+    return mode ? mode : MODE_PLAIN;
 }
 
-// max key of s over the row (needed for top-p masses and the p <= 0 case)
+// First pass of filtered sampling: per-chunk max of s.  Chunk 0 of each row
+// also sets up the row's control block, and the chunks of a filtered row
+// clear its histogram between them.
 template <bool VEC4>
 __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
-    SampCtl *ctl = a.ctl + b;
-    if (!(ctl->mode & (MODE_TOPP | MODE_TOPP_MAX))) return;
-    __shared__ uint32_t s_red[kThreads];
-    const float T = a.temperature[b];
     const int i0 = blockIdx.x * a.chunk;
     const int i1 = min(a.vocab, i0 + a.chunk);
     const int per = a.chunk / kThreads;
+    // issued before the row's settings are known, so that the two overlap
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
+    const uint32_t mode = row_mode(a, b);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        SampCtl c = {};
+        c.mode = mode;
+        c.k = (uint32_t)a.top_k[b];
+        c.jstar = kBins;
+        a.ctl[b] = c;
+    }
+    if (!(mode & (MODE_TOPK | MODE_TOPP | MODE_TOPP_MAX))) return;
+    if (mode & (MODE_TOPK | MODE_TOPP)) {
+        for (int d = (int)(blockIdx.x * kThreads + threadIdx.x); d < kBins; d += (int)(gridDim.x * kThreads)) {
+            a.cnt[(int64_t)b * kBins + d] = 0;
+            a.mass[(int64_t)b * kBins + d] = 0;
+        }
+    }
+    __shared__ uint32_t s_red[kThreads / 64];
+    const float T = a.temperature[b];
     uint32_t kmax = 0;
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j)
         if (j < per && Tile<VEC4>::index(i0, j) < i1) kmax = max(kmax, float_key(t.v[j] / T));
-    kmax = block_max(kmax, s_red);
-    if (threadIdx.x == 0) atomicMax(&ctl->max_key, kmax);
+    kmax = block_max<uint32_t, kThreads>(kmax, s_red);
+    if (threadIdx.x == 0) a.part_max[(int64_t)b * a.nchunks + blockIdx.x] = kmax;
 }
 
-// One radix level: histogram of the digit (key >> shift) & mask over the
-// keys that match the prefix fixed so far.
-template <int WHICH, bool VEC4>
-__global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a, int level)
+// Key of the row max of s, from the per-chunk maxima.
+template <int NT>
+__device__ uint32_t row_max_key(const SampArgs &a, int b, uint32_t *scratch)
+{
+    const uint32_t *pm = a.part_max + (int64_t)b * a.nchunks;
+    uint32_t k = 0;
+    for (int c = threadIdx.x; c < a.nchunks; c += NT) k = max(k, pm[c]);
+    return block_max<uint32_t, NT>(k, scratch);
+}
+
+// Counts (and, for the nucleus, masses) per value bin below the row max.
+template <bool VEC4>
+__global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
     SampCtl *ctl = a.ctl + b;
-    const uint32_t mode = ctl->mode;
-    if (WHICH == WHICH_K && !(mode & MODE_TOPK)) return;
-    if (WHICH == WHICH_P && !(mode & MODE_TOPP)) return;
-
-    __shared__ uint32_t s_cnt[kDigits];
-    __shared__ unsigned long long s_mass[WHICH == WHICH_P ? kDigits : 1];
-    __shared__ unsigned long long s_red[kThreads];
-
-    const float T = a.temperature[b];
     const int i0 = blockIdx.x * a.chunk;
     const int i1 = min(a.vocab, i0 + a.chunk);
     const int per = a.chunk / kThreads;
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
-
-    for (int d = threadIdx.x; d < kDigits; d += kThreads) {
+    const uint32_t mode = ctl->mode;
+    if (!(mode & (MODE_TOPK | MODE_TOPP))) return;
+    __shared__ uint32_t s_cnt[kBins];
+    __shared__ unsigned long long s_mass[kBins];
+    __shared__ unsigned long long s_red[kThreads / 64];
+    const float T = a.temperature[b];
+    for (int d = threadIdx.x; d < kBins; d += kThreads) {
         s_cnt[d] = 0;
-        if (WHICH == WHICH_P) s_mass[d] = 0;
+        s_mass[d] = 0;
     }
-    __syncthreads();
-
-    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const int width = level == 2 ? 10 : 11;
-    const int hi = shift + width;
-    const uint32_t dmask = (1u << width) - 1u;
-    const uint32_t prefix = WHICH == WHICH_K ? ctl->k_prefix : ctl->p_prefix;
-    const float M = key_float(ctl->max_key);
-    const uint32_t kkey = ctl->k_key, kcut = ctl->k_cut;
-    const bool topk = (mode & MODE_TOPK) != 0;
-
+    const float M = key_float(row_max_key<kThreads>(a, b, reinterpret_cast<uint32_t *>(s_red)));
+    const bool want_mass = (mode & MODE_TOPP) != 0;
     unsigned long long zloc = 0;
+    uint32_t tail = 0;
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) {
-        const int i = Tile<VEC4>::index(i0, j);
-        if (j >= per || i >= i1) continue;
+        if (j >= per || Tile<VEC4>::index(i0, j) >= i1) continue;
         const float s = t.v[j] / T;
-        const uint32_t key = float_key(s);
-        if (hi < 32 && (key >> hi) != (prefix >> hi)) continue;
-        if (WHICH == WHICH_P && topk && !(key > kkey || (key == kkey && (uint32_t)i <= kcut)))
+        const int bin = bin_of(s, M);
+        if (bin == kBins - 1) {
+            // >= 64 below the max: mass exp(-64) is below the fixed-point unit
+            ++tail;
             continue;
-        const uint32_t d = (key >> shift) & dmask;
-        atomicAdd(&s_cnt[d], 1u);
-        if (WHICH == WHICH_P) {
+        }
+        atomicAdd(&s_cnt[bin], 1u);
+        if (want_mass) {
             const unsigned long long w = mass_fixed(s, M);
-            atomicAdd(&s_mass[d], w);
+            if (w) atomicAdd(&s_mass[bin], w);
             zloc += w;
         }
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < kDigits; d += kThreads) {
-        if (s_cnt[d]) {
-            atomicAdd(&a.cnt[(int64_t)b * kDigits + d], s_cnt[d]);
-            if (WHICH == WHICH_P) atomicAdd(&a.mass[(int64_t)b * kDigits + d], s_mass[d]);
-        }
+    for (int d = threadIdx.x; d < kBins - 1; d += kThreads) {
+        if (s_cnt[d]) atomicAdd(&a.cnt[(int64_t)b * kBins + d], s_cnt[d]);
+        if (s_mass[d]) atomicAdd(&a.mass[(int64_t)b * kBins + d], s_mass[d]);
     }
-    if (WHICH == WHICH_P && level == 0) {
-        const unsigned long long zs = block_sum(zloc, s_red);
+    const unsigned long long tails = block_sum<unsigned long long, kThreads>(tail, s_red);
+    if (threadIdx.x == 0 && tails)
+        atomicAdd(&a.cnt[(int64_t)b * kBins + kBins - 1], (uint32_t)tails);
+    if (want_mass) {
+        const unsigned long long zs = block_sum<unsigned long long, kThreads>(zloc, s_red);
         if (threadIdx.x == 0 && zs) atomicAdd(&ctl->Z, zs);
     }
 }
 
-// One workgroup per row: pick the digit of the current level from the
-// completed histogram, update the row's prefix, clear the histogram.
-template <int WHICH>
-__global__ __launch_bounds__(kThreads) void samp_select_kernel(const SampArgs a, int level)
+// One workgroup per row: the row max, and the threshold bin.  Top-k: the
+// bin holding the k-th largest s, with the rank inside it.  Nucleus: the
+// lowest non-empty bin whose strictly-greater mass is within p of the total;
+// every bin above it is eligible in full.
+__global__ __launch_bounds__(kRThreads) void samp_select_kernel(const SampArgs a)
 {
+    constexpr int BPT = kBins / kRThreads;
     const int b = blockIdx.x;
     SampCtl *ctl = a.ctl + b;
     const uint32_t mode = ctl->mode;
-    if (WHICH == WHICH_K && !(mode & MODE_TOPK)) return;
-    if (WHICH == WHICH_P && !(mode & MODE_TOPP)) return;
-    __shared__ unsigned long long s_red[kThreads];
-    __shared__ int s_dstar;
-
-    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const int d_lo = (int)threadIdx.x * kDigitsPerThread;
-    uint32_t cnt[kDigitsPerThread];
-    unsigned long long mass[kDigitsPerThread];
+    if (!(mode & (MODE_TOPK | MODE_TOPP | MODE_TOPP_MAX))) return;
+    __shared__ unsigned long long s_red[kRThreads / 64];
+    const uint32_t max_key = row_max_key<kRThreads>(a, b, reinterpret_cast<uint32_t *>(s_red));
+    if (threadIdx.x == 0) ctl->max_key = max_key;
+    if (mode & MODE_TOPP_MAX) return;
+    const int d0 = (int)threadIdx.x * BPT;
+    uint32_t cnt[BPT];
+    unsigned long long mass[BPT];
+    unsigned long long own_c = 0, own_m = 0;
 #pragma unroll
-    for (int j = 0; j < kDigitsPerThread; ++j) {
-        uint32_t *gc = &a.cnt[(int64_t)b * kDigits + d_lo + j];
-        cnt[j] = *gc;
-        *gc = 0;
-        mass[j] = 0;
-        if (WHICH == WHICH_P) {
-            unsigned long long *gm = &a.mass[(int64_t)b * kDigits + d_lo + j];
-            mass[j] = *gm;
-            *gm = 0;
-        }
+    for (int j = 0; j < BPT; ++j) {
+        cnt[j] = a.cnt[(int64_t)b * kBins + d0 + j];
+        mass[j] = a.mass[(int64_t)b * kBins + d0 + j];
+        own_c += cnt[j];
+        own_m += mass[j];
     }
-    if (threadIdx.x == 0) s_dstar = kDigits;
-
-    if (WHICH == WHICH_K) {
-        unsigned long long own = 0;
+    unsigned long long above_c = block_scan_inclusive<unsigned long long, kRThreads>(own_c, s_red) - own_c;
+    unsigned long long above_m = block_scan_inclusive<unsigned long long, kRThreads>(own_m, s_red) - own_m;
+    if (mode & MODE_TOPK) {
+        const unsigned long long k = ctl->k;
 #pragma unroll
-        for (int j = 0; j < kDigitsPerThread; ++j) own += cnt[j];
-        // count in the digits above this thread's range
-        unsigned long long above = block_scan_inclusive<unsigned long long, true>(own, s_red) - own;
-        const unsigned long long r = ctl->k_rank;
-#pragma unroll
-        for (int j = kDigitsPerThread - 1; j >= 0; --j) {
-            const unsigned long long cd = cnt[j];
-            if (above < r && r <= above + cd) {
-                // the unique digit holding the rank-th largest key
-                const int d = d_lo + j;
-                const uint32_t pre = ctl->k_prefix | ((uint32_t)d << shift);
-                const uint32_t rank = (uint32_t)(r - above);
-                ctl->k_prefix = pre;
-                ctl->k_rank = rank;
-                if (level == 2) {
-                    ctl->k_key = pre;
-                    if (rank < cd) ctl->k_tie = rank;  // keep only the lowest-index ties
-                }
+        for (int j = 0; j < BPT; ++j) {
+            if (above_c < k && k <= above_c + cnt[j]) {
+                ctl->jstar = (uint32_t)(d0 + j);
+                ctl->rank = (uint32_t)(k - above_c);
+                ctl->A = above_m;
             }
-            above += cd;
+            above_c += cnt[j];
+            above_m += mass[j];
         }
-    } else {
-        unsigned long long own = 0;
+        return;
+    }
+    // nucleus only
+    const double limit = (double)a.top_p[b] * (double)ctl->Z;
+    long long cand = -1;
+    unsigned long long cand_above = 0;
 #pragma unroll
-        for (int j = 0; j < kDigitsPerThread; ++j) own += mass[j];
-        unsigned long long above = block_scan_inclusive<unsigned long long, true>(own, s_red) - own;
-        const unsigned long long A = ctl->A;
-        const double limit = (double)a.top_p[b] * (double)ctl->Z;
-        int cand = kDigits;
-        unsigned long long cand_above = 0;
-        // the lowest non-empty digit whose strictly-greater mass is within
-        // the limit (that mass only grows as the digit falls)
-#pragma unroll
-        for (int j = kDigitsPerThread - 1; j >= 0; --j) {
-            if ((double)(A + above) <= limit && cnt[j]) {
-                cand = d_lo + j;
-                cand_above = above;
-            }
-            above += mass[j];
+    for (int j = 0; j < BPT; ++j) {
+        if (cnt[j] && (double)above_m <= limit) {
+            cand = d0 + j;
+            cand_above = above_m;
         }
-        if (cand < kDigits) atomicMin(&s_dstar, cand);
-        __syncthreads();
-        if (cand < kDigits && cand == s_dstar) {
-            const uint32_t pre = ctl->p_prefix | ((uint32_t)cand << shift);
-            ctl->A = A + cand_above;
-            ctl->p_prefix = pre;
-            if (level == 2) ctl->p_key = pre;
-        }
+        above_m += mass[j];
+    }
+    const long long best = block_max<long long, kRThreads>(cand, reinterpret_cast<long long *>(s_red));
+    if (cand >= 0 && cand == best) {
+        ctl->jstar = (uint32_t)cand;
+        ctl->A = cand_above;
     }
 }
 
-// top-k ties, count step: logits per chunk whose key equals k_key
-template <bool VEC4>
-__global__ __launch_bounds__(kThreads) void samp_tie_count_kernel(const SampArgs a)
+// Eligible logits above the threshold bin join the Gumbel argmax; logits of
+// the threshold bin are appended to the candidate list.  The noise is read
+// only where it is needed: the (index, s) pairs that need it are compacted
+// in LDS and their noise fetched together, kList pairs per round.  ROUND2:
+// only rows waiting for a second round work.
+template <bool VEC4, bool ROUND2>
+__global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
     SampCtl *ctl = a.ctl + b;
-    if (!(ctl->mode & MODE_TOPK) || ctl->k_tie == 0) return;
-    __shared__ uint32_t s_red[kThreads];
-    const float T = a.temperature[b];
-    const uint32_t kkey = ctl->k_key;
+    if (ROUND2 && !ctl->round2) return;
+    const uint32_t mode = a.flags ? ctl->mode : row_mode(a, b);
+    __shared__ unsigned long long s_red[kThreads / 64];
+    __shared__ uint32_t s_tot, s_base;
+    __shared__ uint32_t s_idx[kList];   // index | kCandBit
+    __shared__ float s_s[kList];
+    __shared__ uint32_t s_slot[kList];
     const int i0 = blockIdx.x * a.chunk;
     const int i1 = min(a.vocab, i0 + a.chunk);
     const int per = a.chunk / kThreads;
-    Tile<VEC4> t;
-    t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
-    uint32_t eq = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j)
-        if (j < per && Tile<VEC4>::index(i0, j) < i1) eq += float_key(t.v[j] / T) == kkey;
-    eq = block_sum(eq, s_red);
-    if (threadIdx.x == 0) a.chunk_cnt[(int64_t)b * a.nchunks + blockIdx.x] = eq;
-}
-
-// top-k ties, cut step (one workgroup per row): keep only the k_tie
-// lowest-index logits whose key equals k_key
-__global__ __launch_bounds__(kThreads) void samp_tie_cut_kernel(const SampArgs a)
-{
-    const int b = blockIdx.x;
-    SampCtl *ctl = a.ctl + b;
-    if (!(ctl->mode & MODE_TOPK) || ctl->k_tie == 0) return;
-    __shared__ uint32_t s_red[kThreads];
-    __shared__ int s_chunk;
-    __shared__ uint32_t s_rem;
-    const float T = a.temperature[b];
-    const uint32_t kkey = ctl->k_key;
-    const float *z = a.logits + (int64_t)b * a.lstride;
-    if (threadIdx.x == 0) {
-        const uint32_t need = ctl->k_tie;
-        uint32_t run = 0;
-        int cstar = a.nchunks - 1;
-        uint32_t rem = 1;
-        for (int c = 0; c < a.nchunks; ++c) {
-            const uint32_t v = a.chunk_cnt[(int64_t)b * a.nchunks + c];
-            if (run + v >= need) {
-                cstar = c;
-                rem = need - run;
-                break;
-            }
-            run += v;
-        }
-        s_chunk = cstar;
-        s_rem = rem;
-    }
-    __syncthreads();
-    // ordered scan of the chosen chunk: thread t owns a contiguous range
-    const int per = a.chunk / kThreads;
-    const int i0 = s_chunk * a.chunk + (int)threadIdx.x * per;
-    const int i1 = min(a.vocab, i0 + per);
-    uint32_t own = 0;
-    for (int i = i0; i < i1; ++i) own += float_key(z[i] / T) == kkey;
-    const uint32_t incl = block_scan_inclusive<uint32_t, false>(own, s_red);
-    const uint32_t excl = incl - own;
-    const uint32_t rem = s_rem;
-    if (excl < rem && rem <= incl) {
-        uint32_t seen = excl;
-        for (int i = i0; i < i1; ++i) {
-            if (float_key(z[i] / T) == kkey && ++seen == rem) {
-                ctl->k_cut = (uint32_t)i;
-                break;
-            }
-        }
-    }
-}
-
-template <bool VEC4>
-__global__ __launch_bounds__(kThreads) void samp_final_kernel(const SampArgs a)
-{
-    const int b = blockIdx.y;
-    SampCtl *ctl = a.ctl + b;
-    __shared__ unsigned long long s_red[kThreads];
-    const uint32_t mode = ctl->mode;
-    const int i0 = blockIdx.x * a.chunk;
-    const int i1 = min(a.vocab, i0 + a.chunk);
-    const int per = a.chunk / kThreads;
+    const float *g = a.gumbel + (int64_t)b * a.gstride;
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
     unsigned long long best = 0;
@@ -498,81 +494,573 @@ __global__ __launch_bounds__(kThreads) void samp_final_kernel(const SampArgs a)
             const int i = Tile<VEC4>::index(i0, j);
             if (j < per && i < i1) best = max(best, pack_key_index(float_key(t.v[j]), (uint32_t)i));
         }
+    } else if (mode & MODE_PLAIN) {
+        // every logit is eligible: stream the noise as a tile too
+        const float T = a.temperature[b];
+        Tile<VEC4> gt;
+        gt.load(g, i0, i1, per);
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) {
+            const int i = Tile<VEC4>::index(i0, j);
+            if (j < per && i < i1) {
+                const float kappa = t.v[j] / T + gt.v[j];
+                best = max(best, pack_key_index(float_key(kappa), (uint32_t)i));
+            }
+        }
     } else {
         const float T = a.temperature[b];
-        const float *g = a.gumbel + (int64_t)b * a.gstride;
-        const bool topk = (mode & MODE_TOPK) != 0;
-        const bool topp = (mode & (MODE_TOPP | MODE_TOPP_MAX)) != 0;
-        if (!topk && !topp) {
-            // every logit is eligible: stream the noise as a tile too
-            Tile<VEC4> gt;
-            gt.load(g, i0, i1, per);
+        const uint32_t max_key = ctl->max_key;
+        const float M = key_float(max_key);
+        const int jstar = (int)ctl->jstar;
+        const bool maxima = (mode & MODE_TOPP_MAX) != 0;
+        uint32_t kept = 0, incand = 0;
 #pragma unroll
-            for (int j = 0; j < kMaxPer; ++j) {
-                const int i = Tile<VEC4>::index(i0, j);
-                if (j < per && i < i1) {
-                    const float kappa = t.v[j] / T + gt.v[j];
-                    best = max(best, pack_key_index(float_key(kappa), (uint32_t)i));
+        for (int j = 0; j < kMaxPer; ++j) {
+            const int i = Tile<VEC4>::index(i0, j);
+            const float s = t.v[j] / T;
+            bool ok = false, c = false;
+            if (j < per && i < i1) {
+                if (maxima) {
+                    ok = float_key(s) == max_key;
+                } else {
+                    const int bin = bin_of(s, M);
+                    ok = bin < jstar;
+                    c = bin == jstar;
                 }
             }
-        } else {
-            const uint32_t kkey = ctl->k_key, kcut = ctl->k_cut;
-            const uint32_t pkey = (mode & MODE_TOPP) ? ctl->p_key : ctl->max_key;
-            uint32_t kept = 0;
+            t.v[j] = s;
+            kept |= (ok ? 1u : 0u) << j;
+            incand |= (c ? 1u : 0u) << j;
+        }
+        const uint32_t need = kept | incand;
+        const uint32_t nc = __popc(incand), nn = __popc(need);
+        // candidates (high half) and noise reads (low half) before this thread;
+        // both totals stay below 2^16
+        const uint32_t incl = block_scan_inclusive<uint32_t, kThreads>((nc << 16) | nn,
+                                                                       reinterpret_cast<uint32_t *>(s_red));
+        if (threadIdx.x == kThreads - 1) {
+            s_tot = incl;
+            if (incl >> 16) s_base = atomicAdd(&ctl->ncand, incl >> 16);
+        }
+        __syncthreads();
+        const uint32_t tot = s_tot;
+        const uint32_t tot_n = tot & 0xffffu;
+        uint32_t slot = ((tot >> 16) ? s_base : 0u) + (incl >> 16) - nc;
+        unsigned long long *cand = a.cand + (int64_t)b * kCap;
+        uint32_t *kap = a.kap + (int64_t)b * kCap;
+        // rounds of at most kList list entries: each thread's entries hold
+        // the consecutive list positions [pos0, pos0 + nn)
+        const uint32_t pos0 = (incl & 0xffffu) - nn;
+        for (uint32_t base = 0; base < tot_n; base += (uint32_t)kList) {
+            if (base) __syncthreads();  // the previous round's entries are consumed
+            uint32_t pos = pos0, sl = slot;
 #pragma unroll
             for (int j = 0; j < kMaxPer; ++j) {
-                const int i = Tile<VEC4>::index(i0, j);
-                const float s = t.v[j] / T;
-                const uint32_t key = float_key(s);
-                bool ok = j < per && i < i1;
-                if (topk) ok = ok && (key > kkey || (key == kkey && (uint32_t)i <= kcut));
-                if (topp) ok = ok && key >= pkey;
-                t.v[j] = s;
-                kept |= (ok ? 1u : 0u) << j;
+                if (!((need >> j) & 1u)) continue;
+                const bool c = (incand >> j) & 1u;
+                if (pos - base < (uint32_t)kList) {
+                    const uint32_t i = (uint32_t)Tile<VEC4>::index(i0, j);
+                    s_idx[pos - base] = i | (c ? kCandBit : 0u) | (((kept >> j) & 1u) ? kKeptBit : 0u);
+                    s_s[pos - base] = t.v[j];
+                    s_slot[pos - base] = sl;
+                }
+                ++pos;
+                sl += c ? 1u : 0u;
             }
-            // noise only for the eligible logits, all loads issued together
-            float gv[kMaxPer];
+            __syncthreads();
+            const uint32_t cnt = min((uint32_t)kList, tot_n - base);
+            constexpr int R = kList / kThreads;
+            float gv[R];
 #pragma unroll
-            for (int j = 0; j < kMaxPer; ++j)
-                gv[j] = ((kept >> j) & 1u) ? g[Tile<VEC4>::index(i0, j)] : 0.f;
+            for (int r = 0; r < R; ++r) {
+                const uint32_t q = (uint32_t)(r * kThreads) + threadIdx.x;
+                gv[r] = q < cnt ? g[s_idx[q] & kIndexMask] : 0.f;
+            }
 #pragma unroll
-            for (int j = 0; j < kMaxPer; ++j)
-                if ((kept >> j) & 1u)
-                    best = max(best, pack_key_index(float_key(t.v[j] + gv[j]),
-                                                    (uint32_t)Tile<VEC4>::index(i0, j)));
+            for (int r = 0; r < R; ++r) {
+                const uint32_t q = (uint32_t)(r * kThreads) + threadIdx.x;
+                if (q >= cnt) continue;
+                const uint32_t e = s_idx[q];
+                const uint32_t i = e & kIndexMask;
+                const float sv = s_s[q];
+                const uint32_t kk = float_key(sv + gv[r]);
+                if (e & kKeptBit) best = max(best, pack_key_index(kk, i));
+                if (e & kCandBit) {
+                    const uint32_t cs = s_slot[q];
+                    if (cs < (uint32_t)kCap) {
+                        cand[cs] = pack_key_index(float_key(sv), i);
+                        kap[cs] = kk;
+                    }
+                }
+            }
         }
     }
-    best = block_max(best, s_red);
-    if (threadIdx.x == 0 && best) atomicMax(&ctl->best, best);
+    best = block_max<unsigned long long, kThreads>(best, s_red);
+    if (threadIdx.x == 0) a.part_best[(int64_t)b * a.nchunks + blockIdx.x] = best;
 }
 
-__global__ __launch_bounds__(kThreads) void samp_write_ids_kernel(const SampArgs a)
+// ---- per-row resolution ---------------------------------------------------
+
+struct ResolveShared {
+    union {
+        struct {
+            unsigned long long key[kCap];  // candidates (sorted, descending, above kRThreads)
+            uint32_t kap[kCap];
+            unsigned long long w[kRThreads];  // masses of the kept few
+        };
+        struct {                           // exact in-row fallback
+            uint32_t hcnt[kDigits];
+            unsigned long long hmass[kDigits];
+        };
+    };
+    unsigned long long scan[kRThreads];
+};
+
+// Descending bitonic sort of n (a power of two) packed keys with payload.
+__device__ void bitonic_sort_desc(unsigned long long *key, uint32_t *pay, int n)
 {
-    const int b = blockIdx.x * kThreads + threadIdx.x;
-    if (b >= a.batch) return;
-    const unsigned long long v = a.ctl[b].best;
-    a.out_ids[b] = (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffull));
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += kRThreads) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const unsigned long long x = key[i], y = key[ixj];
+                    const bool first = (i & k) == 0;
+                    if (first ? (x < y) : (x > y)) {
+                        key[i] = y;
+                        key[ixj] = x;
+                        const uint32_t p = pay[i];
+                        pay[i] = pay[ixj];
+                        pay[ixj] = p;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// In-row exact machinery (used when the threshold bin overflows the
+// candidate list).  The row is rescanned from memory; `sel` picks the logits
+// that take part (in the threshold bin, maybe kept by top-k).
+struct RowScan {
+    const float *z;
+    float T, M;
+    int V;
+    int jstar;
+};
+
+__device__ __forceinline__ bool in_bin(const RowScan &r, int i, float &s, uint32_t &key)
+{
+    s = r.z[i] / r.T;
+    key = float_key(s);
+    return bin_of(s, r.M) == r.jstar;
+}
+
+// Radix select, three levels of 11/11/10 key bits, over the logits of the
+// threshold bin that pass `kept_k` (top-k cut: key > kkey or key == kkey and
+// index <= kcut; kkey == 0 means no cut).  BY_MASS: the lowest digit whose
+// strictly-greater mass stays within `limit` given mass `above` of keys
+// above the bin; else: the digit holding the rank-th largest key.  Returns
+// the exact key; for ranks, `rank_left` is how many of its ties to keep.
+template <bool BY_MASS>
+__device__ uint32_t radix_in_bin(const RowScan &r, ResolveShared &sh, uint32_t kkey, uint32_t kcut,
+                                 unsigned long long above, double limit, uint32_t rank,
+                                 uint32_t *rank_left)
+{
+    uint32_t prefix = 0;
+    constexpr int DPT = kDigits / kRThreads;
+    __shared__ int s_d;
+    __shared__ unsigned long long s_above;
+    __shared__ uint32_t s_rank;
+    if (threadIdx.x == 0) {
+        s_above = above;
+        s_rank = rank;
+    }
+    __syncthreads();
+    for (int level = 0; level < 3; ++level) {
+        const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
+        const int width = level == 2 ? 10 : 11;
+        const int hi = shift + width;
+        const unsigned long long rk = s_rank;   // read before any thread can update it
+        const unsigned long long A = s_above;
+        for (int d = threadIdx.x; d < kDigits; d += kRThreads) {
+            sh.hcnt[d] = 0;
+            sh.hmass[d] = 0;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < r.V; i += kRThreads) {
+            float s;
+            uint32_t key;
+            if (!in_bin(r, i, s, key)) continue;
+            if (kkey && !(key > kkey || (key == kkey && (uint32_t)i <= kcut))) continue;
+            if (hi < 32 && (key >> hi) != (prefix >> hi)) continue;
+            const uint32_t d = (key >> shift) & ((1u << width) - 1u);
+            atomicAdd(&sh.hcnt[d], 1u);
+            if (BY_MASS) atomicAdd(&sh.hmass[d], mass_fixed(s, r.M));
+        }
+        __syncthreads();
+        // thread t owns digits [DPT t, DPT t + DPT); scan from the top digit down
+        const int d_hi = (int)threadIdx.x * DPT + DPT - 1;
+        unsigned long long own = 0;
+        for (int j = 0; j < DPT; ++j) own += BY_MASS ? sh.hmass[d_hi - j] : sh.hcnt[d_hi - j];
+        // exclusive sum over the digits above this thread's range
+        __syncthreads();
+        sh.scan[kRThreads - 1 - threadIdx.x] = own;
+        __syncthreads();
+        for (int off = 1; off < kRThreads; off <<= 1) {
+            const int tt = kRThreads - 1 - (int)threadIdx.x;
+            const unsigned long long add = tt >= off ? sh.scan[tt - off] : 0ull;
+            __syncthreads();
+            sh.scan[tt] += add;
+            __syncthreads();
+        }
+        unsigned long long up = sh.scan[kRThreads - 1 - threadIdx.x] - own;
+        if (threadIdx.x == 0) s_d = kDigits;
+        __syncthreads();
+        if (BY_MASS) {
+            int cand = -1;
+            unsigned long long cand_up = 0;
+            for (int j = 0; j < DPT; ++j) {
+                const int d = d_hi - j;
+                if ((double)(A + up) > limit) break;
+                if (sh.hcnt[d]) {
+                    cand = d;
+                    cand_up = up;
+                }
+                up += sh.hmass[d];
+            }
+            // the lowest qualifying digit
+            if (cand >= 0) atomicMin(&s_d, cand);
+            __syncthreads();
+            if (cand >= 0 && cand == s_d) s_above = A + cand_up;
+            __syncthreads();
+            prefix |= (uint32_t)s_d << shift;
+        } else {
+            for (int j = 0; j < DPT; ++j) {
+                const int d = d_hi - j;
+                const unsigned long long c = sh.hcnt[d];
+                if (up < rk && rk <= up + c) {
+                    s_d = d;
+                    s_rank = (uint32_t)(rk - up);
+                }
+                up += c;
+            }
+            __syncthreads();
+            prefix |= (uint32_t)s_d << shift;
+        }
+        __syncthreads();
+    }
+    if (rank_left) *rank_left = s_rank;
+    return prefix;
+}
+
+// Index of the `need`-th (1-based) logit of the threshold bin, in index
+// order, whose key equals `key`.
+__device__ uint32_t nth_tie_index(const RowScan &r, ResolveShared &sh, uint32_t key, uint32_t need)
+{
+    __shared__ uint32_t s_wave[kRThreads / 64];
+    __shared__ uint32_t s_found;
+    __shared__ uint32_t s_seen;
+    if (threadIdx.x == 0) {
+        s_found = 0xffffffffu;
+        s_seen = 0;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int base = 0; base < r.V; base += kRThreads) {
+        const int i = base + (int)threadIdx.x;
+        bool hit = false;
+        if (i < r.V) {
+            float s;
+            uint32_t k2;
+            hit = in_bin(r, i, s, k2) && k2 == key;
+        }
+        const unsigned long long m = __ballot(hit);
+        if (lane == 0) s_wave[wave] = __popcll(m);
+        __syncthreads();
+        uint32_t before = s_seen;
+        for (int w = 0; w < wave; ++w) before += s_wave[w];
+        const uint32_t below = __popcll(m & ((1ull << lane) - 1ull));
+        if (hit && before + below + 1 == need) s_found = (uint32_t)i;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t tot = 0;
+            for (int w = 0; w < kRThreads / 64; ++w) tot += s_wave[w];
+            s_seen += tot;
+        }
+        __syncthreads();
+        if (s_found != 0xffffffffu) break;
+    }
+    return s_found;
+}
+
+// Gumbel argmax over the threshold bin's logits that pass the final cut.
+__device__ unsigned long long best_in_bin(const RowScan &r, const float *g, ResolveShared &sh,
+                                          uint32_t kkey, uint32_t kcut, uint32_t tau)
+{
+    unsigned long long best = 0;
+    for (int i = threadIdx.x; i < r.V; i += kRThreads) {
+        float s;
+        uint32_t key;
+        if (!in_bin(r, i, s, key)) continue;
+        if (kkey && !(key > kkey || (key == kkey && (uint32_t)i <= kcut))) continue;
+        if (key < tau) continue;
+        best = max(best, pack_key_index(float_key(s + g[i]), (uint32_t)i));
+    }
+    return block_max<unsigned long long, kRThreads>(best, sh.scan);
+}
+
+// Mass of the threshold bin's logits kept by the top-k cut.
+__device__ unsigned long long kept_mass_in_bin(const RowScan &r, ResolveShared &sh, uint32_t kkey,
+                                               uint32_t kcut)
+{
+    unsigned long long m = 0;
+    for (int i = threadIdx.x; i < r.V; i += kRThreads) {
+        float s;
+        uint32_t key;
+        if (!in_bin(r, i, s, key)) continue;
+        if (!(key > kkey || (key == kkey && (uint32_t)i <= kcut))) continue;
+        m += mass_fixed(s, r.M);
+    }
+    return block_sum<unsigned long long, kRThreads>(m, sh.scan);
+}
+
+// Round 2 set-up: the nucleus cut of a top-k row lies above its top-k bin.
+// Every logit in bins above `jk` is in the top-k set, so the nucleus over
+// that set is found like a plain nucleus with total mass Zk.
+__device__ void setup_round2(const SampArgs &a, SampCtl *ctl, ResolveShared &sh, int b, int jk,
+                             unsigned long long Zk)
+{
+    constexpr int BPT = kBins / kRThreads;
+    const double limit = (double)a.top_p[b] * (double)Zk;
+    const int d0 = (int)threadIdx.x * BPT;
+    unsigned long long own = 0;
+    for (int j = 0; j < BPT; ++j) own += a.mass[(int64_t)b * kBins + d0 + j];
+    unsigned long long above = block_scan_inclusive<unsigned long long, kRThreads>(own, sh.scan) - own;
+    long long cand = -1;
+    unsigned long long cand_above = 0;
+    for (int j = 0; j < BPT; ++j) {
+        const int d = d0 + j;
+        if (d < jk && a.cnt[(int64_t)b * kBins + d] && (double)above <= limit) {
+            cand = d;
+            cand_above = above;
+        }
+        above += a.mass[(int64_t)b * kBins + d];
+    }
+    const long long best = block_max<long long, kRThreads>(cand, reinterpret_cast<long long *>(sh.scan));
+    if (cand >= 0 && cand == best) {
+        ctl->jstar = (uint32_t)cand;
+        ctl->A = cand_above;
+        ctl->Z = Zk;
+        ctl->mode = MODE_TOPP;
+        ctl->ncand = 0;
+        ctl->round2 = 1;
+    }
+}
+
+template <bool ROUND2>
+__global__ __launch_bounds__(kRThreads) void samp_resolve_kernel(const SampArgs a)
+{
+    __shared__ ResolveShared sh;
+    const int b = blockIdx.x;
+    SampCtl *ctl = a.ctl + b;
+    // Everything the row may need is requested up front, so that the loads
+    // overlap: the chunks' best keys, the first kRThreads list entries (in
+    // bounds whatever the count; entries past it are ignored) and the
+    // control block.
+    const int i = (int)threadIdx.x;
+    unsigned long long best = 0;
+    {
+        const unsigned long long *pb = a.part_best + (int64_t)b * a.nchunks;
+        for (int c = i; c < a.nchunks; c += kRThreads) best = max(best, pb[c]);
+    }
+    const unsigned long long cand0 = a.cand[(int64_t)b * kCap + i];
+    const uint32_t kap0 = a.kap[(int64_t)b * kCap + i];
+    const double p = (double)a.top_p[b];
+    SampCtl c = {};
+    if (a.flags) c = *ctl;
+    if (ROUND2 && !c.round2) return;
+    const uint32_t mode = a.flags ? c.mode : row_mode(a, b);
+    if (mode & MODE_DONE) return;
+    // best eligible logit outside the threshold bin, over the chunks
+    best = block_max<unsigned long long, kRThreads>(best, sh.scan);
+    if (mode & (MODE_GREEDY | MODE_PLAIN | MODE_TOPP_MAX)) {
+        if (threadIdx.x == 0) {
+            a.out_ids[b] = (int32_t)unpack_index(best);
+            if (a.flags) ctl->mode = mode | MODE_DONE;
+        }
+        return;
+    }
+    const bool topk = (mode & MODE_TOPK) != 0;
+    const bool topp = (mode & MODE_TOPP) != 0;
+    const uint32_t n = c.ncand;
+    const float M = key_float(c.max_key);
+    const unsigned long long A = c.A;
+    const int jstar = (int)c.jstar;
+
+    if (n <= (uint32_t)kRThreads) {
+        // ---- few candidates: ranks and masses above by direct counting ----
+        // q lanes (consecutive, q <= 64) share candidate e = i / q and split
+        // the comparisons against all n candidates between them.
+        int np = 1;
+        while (np < (int)n) np <<= 1;
+        const int q = min(64, kRThreads / np);
+        const int e = i / q, part = i % q;
+        sh.key[i] = i < (int)n ? cand0 : 0ull;
+        sh.kap[i] = kap0;
+        __syncthreads();
+        const bool real = e < (int)n;
+        const unsigned long long ke = real ? sh.key[e] : 0ull;
+        const uint32_t se = (uint32_t)(ke >> 32);
+        // top-k keeps the r largest (s, then lowest index); the nucleus runs
+        // over what top-k keeps
+        bool kept = real;
+        if (topk) {
+            uint32_t larger = 0;
+            for (int j = part; j < (int)n; j += q) larger += sh.key[j] > ke ? 1u : 0u;
+            larger = group_sum_lanes(larger, q);
+            kept = real && larger < c.rank;
+        }
+        uint32_t tau = 0;
+        if (topp) {
+            __shared__ unsigned long long s_tot;
+            const unsigned long long w = kept ? mass_fixed(key_float(se), M) : 0ull;
+            if (part == 0 && real) sh.w[e] = w;
+            const unsigned long long tot = block_sum<unsigned long long, kRThreads>(part == 0 ? w : 0ull, sh.scan);
+            unsigned long long Zrow = c.Z;
+            if (topk) {
+                // the nucleus over the top-k set: total mass above the bin + kept candidates
+                Zrow = A + tot;
+                if ((double)A > p * (double)Zrow) {
+                    setup_round2(a, ctl, sh, b, jstar, Zrow);
+                    return;
+                }
+            }
+            const double limit = p * (double)Zrow;
+            // mass of kept candidates with a strictly larger s
+            unsigned long long above = 0;
+            for (int j = part; j < (int)n; j += q) above += (uint32_t)(sh.key[j] >> 32) > se ? sh.w[j] : 0ull;
+            above = group_sum_lanes(above, q);
+            // the smallest s whose strictly-larger mass fits the limit
+            const uint32_t fit = (kept && (double)(A + above) <= limit) ? se : 0xffffffffu;
+            tau = ~block_max<uint32_t, kRThreads>(~fit, reinterpret_cast<uint32_t *>(sh.scan));
+        }
+        if (part == 0 && kept && se >= tau) best = max(best, pack_key_index(sh.kap[e], unpack_index(ke)));
+        best = block_max<unsigned long long, kRThreads>(best, sh.scan);
+    } else if (n <= (uint32_t)kCap) {
+        // ---- sort the candidates of the threshold bin ----
+        int np = 1;
+        while (np < (int)n) np <<= 1;
+        for (int i = threadIdx.x; i < np; i += kRThreads) {
+            sh.key[i] = i < (int)n ? a.cand[(int64_t)b * kCap + i] : 0ull;
+            sh.kap[i] = i < (int)n ? a.kap[(int64_t)b * kCap + i] : 0u;
+        }
+        __syncthreads();
+        bitonic_sort_desc(sh.key, sh.kap, np);
+        // thread t owns sorted positions [PT t, PT t + PT)
+        constexpr int PT = kCap / kRThreads;
+        const int i0 = (int)threadIdx.x * PT;
+        // top-k keeps the first r; the nucleus runs over what top-k keeps
+        const int r = topk ? (int)c.rank : (int)n;
+        unsigned long long w[PT];
+        unsigned long long own = 0;
+        for (int j = 0; j < PT; ++j) {
+            const int i = i0 + j;
+            w[j] = (topp && i < r) ? mass_fixed(key_float((uint32_t)(sh.key[i] >> 32)), M) : 0ull;
+            own += w[j];
+        }
+        const unsigned long long incl = block_scan_inclusive<unsigned long long, kRThreads>(own, sh.scan);
+        const unsigned long long excl0 = incl - own;
+        uint32_t tau = 0;
+        if (topp) {
+            unsigned long long Zrow = c.Z;
+            if (topk) {
+                // the nucleus over the top-k set: total mass above the bin + kept candidates
+                __shared__ unsigned long long s_tot;
+                if (threadIdx.x == kRThreads - 1) s_tot = incl;
+                __syncthreads();
+                Zrow = A + s_tot;
+                if ((double)A > p * (double)Zrow) {
+                    setup_round2(a, ctl, sh, b, jstar, Zrow);
+                    return;
+                }
+            }
+            const double limit = p * (double)Zrow;
+            // the lowest group head whose strictly-greater mass fits the limit
+            long long last = -1;
+            unsigned long long run = excl0;
+            for (int j = 0; j < PT; ++j) {
+                const int i = i0 + j;
+                if (i < r) {
+                    const uint32_t k1 = (uint32_t)(sh.key[i] >> 32);
+                    const bool head = i == 0 || (uint32_t)(sh.key[i - 1] >> 32) != k1;
+                    if (head && (double)(A + run) <= limit) last = i;
+                }
+                run += w[j];
+            }
+            const long long lh = block_max<long long, kRThreads>(last, reinterpret_cast<long long *>(sh.scan));
+            tau = lh >= 0 ? (uint32_t)(sh.key[lh] >> 32) : 0u;
+        }
+        // best Gumbel key over the kept candidates
+        for (int j = 0; j < PT; ++j) {
+            const int i = i0 + j;
+            if (i < r && (uint32_t)(sh.key[i] >> 32) >= tau)
+                best = max(best, pack_key_index(sh.kap[i], unpack_index(sh.key[i])));
+        }
+        best = block_max<unsigned long long, kRThreads>(best, sh.scan);
+    } else {
+        // ---- the threshold bin overflowed the list: exact cut from the row ----
+        RowScan rs;
+        rs.z = a.logits + (int64_t)b * a.lstride;
+        rs.T = a.temperature[b];
+        rs.M = M;
+        rs.V = a.vocab;
+        rs.jstar = jstar;
+        const float *g = a.gumbel + (int64_t)b * a.gstride;
+        uint32_t kkey = 0, kcut = 0xffffffffu, tau = 0;
+        if (topk) {
+            uint32_t left = 0;
+            kkey = radix_in_bin<false>(rs, sh, 0, 0, 0, 0.0, c.rank, &left);
+            // keep only the `left` lowest-index logits equal to the k-th key
+            kcut = nth_tie_index(rs, sh, kkey, left);
+        }
+        if (topp) {
+            unsigned long long Zrow = c.Z;
+            if (topk) {
+                Zrow = A + kept_mass_in_bin(rs, sh, kkey, kcut);
+                if ((double)A > p * (double)Zrow) {
+                    setup_round2(a, ctl, sh, b, jstar, Zrow);
+                    return;
+                }
+            }
+            tau = radix_in_bin<true>(rs, sh, kkey, kcut, A, p * (double)Zrow, 0, nullptr);
+        }
+        const unsigned long long bb = best_in_bin(rs, g, sh, kkey, kcut, tau);
+        best = max(best, bb);
+    }
+    if (threadIdx.x == 0) {
+        a.out_ids[b] = (int32_t)unpack_index(best);
+        ctl->mode = mode | MODE_DONE;
+        ctl->round2 = 0;
+    }
 }
 
 template <bool VEC4>
 void launch_passes(const SampArgs &a, const dim3 grid, uint32_t flags, hipStream_t stream)
 {
-    if (flags & 2u) samp_max_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
-    if (flags & 1u) {
-        for (int level = 0; level < 3; ++level) {
-            samp_hist_kernel<WHICH_K, VEC4><<<grid, kThreads, 0, stream>>>(a, level);
-            samp_select_kernel<WHICH_K><<<a.batch, kThreads, 0, stream>>>(a, level);
-        }
-        samp_tie_count_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
-        samp_tie_cut_kernel<<<a.batch, kThreads, 0, stream>>>(a);
+    if (flags) {
+        samp_max_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
+        samp_bins_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
+        samp_select_kernel<<<a.batch, kRThreads, 0, stream>>>(a);
     }
-    if (flags & 2u)
-        for (int level = 0; level < 3; ++level) {
-            samp_hist_kernel<WHICH_P, VEC4><<<grid, kThreads, 0, stream>>>(a, level);
-            samp_select_kernel<WHICH_P><<<a.batch, kThreads, 0, stream>>>(a, level);
-        }
-    samp_final_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
-    samp_write_ids_kernel<<<(a.batch + kThreads - 1) / kThreads, kThreads, 0, stream>>>(a);
+    samp_collect_kernel<VEC4, false><<<grid, kThreads, 0, stream>>>(a);
+    samp_resolve_kernel<false><<<a.batch, kRThreads, 0, stream>>>(a);
+    if ((flags & 3u) == 3u) {
+        // top-k then nucleus: rows whose nucleus cut lies above their top-k bin
+        samp_collect_kernel<VEC4, true><<<grid, kThreads, 0, stream>>>(a);
+        samp_resolve_kernel<true><<<a.batch, kRThreads, 0, stream>>>(a);
+    }
 }
 
 }  // namespace
@@ -607,10 +1095,12 @@ hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_
     a.ctl = reinterpret_cast<SampCtl *>(ws + L.ctl_off);
     a.cnt = reinterpret_cast<uint32_t *>(ws + L.cnt_off);
     a.mass = reinterpret_cast<unsigned long long *>(ws + L.mass_off);
-    a.chunk_cnt = reinterpret_cast<uint32_t *>(ws + L.chunk_off);
+    a.cand = reinterpret_cast<unsigned long long *>(ws + L.cand_off);
+    a.kap = reinterpret_cast<uint32_t *>(ws + L.kap_off);
+    a.part_max = reinterpret_cast<uint32_t *>(ws + L.pmax_off);
+    a.part_best = reinterpret_cast<unsigned long long *>(ws + L.pbest_off);
 
     const dim3 grid(L.nchunks, batch);
-    samp_init_kernel<<<batch, kThreads, 0, stream>>>(a);
     const bool vec4 = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && logits_stride % 4 == 0 &&
                       (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0) && gumbel_stride % 4 == 0 &&
                       vocab % 4 == 0;

@@ -424,3 +424,71 @@ def test_fused_decode_step_qwen3_layer():
     err = np.abs(bf16_out_to_f64(out) - ref).max()
     say(f"  max abs err {err:.3e}")
     assert err <= ATTN_TOL
+
+
+# ------------------------------------------- sampler: threshold-bin paths --
+
+def test_sampler_nucleus_threshold_bin_overflow():
+    """More equal (or nearly equal) logits in the threshold bin than the
+    candidate list holds: the cut is found by rescanning the row."""
+    rng = np.random.default_rng(60)
+    B, V = 4, 20000
+    z = rng.standard_normal((B, V), dtype=np.float32)
+    z[0] = 0.0                                   # all equal: every token kept
+    z[1, :6000] = 3.0                            # 6000 tied maxima
+    z[2] = (rng.integers(0, 3, V) * 1e-3).astype(np.float32)   # 3 values inside one bin
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = np.ones(B, np.float32)
+    p = np.array([0.5, 0.3, 0.7, 0.9], np.float32)
+    k = np.zeros(B, np.int32)
+    bad, amb, infos = _sample_and_compare(z, g, t, p, k)
+    assert not bad, bad
+    assert infos[0].kept == V and infos[1].kept >= 6000
+
+
+def test_sampler_top_k_in_catch_all_bin_and_wide_spread():
+    """Logits spread over thousands of units: most tokens sit in the last
+    value bin; top-k ranks deep inside it and a nucleus near the top."""
+    rng = np.random.default_rng(61)
+    B, V = 4, 30000
+    z = (rng.standard_normal((B, V), dtype=np.float32) * 500).astype(np.float32)
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = np.array([1.0, 1.0, 0.01, 3.0], np.float32)
+    p = np.array([1.0, 1.0, 0.9, 0.99], np.float32)
+    k = np.array([V - 7, 25000, 0, 0], np.int32)
+    bad, amb, _ = _sample_and_compare(z, g, t, p, k)
+    assert not bad, bad
+
+
+def test_sampler_top_k_then_nucleus_rounds():
+    """Top-k then nucleus on the top-k set: the nucleus cut inside the top-k
+    threshold bin, above it (a second round), and with overflowing ties."""
+    rng = np.random.default_rng(62)
+    B, V = 6, 40000
+    z = (rng.standard_normal((B, V), dtype=np.float32) * 2).astype(np.float32)
+    z[1, 123] = 30.0              # one dominant token: nucleus = {123}, far above the k bin
+    z[2, :5000] = 6.0             # 5000 ties around the k-th value (overflow)
+    z[3, 10:20] = 8.0
+    z[3, 20:30] = 7.99            # nucleus cut among near-equal values
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = np.array([1.0, 1.0, 1.0, 0.5, 0.8, 1.2], np.float32)
+    p = np.array([0.9, 0.5, 0.6, 0.95, 0.3, 0.999], np.float32)
+    k = np.array([500, 3000, 4500, 25, 2, 39000], np.int32)
+    bad, amb, _ = _sample_and_compare(z, g, t, p, k)
+    assert not bad, bad
+    assert amb == 0
+
+
+@pytest.mark.parametrize("seed", [63, 64, 65])
+def test_sampler_random_mixed_settings(seed):
+    """Random per-row settings over a mid-size batch, both filters enabled."""
+    rng = np.random.default_rng(seed)
+    B, V = 32, 50000
+    z = (rng.standard_normal((B, V), dtype=np.float32) * rng.uniform(0.5, 6, (B, 1))).astype(np.float32)
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = rng.choice([0.0, 0.3, 0.7, 1.0, 1.5], B).astype(np.float32)
+    p = rng.choice([0.0, 0.2, 0.5, 0.9, 0.95, 1.0], B).astype(np.float32)
+    k = rng.choice([0, 1, 10, 50, 1000, 20000], B).astype(np.int32)
+    bad, amb, _ = _sample_and_compare(z, g, t, p, k)
+    assert not bad, bad
+    assert amb <= 1
