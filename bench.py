@@ -8,11 +8,17 @@ contexts uniform in [128, 4096], GQA 16/8, head_dim 128, block 256,
 resident in HBM before timing starts.
 
 Prints ONE JSON line.  `value` is the paged decode-attention throughput in
-GB/s of algorithmic bytes (each cached K/V element once + Q + O, per layer)
-over the measured time of the attention kernels; decode steps/s and
-sampler tokens/s ride along.  `roofline` covers the dominant kernel (the
-attention partial step) with per-launch HIP-event timing; `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload.
+GB/s of algorithmic bytes (each distinct cached K/V element once + Q + O,
+per layer) over the attention time per layer, measured by replaying the
+L layers' partial + reduce launches as a HIP graph between two HIP events.
+Decode steps/s (whole step replayed as a graph) and sampler tokens/s ride
+along, with per-kernel HIP-event times of eager steps.  `roofline` covers
+the dominant kernel (the attention partial step): its average launch time
+from a graph of the L partial launches alone.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.  Workloads small
+enough to sit in the 256 MB Infinity Cache cycle over copies of their
+pools so that each step reads from HBM; their warm (same pools) figure is
+reported beside it.
 """
 from __future__ import annotations
 
@@ -25,6 +31,13 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+WORKLOAD_TITLES = {
+    "tiny": "tiny: 4 rows, contexts 17/256/299/513, MHA 16 heads x 64, vocab 32768",
+    "qwen3": "qwen3: Qwen3-0.6B-shaped paged decode step",
+    "grok": "grok: Grok-1-shaped attention, 32 rows x 2048 positions, GQA 48/8, contiguous tables",
+    "clone": "clone: 16-way clone, 4 shared prefix blocks + private tails, MHA 10 heads, top-k 50",
+    "long": "long: 8 rows, contexts 32k-128k, GQA 64/8, fragmented pool",
+}
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -49,7 +62,24 @@ def parse():
                     help="time eager launches only (no HIP-graph replay of the step)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run a device copy of this many MiB (counter calibration)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="independent copies of the pools, cycled step by step so that at "
+                         "least 1 GB of cache is touched between reuses (0 = automatic)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads for the oracle baseline (0 = the CPUs this process "
+                         "may use, at most 16)")
     return ap.parse_args()
+
+
+def unique_positions(n, tables, bs):
+    """Distinct physical slots read by all rows (shared prefix blocks once)."""
+    seen = set()
+    for b in range(len(n)):
+        nb = int(n[b])
+        for j in range((nb + bs - 1) // bs):
+            used = min(bs, nb - j * bs)
+            seen.update(int(tables[b][j]) * bs + o for o in range(used))
+    return len(seen)
 
 
 def main():
@@ -91,10 +121,19 @@ def main():
     q = [bf16(x) for x in inp.q]
     kn = [bf16(x) for x in inp.k_new]
     vn = [bf16(x) for x in inp.v_new]
-    kp, vp = [], []
-    for layer in range(L):
-        kp.append(device_pool(cfg, inp.num_blocks, "kpool", layer))
-        vp.append(device_pool(cfg, inp.num_blocks, "vpool", layer))
+    # cache hygiene: workloads whose pools fit in the 256 MB Infinity Cache
+    # cycle over R copies so that >= 1 GB is touched between two reuses
+    uniq = unique_positions(n, tables, bs)
+    touched = uniq * Hkv * D * 4 * L
+    R = args.rotate or max(1, min(256, -(-1_000_000_000 // touched)))
+    kp, vp = [], []   # [copy][layer]
+    for c in range(R):
+        if c == 0:
+            kp.append([device_pool(cfg, inp.num_blocks, "kpool", layer) for layer in range(L)])
+            vp.append([device_pool(cfg, inp.num_blocks, "vpool", layer) for layer in range(L)])
+        else:
+            kp.append([x.clone() for x in kp[0]])
+            vp.append([x.clone() for x in vp[0]])
     logits = torch.from_numpy(inp.logits).to(dev)
     gumbel = torch.from_numpy(inp.gumbel).to(dev)
     t, p, k = (torch.from_numpy(x).to(dev) for x in sampling_params(cfg))
@@ -108,26 +147,26 @@ def main():
     slots = torch.empty(B, dtype=torch.int32, device=dev)
     ids = torch.empty(B, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
-    log(f"[bench] inputs resident: {sum(x.numel() * 2 for x in kp + vp) / 1e9:.2f} GB of pools, "
-        f"split_tokens={split}")
+    log(f"[bench] inputs resident: {sum(x.numel() * 2 for c in range(R) for x in kp[c] + vp[c]) / 1e9:.2f} GB "
+        f"of pools ({R} cop{'y' if R == 1 else 'ies'}), split_tokens={split}")
 
     fused = not args.unfused
 
-    def step(ev=None):
+    def step(ev=None, c=0):
         if not fused:
             pkv.slot_mapping(td, nd, bs, out=slots)
         for layer in range(L):
+            K, V = kp[c][layer], vp[c][layer]
             if not fused:
-                pkv.kv_store(kp[layer], vp[layer], kn[layer], vn[layer], slots)
+                pkv.kv_store(K, V, kn[layer], vn[layer], slots)
             if ev is not None:
                 ev["p0"][layer].record()
             if fused:
                 # store of the new K/V fused into the attention partial step
-                pkv.decode_attention_partial_store(q[layer], kp[layer], vp[layer], kn[layer],
-                                                   vn[layer], td, nd, max_len, ws,
-                                                   split_tokens=split)
+                pkv.decode_attention_partial_store(q[layer], K, V, kn[layer], vn[layer], td, nd,
+                                                   max_len, ws, split_tokens=split)
             else:
-                pkv.decode_attention_partial(q[layer], kp[layer], vp[layer], td, nd, max_len, ws,
+                pkv.decode_attention_partial(q[layer], K, V, td, nd, max_len, ws,
                                              split_tokens=split)
             if ev is not None:
                 ev["p1"][layer].record()
@@ -141,8 +180,8 @@ def main():
         if ev is not None:
             ev["s1"].record()
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(c=i % R)
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
@@ -157,7 +196,7 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], c=i % R)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -167,51 +206,84 @@ def main():
     log(f"[bench] timed {args.steps} eager steps in {total_ms:.2f} ms")
     eager_ms_per_step = total_ms / args.steps
 
+
     # the same step captured once as a HIP graph and replayed: removes the
     # host launch gaps between the ~3L+10 kernels of a step
-    graph_ms_per_step = None
-    if not args.no_graph:
+    def attention_only(c, with_reduce=True):
+        for layer in range(L):
+            K, V = kp[c][layer], vp[c][layer]
+            if fused:
+                pkv.decode_attention_partial_store(q[layer], K, V, kn[layer], vn[layer], td, nd,
+                                                   max_len, ws, split_tokens=split)
+            else:
+                pkv.decode_attention_partial(q[layer], K, V, td, nd, max_len, ws,
+                                             split_tokens=split)
+            if with_reduce:
+                pkv.decode_attention_reduce(out, nd, Hkv, tables.shape[1], bs, max_len, ws,
+                                            split_tokens=split)
+
+    def graph_time_ms(fn):
+        """Capture R consecutive calls fn(c), c = 0..R-1 (one per pool copy),
+        as one HIP graph; return the replayed time per call in ms."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()
+            fn(0)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
+            for c in range(R):
+                fn(c)
+        for _ in range(max(1, args.warmup // R)):
             graph.replay()
         torch.cuda.synchronize()
+        reps = max(1, args.steps // R)
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
-        for _ in range(args.steps):
+        for _ in range(reps):
             graph.replay()
         g1.record()
         torch.cuda.synchronize()
-        graph_ms_per_step = g0.elapsed_time(g1) / args.steps
-        log(f"[bench] timed {args.steps} graph replays: {graph_ms_per_step:.4f} ms per step")
+        return g0.elapsed_time(g1) / (reps * R)
 
-    # algorithmic bytes
-    kv_bytes = int(n.astype(np.int64).sum()) * Hkv * D * 2 * 2   # K and V, each element once
+    # HIP-graph replay, as a serving engine runs a decode step: removes the
+    # host launch gaps between kernels.  Three graphs: the whole step, the
+    # attention alone (L x (partial + reduce)) and the partial kernels alone.
+    graph_ms_per_step = graph_attn_us = graph_part_us = None
+    if not args.no_graph:
+        graph_ms_per_step = graph_time_ms(lambda c: step(c=c))
+        graph_attn_us = 1e3 * graph_time_ms(lambda c: attention_only(c)) / L
+        graph_part_us = 1e3 * graph_time_ms(lambda c: attention_only(c, with_reduce=False)) / L
+        log(f"[bench] graph replays: {graph_ms_per_step:.4f} ms per step, attention "
+            f"{graph_attn_us:.2f} us per layer, partial {graph_part_us:.2f} us per launch")
+    warm_attn_us = None
+    if R > 1 and not args.no_graph:
+        # the same pools every time: what a cache-resident workload reaches
+        warm_attn_us = 1e3 * graph_time_ms(lambda c: attention_only(0)) / L
+
+    # algorithmic bytes: K and V of every distinct cached position once (a
+    # shared prefix counts once), + Q + O
+    kv_logical = int(n.astype(np.int64).sum()) * Hkv * D * 2 * 2
+    kv_bytes = uniq * Hkv * D * 2 * 2
     q_bytes = B * Hq * D * 2
     o_bytes = B * Hq * D * 2
     attn_bytes_layer = kv_bytes + q_bytes + o_bytes
-    part_avg_us = 1e3 * float(np.mean(part_ms))
-    red_avg_us = 1e3 * float(np.mean(red_ms))
-    attn_us_layer = part_avg_us + red_avg_us
+    part_ev_us = 1e3 * float(np.mean(part_ms))
+    red_ev_us = 1e3 * float(np.mean(red_ms))
+    attn_us_layer = graph_attn_us if graph_attn_us is not None else part_ev_us + red_ev_us
+    part_avg_us = graph_part_us if graph_part_us is not None else part_ev_us
     value = attn_bytes_layer / (attn_us_layer * 1e-6) / 1e9
     store_bytes = 2 * B * Hkv * D * 2 if fused else 0   # new K and V rows written
     part_bytes = kv_bytes + q_bytes + store_bytes
     part_gbs = part_bytes / (part_avg_us * 1e-6) / 1e9
     ms_per_step = graph_ms_per_step if graph_ms_per_step is not None else eager_ms_per_step
     samp_avg_us = 1e3 * float(np.mean(samp_ms))
-
     traffic = read_traffic(cfg.name, fused)
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(cfg, inp, kp[0], vp[0], args.cpu_seconds, kv_bytes + q_bytes + o_bytes)
+        cpu = cpu_baseline(cfg, inp, kp[0][0], vp[0][0], args.cpu_seconds, args.cpu_threads)
 
     if args.calibrate_copy > 0:
         nbytes = args.calibrate_copy << 20
@@ -235,8 +307,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: Qwen3-0.6B-shaped paged decode step"
-                   if cfg.name == "qwen3" else cfg.name,
+        "config": {"workload": WORKLOAD_TITLES.get(cfg.name, cfg.name),
                    "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": bs, "layers": L, "vocab": cfg.vocab,
                    "context_tokens": int(n.sum()), "split_tokens": split,
@@ -246,14 +317,25 @@ def main():
         "step_timing": "hip_graph_replay" if graph_ms_per_step is not None else "eager",
         "ms_per_step_eager": round(eager_ms_per_step, 4),
         "sampler_tokens_per_s": round(B / (samp_avg_us * 1e-6), 1),
-        "attention_us_per_layer": {"partial": round(part_avg_us, 3), "reduce": round(red_avg_us, 3)},
+        "attention_us_per_layer": round(attn_us_layer, 3),
+        "attention_timing": "hip_graph_replay" if graph_attn_us is not None else "hip_events",
+        "eager_event_us_per_layer": {"partial": round(part_ev_us, 3), "reduce": round(red_ev_us, 3)},
         "sampler_us": round(samp_avg_us, 3),
+        "kv_bytes_per_layer": {"unique": kv_bytes, "logical": kv_logical},
+        "logical_GBps": round((kv_logical + q_bytes + o_bytes) / (attn_us_layer * 1e-6) / 1e9, 2),
+        "cache": {"pool_copies_cycled": R,
+                  "warm_attention_us_per_layer": None if warm_attn_us is None else
+                  round(warm_attn_us, 3),
+                  "warm_GBps": None if warm_attn_us is None else
+                  round(attn_bytes_layer / (warm_attn_us * 1e-6) / 1e9, 2)},
         "step": "fused store + attention" if fused else "slot mapping, store, attention",
         "roofline": {"kernel": f"decode_partial_kernel<{D},{min(cfg.group, 8)},{'true' if fused else 'false'}>",
                      "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": part_bytes,
                      "avg_launch_us": round(part_avg_us, 3),
+                     "launch_timing": "hip_graph_replay of the layers' partial launches"
+                     if graph_part_us is not None else "hip_events per launch",
                      "traffic": traffic},
         "cpu_baseline": cpu,
     }
@@ -281,10 +363,27 @@ def read_traffic(name, fused):
     return int(float(kv["traffic_bytes_per_launch"]))
 
 
-def cpu_baseline(cfg, inp, kpool, vpool, seconds, layer_bytes):
-    """The oracle as it stands, single-threaded on the host: attention of
-    layer 0 over whole rows (after copying the pools back), repeated until
-    about `seconds` of CPU time, expressed in the same GB/s unit."""
+def host_description():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "usable_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(cfg, inp, kpool, vpool, seconds, threads):
+    """The oracle as it stands on the host: attention of layer 0 over whole
+    rows (pools copied back from the device), rows handed out to `threads`
+    host threads (the C oracle runs outside the interpreter lock), repeated
+    until about `seconds` of wall time; then a single-threaded run of a
+    quarter of that.  Expressed in the same GB/s unit as `value`."""
+    import threading
+
     import oracle
     import torch
 
@@ -292,21 +391,42 @@ def cpu_baseline(cfg, inp, kpool, vpool, seconds, layer_bytes):
     vh = vpool.view(torch.int16).cpu().numpy().view(np.uint16)
     n, t = inp.context_lens, inp.block_tables
     q = inp.q[0]
-    rows, done_bytes, elapsed = 0, 0, 0.0
     per_row = n.astype(np.int64) * cfg.num_kv_heads * cfg.head_dim * 4 + 4 * cfg.num_q_heads * cfg.head_dim
-    t0 = time.perf_counter()
-    b = 0
-    while elapsed < seconds:
-        oracle.decode_attention(q[b:b + 1], kh, vh, t[b:b + 1], n[b:b + 1])
-        done_bytes += int(per_row[b])
-        rows += 1
-        b = (b + 1) % cfg.batch
-        elapsed = time.perf_counter() - t0
-    log(f"[bench] cpu oracle: {rows} rows in {elapsed:.1f} s")
-    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+    host = host_description()
+    T = threads or min(16, host["usable_cpus"])
+
+    def run(nthreads, secs):
+        lock = threading.Lock()
+        state = {"next": 0, "rows": 0, "bytes": 0}
+        t0 = time.perf_counter()
+
+        def worker():
+            while time.perf_counter() - t0 < secs:
+                with lock:
+                    b = state["next"] % cfg.batch
+                    state["next"] += 1
+                oracle.decode_attention(q[b:b + 1], kh, vh, t[b:b + 1], n[b:b + 1])
+                with lock:
+                    state["rows"] += 1
+                    state["bytes"] += int(per_row[b])
+
+        ws = [threading.Thread(target=worker) for _ in range(nthreads)]
+        for w in ws:
+            w.start()
+        for w in ws:
+            w.join()
+        return state["rows"], state["bytes"], time.perf_counter() - t0
+
+    rows, nbytes, elapsed = run(T, seconds)
+    rows1, nbytes1, elapsed1 = run(1, seconds / 4)
+    log(f"[bench] cpu oracle: {rows} rows in {elapsed:.1f} s on {T} threads; "
+        f"{rows1} rows in {elapsed1:.1f} s on 1 thread")
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": T,
             "kind": "oracle",
             "sample": f"layer 0 attention of {rows} rows (cycling over the {cfg.batch} rows, "
-                      f"fp64 two-pass softmax), {elapsed:.1f} s single-threaded"}
+                      f"fp64 two-pass softmax), {elapsed:.1f} s on {T} host threads",
+            "single_thread_value": round(nbytes1 / elapsed1 / 1e9, 4),
+            "host": host}
 
 
 if __name__ == "__main__":
