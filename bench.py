@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="separate slot-mapping and store launches instead of the fused "
                          "store + attention partial")
+    ap.add_argument("--cascade", action="store_true",
+                    help="shared-prefix workloads: the cascade decode (prefix read once for "
+                         "all rows) instead of the plain paged attention")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP-graph replay of the step)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -150,28 +153,46 @@ def main():
     log(f"[bench] inputs resident: {sum(x.numel() * 2 for c in range(R) for x in kp[c] + vp[c]) / 1e9:.2f} GB "
         f"of pools ({R} cop{'y' if R == 1 else 'ies'}), split_tokens={split}")
 
-    fused = not args.unfused
+    # rows sharing their first blocks (the clone workload): cascade decode,
+    # the shared prefix read once per KV head for all rows
+    cascade = cfg.clone_prefix_blocks > 0 and args.cascade
+    fused = not args.unfused and not cascade
+    if cascade:
+        prefix = i32(tables[0, :cfg.clone_prefix_blocks])
+        cws = torch.empty(pkv.cascade_workspace_bytes(B, Hq, Hkv, D, max_len,
+                                                      cfg.clone_prefix_blocks, bs, args.split),
+                          dtype=torch.uint8, device=dev)
+
+    def partial(layer, c):
+        K, V = kp[c][layer], vp[c][layer]
+        if cascade:
+            pkv.cascade_decode_attention(q[layer], K, V, prefix, td, nd, max_len, out=out,
+                                         workspace=cws, split_tokens=args.split)
+        elif fused:
+            # store of the new K/V fused into the attention partial step
+            pkv.decode_attention_partial_store(q[layer], K, V, kn[layer], vn[layer], td, nd,
+                                               max_len, ws, split_tokens=split)
+        else:
+            pkv.decode_attention_partial(q[layer], K, V, td, nd, max_len, ws,
+                                         split_tokens=split)
+
+    def reduce():
+        if not cascade:  # the cascade call includes its reduce
+            pkv.decode_attention_reduce(out, nd, Hkv, tables.shape[1], bs, max_len, ws,
+                                        split_tokens=split)
 
     def step(ev=None, c=0):
         if not fused:
             pkv.slot_mapping(td, nd, bs, out=slots)
         for layer in range(L):
-            K, V = kp[c][layer], vp[c][layer]
             if not fused:
-                pkv.kv_store(K, V, kn[layer], vn[layer], slots)
+                pkv.kv_store(kp[c][layer], vp[c][layer], kn[layer], vn[layer], slots)
             if ev is not None:
                 ev["p0"][layer].record()
-            if fused:
-                # store of the new K/V fused into the attention partial step
-                pkv.decode_attention_partial_store(q[layer], K, V, kn[layer], vn[layer], td, nd,
-                                                   max_len, ws, split_tokens=split)
-            else:
-                pkv.decode_attention_partial(q[layer], K, V, td, nd, max_len, ws,
-                                             split_tokens=split)
+            partial(layer, c)
             if ev is not None:
                 ev["p1"][layer].record()
-            pkv.decode_attention_reduce(out, nd, Hkv, tables.shape[1], bs, max_len, ws,
-                                        split_tokens=split)
+            reduce()
             if ev is not None:
                 ev["r1"][layer].record()
         if ev is not None:
@@ -211,16 +232,9 @@ def main():
     # host launch gaps between the ~3L+10 kernels of a step
     def attention_only(c, with_reduce=True):
         for layer in range(L):
-            K, V = kp[c][layer], vp[c][layer]
-            if fused:
-                pkv.decode_attention_partial_store(q[layer], K, V, kn[layer], vn[layer], td, nd,
-                                                   max_len, ws, split_tokens=split)
-            else:
-                pkv.decode_attention_partial(q[layer], K, V, td, nd, max_len, ws,
-                                             split_tokens=split)
+            partial(layer, c)
             if with_reduce:
-                pkv.decode_attention_reduce(out, nd, Hkv, tables.shape[1], bs, max_len, ws,
-                                            split_tokens=split)
+                reduce()
 
     def graph_time_ms(fn):
         """Capture R consecutive calls fn(c), c = 0..R-1 (one per pool copy),
@@ -328,8 +342,11 @@ def main():
                   round(warm_attn_us, 3),
                   "warm_GBps": None if warm_attn_us is None else
                   round(attn_bytes_layer / (warm_attn_us * 1e-6) / 1e9, 2)},
-        "step": "fused store + attention" if fused else "slot mapping, store, attention",
-        "roofline": {"kernel": f"decode_partial_kernel<{D},{min(cfg.group, 8)},{'true' if fused else 'false'}>",
+        "step": ("slot mapping, store, cascade attention (shared prefix read once)" if cascade
+                 else "fused store + attention" if fused else "slot mapping, store, attention"),
+        "roofline": {"kernel": "cascade prefix + tail partial kernels + reduce" if cascade else
+                     f"decode_partial_kernel<{D},{max(g for g in range(1, 9) if cfg.group % g == 0)},"
+                     f"{'true' if fused else 'false'},false>",
                      "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": part_bytes,

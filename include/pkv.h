@@ -204,6 +204,51 @@ int pkv_decode_attention_partial_store(const void *q, int64_t q_stride,
                                        size_t workspace_bytes,
                                        hipStream_t stream);
 
+/* ---- shared-prefix (cascade) decode --------------------------------------
+ * Rows that begin with the same cached blocks, as after one prefill cloned
+ * into N rows (nanochat engine page, section 3: one batch-1 prefill whose
+ * cache is copied into every row of the decode batch; nano-vllm page,
+ * "prefix cache": cached prefix blocks shared through block tables).  The
+ * result equals pkv_paged_decode_attention over each row's whole context;
+ * only the order of the work differs: the shared prefix, positions
+ * [0, num_prefix_blocks*block_size), is read once per KV head for all the
+ * rows (through prefix_blocks), each row's own positions after it through
+ * its block table, and the two are merged by log-sum-exp.
+ *
+ * prefix_blocks      int32 [num_prefix_blocks]: block ids of the shared
+ *                    prefix, in position order.  Every row's first
+ *                    num_prefix_blocks logical blocks are these; the
+ *                    corresponding block-table entries are not read.
+ * num_prefix_blocks  >= 1
+ * context_lens       as for pkv_paged_decode_attention; a row shorter than
+ *                    the prefix attends to its own first n_b prefix
+ *                    positions only, and n_b = 0 gives a zero output.
+ * workspace          at least pkv_cascade_workspace_bytes(...) bytes,
+ *                    256-byte aligned; contents on entry are ignored.
+ * Other arguments as for pkv_paged_decode_attention (split_tokens applies
+ * to the positions after the prefix).  The new token's K/V is stored with
+ * pkv_kv_store beforehand; it must not lie in a shared block. */
+size_t pkv_cascade_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_context_len,
+                                   int32_t num_prefix_blocks,
+                                   int32_t block_size, int32_t split_tokens);
+
+int pkv_cascade_decode_attention(void *out, int64_t out_stride, const void *q,
+                                 int64_t q_stride, const void *k_cache,
+                                 const void *v_cache,
+                                 const int32_t *prefix_blocks,
+                                 int32_t num_prefix_blocks,
+                                 const int32_t *block_tables,
+                                 int32_t block_table_stride,
+                                 const int32_t *context_lens, int32_t batch,
+                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, int32_t max_context_len,
+                                 float scale, int32_t split_tokens,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* ---- sampler --------------------------------------------------------------
  * Next token per row (Grok-1 runners chapter, section 8.3 and 8.3.1;
  * nanochat engine page, section 3; nano-vllm page, "run model"):

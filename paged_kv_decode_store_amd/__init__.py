@@ -20,6 +20,7 @@ __all__ = [
     "slot_mapping", "kv_store", "paged_decode_attention", "decode_attention_partial",
     "decode_attention_reduce", "decode_workspace_bytes", "decode_split_tokens",
     "paged_decode_attention_store", "decode_attention_partial_store",
+    "cascade_decode_attention", "cascade_workspace_bytes",
     "sample_next_token", "sampler_workspace_bytes", "PkvError",
     "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
 ]
@@ -155,6 +156,44 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs, nb, max_context_len,
         scale, split_tokens, ws.data_ptr(), ws.numel(), _stream()), "pkv_paged_decode_attention")
+    return out
+
+
+def cascade_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                            max_context_len: int, num_prefix_blocks: int, block_size: int,
+                            split_tokens: int = 0) -> int:
+    n = lib().pkv_cascade_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                          max_context_len, num_prefix_blocks, block_size,
+                                          split_tokens)
+    if n == 0:
+        raise ValueError("invalid cascade workspace query (shapes or split_tokens)")
+    return n
+
+
+def cascade_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             prefix_blocks: torch.Tensor, block_tables: torch.Tensor,
+                             context_lens: torch.Tensor, max_context_len: int,
+                             scale: float = 0.0, split_tokens: int = 0,
+                             out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention for rows whose first len(prefix_blocks) blocks are the
+    shared blocks prefix_blocks (int32): the prefix is read once for all
+    rows.  Same result as paged_decode_attention over the whole rows."""
+    B, Hq, D, nb, bs, hkv = _attn_shapes(q, k_cache, block_tables)
+    if prefix_blocks.dim() != 1 or prefix_blocks.numel() == 0:
+        raise ValueError("prefix_blocks must be a non-empty 1-D int32 tensor")
+    npb = prefix_blocks.numel()
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    ws = _workspace(cascade_workspace_bytes(B, Hq, hkv, D, max_context_len, npb, bs, split_tokens),
+                    q.device, workspace)
+    check(lib().pkv_cascade_decode_attention(
+        _dev(out, "out", torch.bfloat16), out.stride(0), _dev(q, "q", torch.bfloat16), q.stride(0),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(prefix_blocks, "prefix_blocks", torch.int32), npb,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs, nb, max_context_len,
+        scale, split_tokens, ws.data_ptr(), ws.numel(), _stream()), "pkv_cascade_decode_attention")
     return out
 
 

@@ -83,6 +83,64 @@ int32_t clamp_len(int32_t max_context_len, int32_t block_table_stride, int32_t b
     return (int32_t)(max_context_len < cap ? max_context_len : cap);
 }
 
+// Prefix launch shape, measured on the 16-way clone workload: chunks of at
+// most 4 virtual queries (8 costs occupancy), ~512 workgroups.
+constexpr int kPrefixMaxG = 4;      // virtual queries per prefix workgroup, at most
+constexpr int kPrefixGroups = 512;  // prefix workgroups wanted
+
+// Workspace geometry of the shared-prefix (cascade) decode: per (row, query
+// head), prefix_splits partials of the shared prefix, then the partials of
+// the row's own positions after it.
+struct CascadeGeometry {
+    int32_t prefix_len;
+    int32_t prefix_split;    // positions per prefix partial
+    int32_t prefix_splits;
+    int32_t tail_split;      // positions per partial after the prefix
+    int32_t num_splits;      // slots per (row, query head)
+    int32_t G;               // virtual queries per prefix workgroup
+    int32_t vchunks;         // virtual-query chunks per KV head
+    pkv::SplitGeometry ws;   // workspace sizes (split_tokens = tail_split)
+};
+
+CascadeGeometry cascade_geometry(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_len, int32_t num_prefix_blocks,
+                                 int32_t block_size, int32_t split_tokens)
+{
+    CascadeGeometry g;
+    const int32_t group = num_q_heads / num_kv_heads;
+    g.prefix_len = num_prefix_blocks * block_size;
+    // every (row, query head) of a KV head is one virtual query; chunks of
+    // at most kPrefixMaxG, evenly filled
+    const int64_t vq = (int64_t)batch * group;
+    g.vchunks = (int32_t)((vq + kPrefixMaxG - 1) / kPrefixMaxG);
+    if (g.vchunks < 1) g.vchunks = 1;
+    g.G = (int32_t)((vq + g.vchunks - 1) / g.vchunks);
+    if (g.G < 1) g.G = 1;
+    // prefix splits: enough workgroups (~512) to stream the prefix in parallel
+    const int64_t per_split = (int64_t)num_kv_heads * g.vchunks;
+    int64_t want = (kPrefixGroups + per_split - 1) / per_split;
+    if (want < 1) want = 1;
+    int64_t ps = (g.prefix_len + want - 1) / want;
+    ps = (ps + 63) / 64 * 64;
+    if (ps < 64) ps = 64;
+    g.prefix_split = (int32_t)ps;
+    g.prefix_splits = (int32_t)((g.prefix_len + ps - 1) / ps);
+    const int32_t tail_len = max_len > g.prefix_len ? max_len - g.prefix_len : 0;
+    g.tail_split = split_tokens > 0
+                       ? split_tokens
+                       : pkv::auto_split_tokens(batch, num_kv_heads, tail_len, group);
+    const int32_t tail_splits = (tail_len + g.tail_split - 1) / g.tail_split;
+    g.num_splits = g.prefix_splits + tail_splits;
+    // workspace: the same layout as the plain split geometry with num_splits slots
+    g.ws = pkv::split_geometry(batch, num_q_heads, head_dim, 0, g.tail_split);
+    const size_t units = (size_t)batch * num_q_heads * g.num_splits;
+    g.ws.num_splits = g.num_splits;
+    g.ws.part_o_bytes = (units * head_dim * sizeof(float) + 255) & ~(size_t)255;
+    g.ws.part_ml_bytes = (units * 2 * sizeof(float) + 255) & ~(size_t)255;
+    g.ws.total_bytes = g.ws.part_o_bytes + g.ws.part_ml_bytes;
+    return g;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,7 +239,8 @@ int setup_partial(pkv::PartialArgs &a, const void *q, int64_t q_stride, const vo
                   int32_t block_table_stride, const int32_t *context_lens, int32_t batch,
                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                   int64_t num_blocks, int32_t max_context_len, float scale, int32_t split_tokens,
-                  void *workspace, size_t workspace_bytes, bool fused)
+                  void *workspace, size_t workspace_bytes, bool fused,
+                  const pkv::SplitGeometry *geometry = nullptr)
 {
     int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                    block_table_stride, max_context_len);
@@ -211,9 +270,11 @@ int setup_partial(pkv::PartialArgs &a, const void *q, int64_t q_stride, const vo
     REQUIRE(aligned(block_tables, 4) && aligned(context_lens, 4), PKV_ERR_INVALID_ARG,
             "int32 arrays must be 4-byte aligned");
     const int32_t split =
-        effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
+        geometry ? geometry->split_tokens
+                 : effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
     const pkv::SplitGeometry g =
-        pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split);
+        geometry ? *geometry
+                 : pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split);
     REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,
             "workspace must be non-null and 256-byte aligned");
     REQUIRE(workspace_bytes >= g.total_bytes, PKV_ERR_WORKSPACE,
@@ -245,6 +306,12 @@ int setup_partial(pkv::PartialArgs &a, const void *q, int64_t q_stride, const vo
     a.new_stride = ns;
     a.k_cache_w = fused ? static_cast<uint16_t *>(const_cast<void *>(k_cache)) : nullptr;
     a.v_cache_w = fused ? static_cast<uint16_t *>(const_cast<void *>(v_cache)) : nullptr;
+    a.pos_base = 0;
+    a.split_base = 0;
+    a.prefix_blocks = nullptr;
+    a.prefix_len = 0;
+    a.vq_per_kv = 0;
+    a.vchunks = 1;
     return PKV_OK;
 }
 
@@ -325,7 +392,88 @@ int pkv_decode_attention_reduce(void *out, int64_t out_stride, const int32_t *co
     a.max_len = clamp_len(max_context_len, block_table_stride, block_size);
     a.split_tokens = split;
     a.num_splits = g.num_splits;
+    a.prefix_len = 0;
+    a.prefix_splits = 0;
     return hip_status(pkv::launch_decode_reduce(a, head_dim, stream), "decode reduce launch");
+}
+
+size_t pkv_cascade_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t num_prefix_blocks, int32_t block_size,
+                                   int32_t split_tokens)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        head_dim <= 0 || max_context_len < 0 || num_prefix_blocks <= 0 || !pow2(block_size) ||
+        (int64_t)num_prefix_blocks * block_size > (1 << 30) || check_split(split_tokens) != PKV_OK)
+        return 0;
+    return cascade_geometry(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                            num_prefix_blocks, block_size, split_tokens)
+        .ws.total_bytes;
+}
+
+int pkv_cascade_decode_attention(void *out, int64_t out_stride, const void *q, int64_t q_stride,
+                                 const void *k_cache, const void *v_cache,
+                                 const int32_t *prefix_blocks, int32_t num_prefix_blocks,
+                                 const int32_t *block_tables, int32_t block_table_stride,
+                                 const int32_t *context_lens, int32_t batch,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks,
+                                 int32_t max_context_len, float scale, int32_t split_tokens,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   block_table_stride, max_context_len);
+    if (rc) return rc;
+    if ((rc = check_split(split_tokens))) return rc;
+    REQUIRE(num_prefix_blocks > 0 && (int64_t)num_prefix_blocks * block_size <= (1 << 30),
+            PKV_ERR_INVALID_ARG, "num_prefix_blocks must be > 0 (and the prefix < 2^30)");
+    const int64_t os = out_stride ? out_stride : (int64_t)num_q_heads * head_dim;
+    REQUIRE(os >= (int64_t)num_q_heads * head_dim && os % 8 == 0, PKV_ERR_INVALID_ARG,
+            "out_stride must be >= num_q_heads*head_dim and a multiple of 8");
+    const int32_t max_len = clamp_len(max_context_len, block_table_stride, block_size);
+    const CascadeGeometry cg = cascade_geometry(batch, num_q_heads, num_kv_heads, head_dim, max_len,
+                                                num_prefix_blocks, block_size, split_tokens);
+    // the ordinary partial arguments cover the positions after the prefix
+    pkv::SplitGeometry tail_geo = cg.ws;
+    tail_geo.split_tokens = cg.tail_split;
+    pkv::PartialArgs a;
+    rc = setup_partial(a, q, q_stride, k_cache, v_cache, nullptr, nullptr, 0, block_tables,
+                       block_table_stride, context_lens, batch, num_q_heads, num_kv_heads,
+                       head_dim, block_size, num_blocks, max_context_len, scale, split_tokens,
+                       workspace, workspace_bytes, false, &tail_geo);
+    if (rc || batch == 0) return rc;
+    REQUIRE(out && prefix_blocks, PKV_ERR_INVALID_ARG, "null pointer");
+    REQUIRE(aligned(out, 16), PKV_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    REQUIRE(aligned(prefix_blocks, 4), PKV_ERR_INVALID_ARG, "prefix_blocks must be 4-byte aligned");
+
+    // prefix launch: shared blocks, one workgroup per (prefix split, KV head, query chunk)
+    pkv::PartialArgs pa = a;
+    pa.prefix_blocks = prefix_blocks;
+    pa.prefix_len = cg.prefix_len;
+    pa.split_tokens = cg.prefix_split;
+    pa.vq_per_kv = batch * (num_q_heads / num_kv_heads);
+    pa.vchunks = cg.vchunks;
+    rc = hip_status(pkv::launch_decode_prefix(pa, head_dim, cg.G, stream), "cascade prefix launch");
+    if (rc) return rc;
+    // tail launch: each row's positions after the prefix
+    a.pos_base = cg.prefix_len;
+    a.split_base = cg.prefix_splits;
+    rc = hip_status(pkv::launch_decode_partial(a, head_dim, stream), "cascade tail launch");
+    if (rc) return rc;
+    pkv::ReduceArgs r;
+    r.out = static_cast<uint16_t *>(out);
+    r.out_stride = os;
+    r.part_o = a.part_o;
+    r.part_ml = a.part_ml;
+    r.context_lens = context_lens;
+    r.batch = batch;
+    r.num_q_heads = num_q_heads;
+    r.max_len = max_len;
+    r.split_tokens = cg.tail_split;
+    r.num_splits = cg.num_splits;
+    r.prefix_len = cg.prefix_len;
+    r.prefix_splits = cg.prefix_splits;
+    return hip_status(pkv::launch_decode_reduce(r, head_dim, stream), "cascade reduce launch");
 }
 
 int pkv_paged_decode_attention(void *out, int64_t out_stride, const void *q, int64_t q_stride,

@@ -60,6 +60,18 @@ struct PartialArgs {
     int64_t new_stride;     // elements between consecutive rows of k_new/v_new
     uint16_t *k_cache_w;    // same pools as k_cache/v_cache, written by the fused store
     uint16_t *v_cache_w;
+    // shared-prefix (cascade) decode.  Tail launch: positions start at
+    // pos_base and partial s goes to slot split_base + s.  Prefix launch
+    // (prefix_blocks non-null): one workgroup per (prefix split, KV head,
+    // chunk of virtual queries), where the virtual queries of a KV head are
+    // the (row, query head) pairs that use it, vq_per_kv = batch * group;
+    // positions [0, prefix_len) are read once through prefix_blocks.
+    int32_t pos_base;
+    int32_t split_base;
+    const int32_t *prefix_blocks;
+    int32_t prefix_len;
+    int32_t vq_per_kv;
+    int32_t vchunks;        // virtual-query chunks per KV head
 };
 
 struct ReduceArgs {
@@ -73,10 +85,16 @@ struct ReduceArgs {
     int32_t max_len;
     int32_t split_tokens;
     int32_t num_splits;
+    int32_t prefix_len;     // cascade: shared positions [0, prefix_len) ...
+    int32_t prefix_splits;  // ... held in the first prefix_splits slots
 };
 
 hipError_t launch_decode_partial(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceArgs &a, int32_t head_dim, hipStream_t stream);
+// Prefix step of the cascade decode: `a` describes the prefix launch; G is
+// the number of virtual queries per workgroup.
+hipError_t launch_decode_prefix(const PartialArgs &a, int32_t head_dim, int32_t G,
+                                hipStream_t stream);
 
 // Sampler
 size_t sampler_workspace_bytes(int32_t batch, int32_t vocab);

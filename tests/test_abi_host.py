@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.PROTOTYPES)
@@ -167,4 +167,32 @@ def test_fused_attention_validation():
     assert call(vn=FAKE + 4) == _lib.PKV_ERR_INVALID_ARG
     assert call(ns=8 * 128 - 8) == _lib.PKV_ERR_INVALID_ARG
     assert call(out=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
+
+
+def test_cascade_validation():
+    L = _lib.lib()
+    need = L.pkv_cascade_workspace_bytes(16, 10, 10, 128, 1281, 4, 256, 0)
+    assert need > 0
+    # more than the plain split-KV workspace of the same batch: prefix partials come first
+    assert need >= L.pkv_decode_workspace_bytes(16, 10, 10, 128, 1281 - 1024, 0)
+    assert L.pkv_cascade_workspace_bytes(16, 10, 10, 128, 1281, 0, 256, 0) == 0
+    assert L.pkv_cascade_workspace_bytes(16, 12, 8, 128, 1281, 4, 256, 0) == 0
+    assert L.pkv_cascade_workspace_bytes(16, 10, 10, 128, 1281, 4, 256, 100) == 0
+
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, pb=FAKE, npb=4, bt=FAKE, lens=FAKE, D=128,
+                 ws=FAKE, wsb=need)
+        a.update(kw)
+        return L.pkv_cascade_decode_attention(a["out"], 0, a["q"], 0, a["k"], a["v"], a["pb"],
+                                              a["npb"], a["bt"], 6, a["lens"], 16, 10, 10, a["D"],
+                                              256, 40, 1281, 0.0, 0, a["ws"], a["wsb"], None)
+
+    assert call(pb=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(pb=FAKE + 2) == _lib.PKV_ERR_INVALID_ARG
+    assert call(npb=0) == _lib.PKV_ERR_INVALID_ARG
+    assert call(out=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(q=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(D=96) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.PKV_ERR_WORKSPACE
     assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
