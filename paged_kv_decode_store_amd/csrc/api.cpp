@@ -83,10 +83,14 @@ int32_t clamp_len(int32_t max_context_len, int32_t block_table_stride, int32_t b
     return (int32_t)(max_context_len < cap ? max_context_len : cap);
 }
 
-// Prefix launch shape, measured on the 16-way clone workload: chunks of at
-// most 4 virtual queries (8 costs occupancy), ~512 workgroups.
-constexpr int kPrefixMaxG = 4;      // virtual queries per prefix workgroup, at most
-constexpr int kPrefixGroups = 512;  // prefix workgroups wanted
+// Prefix launch shape: the matrix-core kernel takes 16 virtual queries per
+// workgroup; the prefix is cut into splits so that about kPrefixGroups
+// workgroups stream it.
+#ifndef PKV_PREFIX_GROUPS
+#define PKV_PREFIX_GROUPS 256
+#endif
+constexpr int kPrefixMaxG = 16;     // virtual queries per prefix workgroup, at most
+constexpr int kPrefixGroups = PKV_PREFIX_GROUPS;  // prefix workgroups wanted
 
 // Workspace geometry of the shared-prefix (cascade) decode: per (row, query
 // head), prefix_splits partials of the shared prefix, then the partials of
@@ -453,7 +457,7 @@ int pkv_cascade_decode_attention(void *out, int64_t out_stride, const void *q, i
     pa.split_tokens = cg.prefix_split;
     pa.vq_per_kv = batch * (num_q_heads / num_kv_heads);
     pa.vchunks = cg.vchunks;
-    rc = hip_status(pkv::launch_decode_prefix(pa, head_dim, cg.G, stream), "cascade prefix launch");
+    rc = hip_status(pkv::launch_decode_prefix_mfma(pa, head_dim, stream), "cascade prefix launch");
     if (rc) return rc;
     // tail launch: each row's positions after the prefix
     a.pos_base = cg.prefix_len;

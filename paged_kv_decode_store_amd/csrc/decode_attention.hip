@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     // Issue the K/V loads of the chunk starting at t0 (one block, U positions
     // per lane group, one 16-byte piece per lane and position).
     auto load_chunk = [&](int t0, uint4 (&kr)[U], uint4 (&vr)[U]) {
-        const int raw = table[t0 >> a.bs_log2];
+        const int raw = load_block_id(table, uniform(t0 >> a.bs_log2));
         const bool blk_ok = raw >= 0 && raw < a.num_blocks;
         const int blk = blk_ok ? raw : 0;
         const int64_t base =
@@ -354,14 +354,15 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
 int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len,
                           int32_t group)
 {
-    // Measured on MI355X: the partial kernel runs best with roughly 1-2k
-    // non-empty workgroups.  Rows are assumed half full on average, so the
-    // split aims at B * Hkv * max_len / 2 positions spread over ~2048
-    // workgroups; groups >= 4 get at least 512 positions per split so the
-    // per-workgroup merge of G heads stays small next to the streaming.
+    // Measured on MI355X: the VALU partial kernel runs best with roughly
+    // 1-2k non-empty workgroups.  Rows are assumed half full on average, so
+    // the split aims at B * Hkv * max_len / 2 positions spread over ~2048
+    // workgroups.  The matrix-core kernel (group >= kMfmaMinGroup) streams
+    // best with long splits, >= 2048 positions per workgroup (Grok-shaped:
+    // 5.6 TB/s at 2048 vs 4.5 at 512; long contexts: flat from 2k to 3k).
     if (max_context_len <= 0 || batch <= 0 || num_kv_heads <= 0) return kRound;
     int64_t split = (int64_t)batch * num_kv_heads * max_context_len / 4096;
-    const int64_t lo = group >= 4 ? 512 : 128;
+    const int64_t lo = group >= kMfmaMinGroup ? 2048 : 128;
     if (split < lo) split = lo;
     if (split > 8192) split = 8192;
     split = ((split + kRound - 1) / kRound) * kRound;
@@ -427,6 +428,7 @@ static hipError_t launch_partial_d(const PartialArgs &a, int G, hipStream_t stre
 hipError_t launch_decode_partial(const PartialArgs &a, int32_t head_dim, hipStream_t stream)
 {
     if (a.batch == 0 || a.num_splits <= a.split_base) return hipSuccess;
+    if (a.group >= kMfmaMinGroup) return launch_decode_partial_mfma(a, head_dim, stream);
     const int G = a.group / a.head_chunks;
     if (head_dim == 128) return launch_partial_d<128, false>(a, G, stream);
     if (head_dim == 64) return launch_partial_d<64, false>(a, G, stream);

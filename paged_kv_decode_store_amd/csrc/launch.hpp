@@ -95,6 +95,15 @@ hipError_t launch_decode_reduce(const ReduceArgs &a, int32_t head_dim, hipStream
 // the number of virtual queries per workgroup.
 hipError_t launch_decode_prefix(const PartialArgs &a, int32_t head_dim, int32_t G,
                                 hipStream_t stream);
+// Matrix-core versions of the partial and prefix steps (up to 16 query heads
+// or virtual queries per workgroup; head_chunks / vchunks are derived).
+hipError_t launch_decode_partial_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
+hipError_t launch_decode_prefix_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
+// Group sizes from which the partial step runs on the matrix cores.
+#ifndef PKV_MFMA_MIN_GROUP
+#define PKV_MFMA_MIN_GROUP 3
+#endif
+constexpr int32_t kMfmaMinGroup = PKV_MFMA_MIN_GROUP;
 
 // Sampler
 size_t sampler_workspace_bytes(int32_t batch, int32_t vocab);

@@ -78,6 +78,18 @@ __device__ __forceinline__ float wave_sum(float v)
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Block id j of a block table, as a scalar load.  The table is read-only in
+// every kernel, but where the same kernel also stores to the KV pools the
+// compiler cannot tell that the stores leave it alone and would fetch it
+// through the vector path (a full memory round trip before each chunk's
+// addresses are known); reading it through the constant address space
+// states that it is not written.
+__device__ __forceinline__ int load_block_id(const int32_t *table, int j)
+{
+    typedef const int32_t __attribute__((address_space(4))) *const_i32_ptr;
+    return ((const_i32_ptr)table)[j];
+}
+
 // Order-preserving map of fp32 onto uint32 (larger float -> larger key);
 // -0 is folded onto +0 first so equal floats get equal keys.
 __device__ __forceinline__ uint32_t float_key(float f)
