@@ -344,9 +344,7 @@ def main():
                   round(attn_bytes_layer / (warm_attn_us * 1e-6) / 1e9, 2)},
         "step": ("slot mapping, store, cascade attention (shared prefix read once)" if cascade
                  else "fused store + attention" if fused else "slot mapping, store, attention"),
-        "roofline": {"kernel": "cascade prefix + tail partial kernels + reduce" if cascade else
-                     f"decode_partial_kernel<{D},{max(g for g in range(1, 9) if cfg.group % g == 0)},"
-                     f"{'true' if fused else 'false'},false>",
+        "roofline": {"kernel": partial_kernel_name(cfg, D, fused, cascade),
                      "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": part_bytes,
@@ -357,6 +355,17 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def partial_kernel_name(cfg, D, fused, cascade):
+    """Name of the partial-step kernel the library runs for this workload."""
+    if cascade:
+        return "cascade: decode_partial_mfma_kernel (prefix) + tail partial kernel + reduce"
+    f = "true" if fused else "false"
+    if cfg.group >= 3:  # the library's matrix-core threshold
+        return f"decode_partial_mfma_kernel<{D}, {f}, false>"
+    g = max(x for x in range(1, 9) if cfg.group % x == 0)
+    return f"decode_partial_kernel<{D}, {g}, {f}>"
 
 
 def read_traffic(name, fused):

@@ -168,10 +168,11 @@ int pkv_decode_attention_reduce(void *out, int64_t out_stride,
  * rows are taken from k_new/v_new (bf16 [batch][num_kv_heads][head_dim],
  * row b at b*new_token_stride elements, 0 = packed), written into the pools
  * at slot block_tables[b][(n_b-1)/block_size]*block_size + (n_b-1)%block_size
- * (skipped if that block id is outside [0, num_blocks)), and attended from
- * registers.  The result equals pkv_slot_mapping + pkv_kv_store +
- * pkv_paged_decode_attention on the same arguments.  Other arguments and the
- * workspace are as for pkv_paged_decode_attention. */
+ * (skipped if that block id is outside [0, num_blocks)) by the workgroup
+ * that attends to that position, before it streams its range.  The result
+ * equals pkv_slot_mapping + pkv_kv_store + pkv_paged_decode_attention on the
+ * same arguments.  Other arguments and the workspace are as for
+ * pkv_paged_decode_attention. */
 int pkv_paged_decode_attention_store(void *out, int64_t out_stride,
                                      const void *q, int64_t q_stride,
                                      void *k_cache, void *v_cache,

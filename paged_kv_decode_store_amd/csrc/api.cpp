@@ -85,12 +85,10 @@ int32_t clamp_len(int32_t max_context_len, int32_t block_table_stride, int32_t b
 
 // Prefix launch shape: the matrix-core kernel takes 16 virtual queries per
 // workgroup; the prefix is cut into splits so that about kPrefixGroups
-// workgroups stream it.
-#ifndef PKV_PREFIX_GROUPS
-#define PKV_PREFIX_GROUPS 256
-#endif
-constexpr int kPrefixMaxG = 16;     // virtual queries per prefix workgroup, at most
-constexpr int kPrefixGroups = PKV_PREFIX_GROUPS;  // prefix workgroups wanted
+// workgroups stream it (clone workload: 256 and 512 are equal, fewer is
+// slower).
+constexpr int kPrefixQ = 16;        // virtual queries per prefix workgroup
+constexpr int kPrefixGroups = 256;  // prefix workgroups wanted
 
 // Workspace geometry of the shared-prefix (cascade) decode: per (row, query
 // head), prefix_splits partials of the shared prefix, then the partials of
@@ -101,7 +99,6 @@ struct CascadeGeometry {
     int32_t prefix_splits;
     int32_t tail_split;      // positions per partial after the prefix
     int32_t num_splits;      // slots per (row, query head)
-    int32_t G;               // virtual queries per prefix workgroup
     int32_t vchunks;         // virtual-query chunks per KV head
     pkv::SplitGeometry ws;   // workspace sizes (split_tokens = tail_split)
 };
@@ -113,13 +110,10 @@ CascadeGeometry cascade_geometry(int32_t batch, int32_t num_q_heads, int32_t num
     CascadeGeometry g;
     const int32_t group = num_q_heads / num_kv_heads;
     g.prefix_len = num_prefix_blocks * block_size;
-    // every (row, query head) of a KV head is one virtual query; chunks of
-    // at most kPrefixMaxG, evenly filled
+    // every (row, query head) of a KV head is one virtual query
     const int64_t vq = (int64_t)batch * group;
-    g.vchunks = (int32_t)((vq + kPrefixMaxG - 1) / kPrefixMaxG);
+    g.vchunks = (int32_t)((vq + kPrefixQ - 1) / kPrefixQ);
     if (g.vchunks < 1) g.vchunks = 1;
-    g.G = (int32_t)((vq + g.vchunks - 1) / g.vchunks);
-    if (g.G < 1) g.G = 1;
     // prefix splits: enough workgroups (~512) to stream the prefix in parallel
     const int64_t per_split = (int64_t)num_kv_heads * g.vchunks;
     int64_t want = (kPrefixGroups + per_split - 1) / per_split;

@@ -13,12 +13,10 @@
 // end.  The partial (max in log2 units, sum, unnormalised output) goes to
 // the fp32 workspace.
 //
-// Shared-prefix (cascade) decode: when many rows begin with the same cached
-// blocks, a prefix launch reads those blocks once per KV head for all the
-// (row, query head) pairs that use it -- the "virtual queries" -- and writes
-// one partial per pair and prefix split; the ordinary partial launch then
-// covers each row's own positions after the prefix, and the reduce merges
-// both kinds of partial alike.
+// Shared-prefix (cascade) decode: the prefix launch (matrix-core kernel)
+// writes one partial per (row, query head) and prefix split; this kernel,
+// started at pos_base with its slots after the prefix ones, covers each
+// row's own positions, and the reduce merges both kinds of partial alike.
 //
 // Reduce step: one wave per (row, query head) merges the row's partials,
 // O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, and writes bf16.
@@ -33,10 +31,9 @@ constexpr int kWaves = 4;                 // waves per partial workgroup
 constexpr int kChunk = 16;                // positions per wave iteration
 constexpr int kRound = kWaves * kChunk;   // positions per workgroup iteration
 
-template <int D, int G, bool FUSED, bool PREFIX>
+template <int D, int G, bool FUSED>
 __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const PartialArgs a)
 {
-    static_assert(!(FUSED && PREFIX), "the prefix launch stores nothing");
     constexpr int LPT = D / 8;        // lanes per position
     constexpr int GPW = 64 / LPT;     // lane groups per wave
     constexpr int U = kChunk / GPW;   // positions per lane group per iteration
@@ -48,62 +45,28 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     const int li = lane % LPT;
 
     int x = blockIdx.x;
-    int hc, kvh, b, s;
-    if constexpr (PREFIX) {
-        hc = x % a.vchunks;   // chunk of virtual queries
-        x /= a.vchunks;
-        kvh = x % a.num_kv_heads;
-        s = x / a.num_kv_heads;
-        b = 0;
-    } else {
-        hc = x % a.head_chunks;
-        x /= a.head_chunks;
-        kvh = x % a.num_kv_heads;
-        x /= a.num_kv_heads;
-        b = x % a.batch;
-        s = x / a.batch;
-    }
+    const int hc = x % a.head_chunks;
+    x /= a.head_chunks;
+    const int kvh = x % a.num_kv_heads;
+    x /= a.num_kv_heads;
+    const int b = x % a.batch;
+    const int s = x / a.batch;
 
-    int n, t_begin, t_end, pos_new = -1;
-    if constexpr (PREFIX) {
-        t_begin = s * a.split_tokens;
-        t_end = min(a.prefix_len, t_begin + a.split_tokens);
-        n = t_end;
-    } else {
-        const int n_row = a.context_lens[b];
-        n = min(max(n_row, 0), a.max_len);
-        t_begin = a.pos_base + s * a.split_tokens;
-        if (t_begin >= n) return;
-        // fused store: the row's new position, if it lies inside the attended range
-        if (FUSED && n_row >= 1 && n_row <= n) pos_new = n_row - 1;
-        t_end = min(n, t_begin + a.split_tokens);
-    }
+    const int n_row = a.context_lens[b];
+    const int n = min(max(n_row, 0), a.max_len);
+    const int t_begin = a.pos_base + s * a.split_tokens;
+    if (t_begin >= n) return;
+    // fused store: the row's new position, if it lies inside the attended range
+    const int pos_new = (FUSED && n_row >= 1 && n_row <= n) ? n_row - 1 : -1;
+    const int t_end = min(n, t_begin + a.split_tokens);
     const int h0 = kvh * a.group + hc * G;
     const float c = a.c;
 
-    // Query j of this workgroup: query head h0 + j of row b, or in the prefix
-    // launch virtual query v = hc*G + j, i.e. query head kvh*group + v%group
-    // of row v/group, which attends to the prefix positions below its own
-    // row length; lim[j] bounds the positions query j attends to.
     uint4 qv[G];
-    int lim[G];
+    {
+        const uint16_t *qrow = a.q + (int64_t)b * a.q_stride + (int64_t)h0 * D + li * 8;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        if constexpr (PREFIX) {
-            const int v = hc * G + h;
-            const bool real = v < a.vq_per_kv;
-            const int rb = real ? v / a.group : 0;
-            const int rh = kvh * a.group + (real ? v % a.group : 0);
-            const int nr = real ? min(max(a.context_lens[rb], 0), a.max_len) : 0;
-            lim[h] = min(t_end, nr);
-            qv[h] = real ? *reinterpret_cast<const uint4 *>(a.q + (int64_t)rb * a.q_stride +
-                                                            (int64_t)rh * D + li * 8)
-                         : make_uint4(0u, 0u, 0u, 0u);
-        } else {
-            lim[h] = t_end;
-            qv[h] = *reinterpret_cast<const uint4 *>(a.q + (int64_t)b * a.q_stride +
-                                                     (int64_t)(h0 + h) * D + li * 8);
-        }
+        for (int h = 0; h < G; ++h) qv[h] = *reinterpret_cast<const uint4 *>(qrow + h * D);
     }
 
     float m[G], l[G], o[G][8];
@@ -118,7 +81,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     const int64_t tok_stride = (int64_t)a.num_kv_heads * D;
     const int64_t lane_off = (int64_t)kvh * D + li * 8 + (int64_t)(gi * U) * tok_stride;
     const int bs_mask = (1 << a.bs_log2) - 1;
-    const int32_t *table = PREFIX ? a.prefix_blocks : a.block_tables + (int64_t)b * a.table_stride;
+    const int32_t *table = a.block_tables + (int64_t)b * a.table_stride;
 
     // Issue the K/V loads of the chunk starting at t0 (one block, U positions
     // per lane group, one 16-byte piece per lane and position).
@@ -128,27 +91,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
         const int blk = blk_ok ? raw : 0;
         const int64_t base =
             (((int64_t)blk << a.bs_log2) + (t0 & bs_mask)) * tok_stride + lane_off;
-        if (FUSED && pos_new >= t0 && pos_new < t0 + kChunk) {
-            // this chunk holds the new position: its K/V come from k_new/v_new,
-            // and the first query-head chunk stores them in the pools
-            const int64_t noff = (int64_t)b * a.new_stride + (int64_t)kvh * D + li * 8;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t off = base + u * tok_stride;
-                if (t0 + gi * U + u == pos_new) {
-                    kr[u] = *reinterpret_cast<const uint4 *>(a.k_new + noff);
-                    vr[u] = *reinterpret_cast<const uint4 *>(a.v_new + noff);
-                    if (hc == 0 && blk_ok) {
-                        *reinterpret_cast<uint4 *>(a.k_cache_w + off) = kr[u];
-                        *reinterpret_cast<uint4 *>(a.v_cache_w + off) = vr[u];
-                    }
-                } else {
-                    kr[u] = load_stream16(a.k_cache + off);
-                    vr[u] = load_stream16(a.v_cache + off);
-                }
-            }
-            return;
-        }
 #pragma unroll
         for (int u = 0; u < U; ++u)
             kr[u] = load_stream16(a.k_cache + base + u * tok_stride);
@@ -184,7 +126,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
                 acc = dot2_bf16(qv[h].z, kr[u].z, acc);
                 acc = dot2_bf16(qv[h].w, kr[u].w, acc);
                 acc = group_sum<LPT>(acc);
-                sc[u] = (tg + u < lim[h]) ? acc : -INFINITY;
+                sc[u] = (tg + u < t_end) ? acc : -INFINITY;
             }
             float mx = m[h];
 #pragma unroll
@@ -215,8 +157,30 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
         }
     };
 
-    // Double-buffered stream: the next chunk's loads are in flight while the
-    // current chunk is computed.
+    if constexpr (FUSED) {
+        // Fused store: the workgroup whose range holds the row's new position
+        // first writes that position's K/V row (this KV head) into the pool,
+        // then streams it back like every other position.  Every query-head
+        // chunk of the KV head writes the same bytes.  The barrier orders the
+        // stores before the other waves' loads: all waves of a workgroup run
+        // on one CU and share its write-through vector L1.
+        if (pos_new >= t_begin && pos_new < t_end) {
+            const int raw = load_block_id(table, pos_new >> a.bs_log2);
+            constexpr int PIECES = D / 8;
+            if (raw >= 0 && raw < a.num_blocks && (int)threadIdx.x < 2 * PIECES) {
+                const bool isv = (int)threadIdx.x >= PIECES;
+                const int piece = (int)threadIdx.x - (isv ? PIECES : 0);
+                const int64_t dst = (((int64_t)raw << a.bs_log2) + (pos_new & bs_mask)) * tok_stride +
+                                    (int64_t)kvh * D + piece * 8;
+                const int64_t src = (int64_t)b * a.new_stride + (int64_t)kvh * D + piece * 8;
+                const uint4 v = *reinterpret_cast<const uint4 *>((isv ? a.v_new : a.k_new) + src);
+                *reinterpret_cast<uint4 *>((isv ? a.v_cache_w : a.k_cache_w) + dst) = v;
+            }
+            __syncthreads();
+        }
+    }
+
+    // One chunk per wave iteration: loads, then the online-softmax update.
     for (int t0 = t_begin + wave * kChunk; t0 < t_end; t0 += kRound) {
         uint4 ka[U], va[U];
         load_chunk(t0, ka, va);
@@ -265,8 +229,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-        // a query that saw no position (prefix launch, short row) keeps
-        // M = -inf, l = 0, o = 0: it weighs nothing in the reduce
+        // a head whose waves all saw no position keeps M = -inf, l = 0, o = 0
         const float ref = (M == -INFINITY) ? 0.f : M;
         float L = 0.f, O = 0.f;
 #pragma unroll
@@ -275,13 +238,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
             L += s_l[w][h] * e;
             O += s_o[w][h][d] * e;
         }
-        int64_t pidx = pbase + (int64_t)h * a.num_splits;
-        if constexpr (PREFIX) {
-            const int v = hc * G + h;
-            if (v >= a.vq_per_kv) continue;
-            const int rb = v / a.group, rh = kvh * a.group + v % a.group;
-            pidx = ((int64_t)rb * a.num_q_heads + rh) * a.num_splits + s;
-        }
+        const int64_t pidx = pbase + (int64_t)h * a.num_splits;
         a.part_o[pidx * D + d] = O;
         if (d == 0) {
             a.part_ml[2 * pidx] = M * c;
@@ -389,37 +346,30 @@ SplitGeometry split_geometry(int32_t batch, int32_t num_q_heads, int32_t head_di
     return g;
 }
 
-template <int D, int G, bool PREFIX>
+template <int D, int G>
 static void launch_partial_g(const PartialArgs &a, hipStream_t stream)
 {
-    if constexpr (PREFIX) {
-        // prefix splits x KV heads x virtual-query chunks
-        const int64_t grid = (int64_t)((a.prefix_len + a.split_tokens - 1) / a.split_tokens) *
-                             a.num_kv_heads * a.vchunks;
-        decode_partial_kernel<D, G, false, true><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
-    } else {
-        // tail splits (all splits when pos_base = 0) x rows x KV heads x head chunks
-        const int64_t grid = (int64_t)(a.num_splits - a.split_base) * a.batch *
-                             a.num_kv_heads * a.head_chunks;
-        if (a.k_new)
-            decode_partial_kernel<D, G, true, false><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
-        else
-            decode_partial_kernel<D, G, false, false><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
-    }
+    // splits after pos_base (all splits when pos_base = 0) x rows x KV heads x head chunks
+    const int64_t grid =
+        (int64_t)(a.num_splits - a.split_base) * a.batch * a.num_kv_heads * a.head_chunks;
+    if (a.k_new)
+        decode_partial_kernel<D, G, true><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
+    else
+        decode_partial_kernel<D, G, false><<<(unsigned)grid, kWaves * 64, 0, stream>>>(a);
 }
 
-template <int D, bool PREFIX>
+template <int D>
 static hipError_t launch_partial_d(const PartialArgs &a, int G, hipStream_t stream)
 {
     switch (G) {
-    case 1: launch_partial_g<D, 1, PREFIX>(a, stream); break;
-    case 2: launch_partial_g<D, 2, PREFIX>(a, stream); break;
-    case 3: launch_partial_g<D, 3, PREFIX>(a, stream); break;
-    case 4: launch_partial_g<D, 4, PREFIX>(a, stream); break;
-    case 5: launch_partial_g<D, 5, PREFIX>(a, stream); break;
-    case 6: launch_partial_g<D, 6, PREFIX>(a, stream); break;
-    case 7: launch_partial_g<D, 7, PREFIX>(a, stream); break;
-    case 8: launch_partial_g<D, 8, PREFIX>(a, stream); break;
+    case 1: launch_partial_g<D, 1>(a, stream); break;
+    case 2: launch_partial_g<D, 2>(a, stream); break;
+    case 3: launch_partial_g<D, 3>(a, stream); break;
+    case 4: launch_partial_g<D, 4>(a, stream); break;
+    case 5: launch_partial_g<D, 5>(a, stream); break;
+    case 6: launch_partial_g<D, 6>(a, stream); break;
+    case 7: launch_partial_g<D, 7>(a, stream); break;
+    case 8: launch_partial_g<D, 8>(a, stream); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -430,17 +380,8 @@ hipError_t launch_decode_partial(const PartialArgs &a, int32_t head_dim, hipStre
     if (a.batch == 0 || a.num_splits <= a.split_base) return hipSuccess;
     if (a.group >= kMfmaMinGroup) return launch_decode_partial_mfma(a, head_dim, stream);
     const int G = a.group / a.head_chunks;
-    if (head_dim == 128) return launch_partial_d<128, false>(a, G, stream);
-    if (head_dim == 64) return launch_partial_d<64, false>(a, G, stream);
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode_prefix(const PartialArgs &a, int32_t head_dim, int32_t G,
-                                hipStream_t stream)
-{
-    if (a.batch == 0 || a.prefix_len <= 0) return hipSuccess;
-    if (head_dim == 128) return launch_partial_d<128, true>(a, G, stream);
-    if (head_dim == 64) return launch_partial_d<64, true>(a, G, stream);
+    if (head_dim == 128) return launch_partial_d<128>(a, G, stream);
+    if (head_dim == 64) return launch_partial_d<64>(a, G, stream);
     return hipErrorInvalidValue;
 }
 

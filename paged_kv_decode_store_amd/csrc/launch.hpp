@@ -52,20 +52,20 @@ struct PartialArgs {
     int32_t split_tokens;
     int32_t num_splits;
     float c;                // softmax scale * log2(e)
-    // fused store: when k_new is non-null, each row's new position
-    // (context_lens[b] - 1) takes its K/V from k_new/v_new and the first
-    // query-head chunk writes them into the pools
+    // fused store: when k_new is non-null, the workgroups whose range holds
+    // a row's new position (context_lens[b] - 1) write its K/V rows from
+    // k_new/v_new into the pools before streaming the range
     const uint16_t *k_new;
     const uint16_t *v_new;
     int64_t new_stride;     // elements between consecutive rows of k_new/v_new
     uint16_t *k_cache_w;    // same pools as k_cache/v_cache, written by the fused store
     uint16_t *v_cache_w;
     // shared-prefix (cascade) decode.  Tail launch: positions start at
-    // pos_base and partial s goes to slot split_base + s.  Prefix launch
-    // (prefix_blocks non-null): one workgroup per (prefix split, KV head,
-    // chunk of virtual queries), where the virtual queries of a KV head are
-    // the (row, query head) pairs that use it, vq_per_kv = batch * group;
-    // positions [0, prefix_len) are read once through prefix_blocks.
+    // pos_base and partial s goes to slot split_base + s.  Prefix launch:
+    // one workgroup per (prefix split, KV head, chunk of virtual queries),
+    // where the virtual queries of a KV head are the (row, query head) pairs
+    // that use it, vq_per_kv = batch * group; positions [0, prefix_len) are
+    // read once through prefix_blocks.
     int32_t pos_base;
     int32_t split_base;
     const int32_t *prefix_blocks;
@@ -91,19 +91,14 @@ struct ReduceArgs {
 
 hipError_t launch_decode_partial(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceArgs &a, int32_t head_dim, hipStream_t stream);
-// Prefix step of the cascade decode: `a` describes the prefix launch; G is
-// the number of virtual queries per workgroup.
-hipError_t launch_decode_prefix(const PartialArgs &a, int32_t head_dim, int32_t G,
-                                hipStream_t stream);
-// Matrix-core versions of the partial and prefix steps (up to 16 query heads
-// or virtual queries per workgroup; head_chunks / vchunks are derived).
+// Matrix-core partial step (up to 16 query heads per workgroup; head_chunks
+// is derived), and the prefix step of the cascade decode on the same kernel
+// (`a` describes the prefix launch; 16 virtual queries per workgroup).
 hipError_t launch_decode_partial_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_decode_prefix_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
-// Group sizes from which the partial step runs on the matrix cores.
-#ifndef PKV_MFMA_MIN_GROUP
-#define PKV_MFMA_MIN_GROUP 3
-#endif
-constexpr int32_t kMfmaMinGroup = PKV_MFMA_MIN_GROUP;
+// Group sizes from which the partial step runs on the matrix cores (the VALU
+// kernel is ALU-bound beyond group 2 on MI355X).
+constexpr int32_t kMfmaMinGroup = 3;
 
 // Sampler
 size_t sampler_workspace_bytes(int32_t batch, int32_t vocab);
