@@ -29,6 +29,14 @@ class SampleInfo(ctypes.Structure):
     ]
 
 
+class SampleExtras(ctypes.Structure):
+    _fields_ = [
+        ("chosen_prob", ctypes.c_double),
+        ("top_ids", ctypes.c_int32 * 8),
+        ("top_probs", ctypes.c_double * 8),
+    ]
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -57,6 +65,9 @@ def lib():
         L.oracle_sample_row.restype = ctypes.c_int32
         L.oracle_sample_row.argtypes = [P, P, I64, ctypes.c_float, ctypes.c_float, ctypes.c_int32,
                                         ctypes.POINTER(SampleInfo)]
+        L.oracle_sample_row_ex.restype = ctypes.c_int32
+        L.oracle_sample_row_ex.argtypes = [P, P, P, I64, ctypes.c_float, ctypes.c_float,
+                                           ctypes.c_int32, P, P]
         L.oracle_sample.restype = None
         L.oracle_sample.argtypes = [P, P, P, I64, P, I64, P, P, P, I64, I64]
         _lib = L
@@ -159,6 +170,19 @@ def sample_row(logits, gumbel, temperature, top_p, top_k):
     lib().oracle_sample_row(_ptr(z), _ptr(g), z.shape[0], float(temperature), float(top_p),
                             int(top_k), ctypes.byref(info))
     return info
+
+
+def sample_row_ex(logits, gumbel, temperature, top_p, top_k, mask=None):
+    """One row with the vocabulary mask (uint8/bool [V], nonzero = allowed,
+    or None) and the extra outputs; returns (SampleInfo, SampleExtras)."""
+    z = _c(logits, np.float32)
+    g = _c(gumbel, np.float32)
+    m = None if mask is None else _c(mask, np.uint8)
+    info, extras = SampleInfo(), SampleExtras()
+    lib().oracle_sample_row_ex(_ptr(z), _ptr(g), None if m is None else _ptr(m), z.shape[0],
+                               float(temperature), float(top_p), int(top_k),
+                               ctypes.byref(info), ctypes.byref(extras))
+    return info, extras
 
 
 def sample(logits, gumbel, temperature, top_p, top_k):

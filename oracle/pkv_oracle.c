@@ -272,25 +272,67 @@ static int cmp_float_asc(const void *pa, const void *pb)
     return (a > b) - (a < b);
 }
 
-int32_t oracle_sample_row(const float *logits, const float *gumbel,
-                          int64_t vocab, float temperature, float top_p,
-                          int32_t top_k, oracle_sample_info *info)
+/* Fills extras for the greedy limit: uniform over the tied maxima of v. */
+static void greedy_extras(const float *v, int64_t vocab, float vmax, int64_t id,
+                          oracle_sample_extras *x)
+{
+    int64_t ties = 0;
+    for (int64_t i = 0; i < vocab; ++i)
+        if (v[i] == vmax)
+            ++ties;
+    x->chosen_prob = 1.0 / (double)ties;
+    (void)id;
+    int r = 0;
+    for (int64_t i = 0; i < vocab && r < 8; ++i)
+        if (v[i] == vmax) {
+            x->top_ids[r] = (int32_t)i;
+            x->top_probs[r++] = 1.0 / (double)ties;
+        }
+    for (int64_t i = 0; i < vocab && r < 8; ++i)
+        if (v[i] != vmax) {
+            x->top_ids[r] = (int32_t)i;
+            x->top_probs[r++] = 0.0;
+        }
+    for (; r < 8; ++r) {
+        x->top_ids[r] = -1;
+        x->top_probs[r] = 0.0;
+    }
+}
+
+int32_t oracle_sample_row_ex(const float *logits, const float *gumbel,
+                             const unsigned char *mask, int64_t vocab,
+                             float temperature, float top_p, int32_t top_k,
+                             oracle_sample_info *info, oracle_sample_extras *extras)
 {
     oracle_sample_info local;
     if (!info)
         info = &local;
     memset(info, 0, sizeof *info);
+    if (extras)
+        memset(extras, 0, sizeof *extras);
+    const float masked = -1e10f;   /* the runner's value for forbidden tokens */
 
     /* T = 0 is the greedy limit of temperature sampling ([grok] 8.1.1,
-     * 8.3); a non-positive temperature is read as that limit. */
+     * 8.3); a non-positive temperature is read as that limit.  The mask
+     * still applies: forbidden tokens count as -1e10. */
     if (!(temperature > 0.0f)) {
+        float *v = (float *)malloc((size_t)vocab * sizeof(float));
+        if (!v) {
+            info->id = -1;
+            return -1;
+        }
+        for (int64_t i = 0; i < vocab; ++i)
+            v[i] = (mask && !mask[i]) ? masked : logits[i];
         int64_t best = 0;
         for (int64_t i = 1; i < vocab; ++i)
-            if (logits[i] > logits[best])
+            if (v[i] > v[best])
                 best = i;
         info->id = (int32_t)best;
         info->greedy = 1;
         info->kept = 1;
+        if (extras)
+            greedy_extras(v, vocab, v[best], best, extras);
+        free(v);
         return info->id;
     }
 
@@ -305,9 +347,12 @@ int32_t oracle_sample_row(const float *logits, const float *gumbel,
         return -1;
     }
 
-    /* 1. temperature: one IEEE fp32 division per logit */
+    /* 1. temperature: one IEEE fp32 division per logit; then the mask:
+     * forbidden tokens get -1e10 (section 8.3, in that order) */
     for (int64_t i = 0; i < vocab; ++i) {
         s[i] = logits[i] / temperature;
+        if (mask && !mask[i])
+            s[i] = masked;
         keep[i] = 1;
     }
 
@@ -399,8 +444,51 @@ int32_t oracle_sample_row(const float *logits, const float *gumbel,
     }
     info->id = (int32_t)best;
     info->kept = kept;
+
+    /* 5. extras: softmax over the kept scaled logits (the filtered ones are
+     * -1e10 on the page, exactly 0 after the softmax), the drawn id's
+     * probability, and the top 8 by probability, ties to the lower index */
+    if (extras) {
+        double mx = -INFINITY;
+        for (int64_t i = 0; i < vocab; ++i)
+            if (keep[i] && (double)s[i] > mx)
+                mx = s[i];
+        double z = 0.0;
+        for (int64_t i = 0; i < vocab; ++i)
+            if (keep[i])
+                z += exp((double)s[i] - mx);
+        extras->chosen_prob = exp((double)s[best] - mx) / z;
+        for (int64_t i = 0; i < vocab; ++i) {
+            order[i].v = s[i];
+            order[i].i = i;
+        }
+        qsort(order, (size_t)vocab, sizeof *order, cmp_desc_value_asc_index);
+        int r = 0;
+        for (int64_t j = 0; j < vocab && r < 8; ++j)
+            if (keep[order[j].i]) {
+                extras->top_ids[r] = (int32_t)order[j].i;
+                extras->top_probs[r++] = exp((double)order[j].v - mx) / z;
+            }
+        for (int64_t i = 0; i < vocab && r < 8; ++i)
+            if (!keep[i]) {
+                extras->top_ids[r] = (int32_t)i;
+                extras->top_probs[r++] = 0.0;
+            }
+        for (; r < 8; ++r) {
+            extras->top_ids[r] = -1;
+            extras->top_probs[r] = 0.0;
+        }
+    }
     free(s); free(keep); free(order); free(asc); free(cum);
     return info->id;
+}
+
+int32_t oracle_sample_row(const float *logits, const float *gumbel,
+                          int64_t vocab, float temperature, float top_p,
+                          int32_t top_k, oracle_sample_info *info)
+{
+    return oracle_sample_row_ex(logits, gumbel, NULL, vocab, temperature, top_p, top_k, info,
+                                NULL);
 }
 
 void oracle_sample(int32_t *ids, oracle_sample_info *infos,

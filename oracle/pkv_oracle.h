@@ -102,6 +102,28 @@ int32_t oracle_sample_row(const float *logits, const float *gumbel,
                           int64_t vocab, float temperature, float top_p,
                           int32_t top_k, oracle_sample_info *info);
 
+/* The runner's extra sampler outputs (Grok-1 runner chapter, section 8.3:
+ * the probability of the drawn token under the filtered distribution, and
+ * the top-8 (TOP_K = 8) ids and probabilities for debugging). */
+typedef struct {
+    double chosen_prob;  /* softmax of the kept scaled logits at the drawn id */
+    int32_t top_ids[8];  /* kept ids by (scaled logit desc, index asc), then
+                            the lowest-index ids outside the kept set */
+    double top_probs[8]; /* their probabilities (0 outside the kept set) */
+} oracle_sample_extras;
+
+/* oracle_sample_row with the vocabulary mask of section 8.3 (mask[i] == 0:
+ * the scaled logit is replaced by -1e10 before the filters; NULL: no mask)
+ * and, when extras is non-NULL, the extra outputs.  A non-positive
+ * temperature is the greedy limit: the drawn id is the lowest index of the
+ * largest masked raw logit, and the distribution is uniform over the tied
+ * largest values. */
+int32_t oracle_sample_row_ex(const float *logits, const float *gumbel,
+                             const unsigned char *mask, int64_t vocab,
+                             float temperature, float top_p, int32_t top_k,
+                             oracle_sample_info *info,
+                             oracle_sample_extras *extras);
+
 void oracle_sample(int32_t *ids, oracle_sample_info *infos,
                    const float *logits, int64_t logits_stride,
                    const float *gumbel, int64_t gumbel_stride,

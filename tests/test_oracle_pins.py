@@ -434,3 +434,121 @@ def test_workload_tables_are_consistent():
             owned.append(row[cfg.clone_prefix_blocks:])
         allowned = np.concatenate(owned)
         assert len(set(allowned.tolist())) == len(allowned)
+
+
+# ------------------------------------------- sampler mask and extra outputs --
+
+def _softmax64(x):
+    # scipy's softmax, the library routine the unfiltered case reduces to
+    from scipy.special import softmax
+    return softmax(np.asarray(x, np.float64))
+
+
+def test_extras_without_filters_equal_library_softmax():
+    """p = 1, k = 0, no mask: the drawn id's probability and the top 8 are
+    those of softmax(z / T) (stable argsort for the order)."""
+    rng = np.random.default_rng(91)
+    V = 300
+    z = (rng.standard_normal(V) * 2).astype(np.float32)
+    z[[10, 11]] = z.max() + 1.0          # a tie at the top: lower index first
+    g = rng.gumbel(size=V).astype(np.float32)
+    T = np.float32(0.7)
+    info, x = oracle.sample_row_ex(z, g, T, 1.0, 0)
+    pr = _softmax64(z / T)
+    assert abs(x.chosen_prob - pr[info.id]) < 1e-12
+    order = np.argsort(-pr, kind="stable")[:8]
+    assert list(x.top_ids) == order.tolist()
+    assert np.allclose(list(x.top_probs), pr[order], rtol=1e-12, atol=0)
+    assert x.top_ids[0] == 10 and x.top_ids[1] == 11
+
+
+def test_mask_forbids_tokens_and_is_applied_after_temperature():
+    rng = np.random.default_rng(92)
+    V = 50
+    z = rng.standard_normal(V).astype(np.float32)
+    mask = np.zeros(V, np.uint8)
+    mask[[3, 17, 40]] = 1
+    for trial in range(200):
+        g = rng.gumbel(size=V).astype(np.float32)
+        info, x = oracle.sample_row_ex(z, g, 1.3, 1.0, 0, mask=mask)
+        assert info.id in (3, 17, 40)
+        assert x.top_ids[:3].__len__() == 3 and set(x.top_ids[:3]) == {3, 17, 40}
+        assert all(p == 0.0 for p in x.top_probs[3:])
+        assert abs(sum(x.top_probs) - 1.0) < 1e-12
+    # the page divides by T first, then sets forbidden tokens to -1e10: with
+    # T = 0.05 an allowed logit of -1e9 scales to -2e10, below the forbidden
+    # tokens' -1e10, so a forbidden token (the lowest-index one) is drawn
+    z2 = np.full(4, -1e9, np.float32)
+    info, _ = oracle.sample_row_ex(z2, np.zeros(4, np.float32), 0.05, 1.0, 0,
+                                   mask=np.array([1, 0, 1, 0], np.uint8))
+    assert info.id == 1
+
+
+def test_all_masked_row_is_uniform():
+    V = 37
+    z = np.linspace(-3, 3, V).astype(np.float32)
+    g = np.random.default_rng(93).gumbel(size=V).astype(np.float32)
+    info, x = oracle.sample_row_ex(z, g, 1.0, 1.0, 0, mask=np.zeros(V, np.uint8))
+    # every key is fl32(-1e10 + g) == -1e10: a tie, lowest index
+    assert info.id == 0
+    assert abs(x.chosen_prob - 1.0 / V) < 1e-15
+    assert list(x.top_ids) == list(range(8))
+
+
+def test_extras_under_top_k_and_nucleus():
+    z = np.array([0.5, 3.0, 2.0, -1.0, 2.0, 1.0, 0.0, -2.0, 1.5, 0.2], np.float32)
+    g = np.zeros_like(z)
+    # top-k 3: the kept set is {1, 2, 4} (2.0 tie: both kept, k = 3)
+    info, x = oracle.sample_row_ex(z, g, 1.0, 1.0, 3)
+    pr = _softmax64(z[[1, 2, 4]])
+    assert list(x.top_ids[:3]) == [1, 2, 4]
+    assert np.allclose(list(x.top_probs[:3]), pr, rtol=1e-12, atol=0)
+    # then the lowest-index ids outside the kept set, probability 0
+    assert list(x.top_ids[3:]) == [0, 3, 5, 6, 7]
+    assert list(x.top_probs[3:]) == [0.0] * 5
+    assert info.id == 1 and abs(x.chosen_prob - pr[0]) < 1e-12
+    # nucleus p = 0.5 on the full set keeps the smallest prefix with mass
+    # > 0.5, plus every value tied with its last one (here: 2.0 twice)
+    full = _softmax64(z)
+    order = np.argsort(-full, kind="stable")
+    last = order[np.searchsorted(np.cumsum(full[order]), 0.5, side="right")]
+    keep = np.nonzero(z >= z[last])[0]
+    assert len(keep) == 3
+    info, x = oracle.sample_row_ex(z, g, 1.0, 0.5, 0)
+    assert info.kept == len(keep)
+    pk = _softmax64(z[np.sort(keep)])
+    got = dict(zip(x.top_ids[:len(keep)], x.top_probs[:len(keep)]))
+    for i, p in zip(np.sort(keep), pk):
+        assert abs(got[i] - p) < 1e-12
+
+
+def test_greedy_extras_split_ties_and_respect_the_mask():
+    z = np.array([1.0, 4.0, 2.0, 4.0, 4.0, 0.0], np.float32)
+    info, x = oracle.sample_row_ex(z, np.zeros_like(z), 0.0, 1.0, 0)
+    assert info.id == 1 and abs(x.chosen_prob - 1 / 3) < 1e-15
+    assert list(x.top_ids[:3]) == [1, 3, 4] and list(x.top_ids[3:6]) == [0, 2, 5]
+    info, x = oracle.sample_row_ex(z, np.zeros_like(z), 0.0, 1.0, 0,
+                                   mask=np.array([1, 0, 1, 0, 0, 1], np.uint8))
+    assert info.id == 2 and x.chosen_prob == 1.0
+
+
+def test_masked_draws_follow_renormalised_softmax():
+    """Chi-square over 40000 draws with a mask and top-k 4: ids follow the
+    softmax of the scaled logits restricted to the allowed top-4."""
+    rng = np.random.default_rng(94)
+    V, N = 10, 40000
+    z = np.array([2.5, 2.0, 1.8, 1.0, 0.7, 0.5, 0.0, -0.4, -1.0, -2.0], np.float32)
+    mask = np.array([0, 1, 1, 0, 1, 1, 1, 1, 0, 1], np.uint8)
+    T = np.float32(0.9)
+    allowed = np.nonzero(mask)[0]
+    top = allowed[np.argsort(-(z[allowed] / T), kind="stable")[:4]]
+    probs = _softmax64((z[top] / T).astype(np.float64))
+    counts = np.zeros(V, np.int64)
+    for _ in range(N):
+        g = rng.gumbel(size=V).astype(np.float32)
+        info, _ = oracle.sample_row_ex(z, g, T, 1.0, 4, mask=mask)
+        counts[info.id] += 1
+    assert counts.sum() == counts[top].sum()
+    exp_ = probs * N
+    chi2 = float(np.sum((counts[top] - exp_) ** 2 / exp_))
+    assert chi2 < 16.3, (chi2, counts[top], exp_)   # 99.9% quantile, 3 dof
