@@ -288,6 +288,34 @@ int pkv_sample_next_token(int32_t *out_ids, const float *logits,
                           void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/* The sampler with the runner's vocabulary mask and extra outputs (Grok-1
+ * runners chapter, section 8.3: sample_token scales by 1/T, replaces the
+ * logits of forbidden tokens by -1e10, filters, draws, and also returns the
+ * drawn token's probability and the top 8 (TOP_K = 8) ids and
+ * probabilities of the filtered distribution for debugging).
+ * vocab_mask     uint8 [batch][vocab], row b at b*mask_stride (0 = packed);
+ *                0 = forbidden: s_i = -1e10 after the scaling (greedy rows:
+ *                the raw logit counts as -1e10).  NULL: no mask.
+ * out_prob       fp32 [batch] or NULL: softmax over the kept s at the drawn
+ *                id (greedy rows: 1 / number of tied maxima)
+ * out_top_ids    int32 [batch][8] or NULL: the kept ids of largest s (ties
+ *                to the lower index); fewer than 8 kept are followed by the
+ *                lowest-index ids outside the kept set; -1 past vocab
+ * out_top_probs  fp32 [batch][8] or NULL: their probabilities (0 outside
+ *                the kept set)
+ * When any output pointer is non-NULL one more workgroup per row reads the
+ * row after the draw.  Everything else is as for pkv_sample_next_token,
+ * which equals this call with NULL mask and outputs. */
+int pkv_sample_next_token_ex(int32_t *out_ids, const float *logits,
+                             int64_t logits_stride, const float *gumbel,
+                             int64_t gumbel_stride, const uint8_t *vocab_mask,
+                             int64_t mask_stride, const float *temperature,
+                             const float *top_p, const int32_t *top_k,
+                             int32_t batch, int32_t vocab, uint32_t flags,
+                             float *out_prob, int32_t *out_top_ids,
+                             float *out_top_probs, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ __all__ = [
     "decode_attention_reduce", "decode_workspace_bytes", "decode_split_tokens",
     "paged_decode_attention_store", "decode_attention_partial_store",
     "cascade_decode_attention", "cascade_workspace_bytes",
-    "sample_next_token", "sampler_workspace_bytes", "PkvError",
+    "sample_next_token", "sample_next_token_ex", "sampler_workspace_bytes", "PkvError",
     "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
 ]
 
@@ -272,3 +272,45 @@ def sample_next_token(logits: torch.Tensor, gumbel: torch.Tensor, temperature: t
         _dev(top_k, "top_k", torch.int32), B, V, flags, ws.data_ptr(), ws.numel(), _stream()),
         "pkv_sample_next_token")
     return out
+
+
+def sample_next_token_ex(logits: torch.Tensor, gumbel: torch.Tensor, temperature: torch.Tensor,
+                         top_p: torch.Tensor, top_k: torch.Tensor,
+                         mask: Optional[torch.Tensor] = None, flags: Optional[int] = None,
+                         extras: bool = True, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """Next-token ids with the vocabulary mask (uint8/bool [B, V], nonzero =
+    allowed, or None) and, when extras is true, the drawn token's
+    probability [B] and the top-8 ids / probabilities [B, 8].  Returns ids,
+    or (ids, prob, top_ids, top_probs)."""
+    B, V = logits.shape
+    if logits.stride(1) != 1 or gumbel.stride(1) != 1 or gumbel.shape != logits.shape:
+        raise ValueError("logits/gumbel must be [B, V] with unit element stride")
+    if flags is None:
+        flags = PKV_SAMPLE_TOPK | PKV_SAMPLE_TOPP
+    mptr, mstride = None, 0
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        if mask.shape != logits.shape or mask.stride(1) != 1:
+            raise ValueError("mask must be [B, V] with unit element stride")
+        mptr, mstride = _dev(mask, "mask", torch.uint8), mask.stride(0)
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    prob = top_ids = top_probs = None
+    if extras:
+        prob = torch.empty(B, dtype=torch.float32, device=logits.device)
+        top_ids = torch.empty((B, 8), dtype=torch.int32, device=logits.device)
+        top_probs = torch.empty((B, 8), dtype=torch.float32, device=logits.device)
+    ws = _workspace(sampler_workspace_bytes(B, V), logits.device, workspace)
+    check(lib().pkv_sample_next_token_ex(
+        _dev(out, "out", torch.int32), _dev(logits, "logits", torch.float32), logits.stride(0),
+        _dev(gumbel, "gumbel", torch.float32), gumbel.stride(0), mptr, mstride,
+        _dev(temperature, "temperature", torch.float32), _dev(top_p, "top_p", torch.float32),
+        _dev(top_k, "top_k", torch.int32), B, V, flags,
+        None if prob is None else prob.data_ptr(), None if top_ids is None else top_ids.data_ptr(),
+        None if top_probs is None else top_probs.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+        "pkv_sample_next_token_ex")
+    if not extras:
+        return out
+    return out, prob, top_ids, top_probs

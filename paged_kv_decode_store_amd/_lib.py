@@ -55,6 +55,8 @@ PROTOTYPES = {
     "pkv_sampler_workspace_bytes": (_SZ, [_I32, _I32]),
     "pkv_sample_next_token": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _U32,
                                              _P, _SZ, _P]),
+    "pkv_sample_next_token_ex": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _I32,
+                                                _I32, _U32, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None

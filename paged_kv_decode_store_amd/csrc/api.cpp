@@ -538,11 +538,12 @@ size_t pkv_sampler_workspace_bytes(int32_t batch, int32_t vocab)
     return pkv::sampler_workspace_bytes(batch, vocab);
 }
 
-int pkv_sample_next_token(int32_t *out_ids, const float *logits, int64_t logits_stride,
-                          const float *gumbel, int64_t gumbel_stride, const float *temperature,
-                          const float *top_p, const int32_t *top_k, int32_t batch, int32_t vocab,
-                          uint32_t flags, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream)
+int pkv_sample_next_token_ex(int32_t *out_ids, const float *logits, int64_t logits_stride,
+                             const float *gumbel, int64_t gumbel_stride, const uint8_t *vocab_mask,
+                             int64_t mask_stride, const float *temperature, const float *top_p,
+                             const int32_t *top_k, int32_t batch, int32_t vocab, uint32_t flags,
+                             float *out_prob, int32_t *out_top_ids, float *out_top_probs,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     REQUIRE(batch >= 0 && batch <= 65535, PKV_ERR_INVALID_ARG, "batch must be in [0, 65535]");
     REQUIRE(vocab > 0 && vocab <= (1 << 24), PKV_ERR_UNSUPPORTED,
@@ -551,21 +552,38 @@ int pkv_sample_next_token(int32_t *out_ids, const float *logits, int64_t logits_
             "unknown flag bits 0x%x", flags);
     const int64_t ls = logits_stride ? logits_stride : vocab;
     const int64_t gs = gumbel_stride ? gumbel_stride : vocab;
+    const int64_t ms = mask_stride ? mask_stride : vocab;
     REQUIRE(ls >= vocab && gs >= vocab, PKV_ERR_INVALID_ARG, "row strides must be >= vocab");
+    REQUIRE(!vocab_mask || ms >= vocab, PKV_ERR_INVALID_ARG, "mask_stride must be >= vocab");
     if (batch == 0) return PKV_OK;
     REQUIRE(out_ids && logits && gumbel && temperature && top_p && top_k, PKV_ERR_INVALID_ARG,
             "null pointer");
     REQUIRE(aligned(out_ids, 4) && aligned(logits, 4) && aligned(gumbel, 4) &&
                 aligned(temperature, 4) && aligned(top_p, 4) && aligned(top_k, 4),
             PKV_ERR_INVALID_ARG, "arrays must be 4-byte aligned");
+    REQUIRE((!out_prob || aligned(out_prob, 4)) && (!out_top_ids || aligned(out_top_ids, 4)) &&
+                (!out_top_probs || aligned(out_top_probs, 4)),
+            PKV_ERR_INVALID_ARG, "outputs must be 4-byte aligned");
     const size_t need = pkv::sampler_workspace_bytes(batch, vocab);
     REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,
             "workspace must be non-null and 256-byte aligned");
     REQUIRE(workspace_bytes >= need, PKV_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes",
             workspace_bytes, need);
-    return hip_status(pkv::launch_sampler(out_ids, logits, ls, gumbel, gs, temperature, top_p,
-                                          top_k, batch, vocab, flags, workspace, stream),
+    return hip_status(pkv::launch_sampler(out_ids, logits, ls, gumbel, gs, vocab_mask, ms,
+                                          temperature, top_p, top_k, batch, vocab, flags,
+                                          out_prob, out_top_ids, out_top_probs, workspace, stream),
                       "sampler launch");
+}
+
+int pkv_sample_next_token(int32_t *out_ids, const float *logits, int64_t logits_stride,
+                          const float *gumbel, int64_t gumbel_stride, const float *temperature,
+                          const float *top_p, const int32_t *top_k, int32_t batch, int32_t vocab,
+                          uint32_t flags, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream)
+{
+    return pkv_sample_next_token_ex(out_ids, logits, logits_stride, gumbel, gumbel_stride,
+                                    nullptr, 0, temperature, top_p, top_k, batch, vocab, flags,
+                                    nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -74,6 +74,8 @@ struct alignas(64) SampCtl {
     uint32_t rank;            // top-k: logits of the threshold bin to keep
     uint32_t ncand;           // logits of the threshold bin appended
     uint32_t round2;          // 1 while a second collect round is pending
+    uint32_t tau;             // final cut: kept logits have key(s) >= tau (0: none)
+    unsigned long long kpack; // top-k cut: kept have (key, ~index) >= kpack (0: none)
 };
 static_assert(sizeof(SampCtl) == 64, "control block");
 
@@ -130,7 +132,15 @@ struct SampArgs {
     uint32_t *kap;                 // [B][kCap]  key of fl32(s + g)
     uint32_t *part_max;            // [B][nchunks] key of the chunk max of s
     unsigned long long *part_best; // [B][nchunks] best packed Gumbel key of the chunk
+    const uint8_t *mask;           // [B][V] (row b at b*mstride), 0 = forbidden; or null
+    int64_t mstride;
+    float *out_prob;               // [B] probability of the drawn id, or null
+    int32_t *out_top_ids;          // [B][8], or null
+    float *out_top_probs;          // [B][8], or null
 };
+
+// The runner's value for forbidden tokens (their scaled logit is replaced).
+constexpr float kMasked = -1e10f;
 
 __device__ __forceinline__ unsigned long long pack_key_index(uint32_t key, uint32_t i)
 {
@@ -251,6 +261,40 @@ __device__ T block_scan_inclusive(T v, T *scratch)
 template <bool VEC4>
 struct Tile {
     float v[kMaxPer];
+    uint32_t ok = 0xffffffffu;  // bit j: element j is allowed by the mask
+
+    // s of element j: z / T, or kMasked where the mask forbids it
+    __device__ __forceinline__ float scaled(int j, float T) const
+    {
+        return ((ok >> j) & 1u) ? v[j] / T : kMasked;
+    }
+    // greedy value of element j: the raw logit, or kMasked
+    __device__ __forceinline__ float raw(int j) const { return ((ok >> j) & 1u) ? v[j] : kMasked; }
+
+    __device__ __forceinline__ void load_mask(const uint8_t *__restrict__ mrow, int i0, int i1,
+                                              int per)
+    {
+        if (!mrow) return;
+        uint32_t bits = 0;
+        if constexpr (VEC4) {
+#pragma unroll
+            for (int q = 0; q < kMaxPer / 4; ++q) {
+                const int i = index(i0, 4 * q);
+                uint32_t w = 0x01010101u;
+                if (4 * q < per && i < i1) w = *reinterpret_cast<const uint32_t *>(mrow + i);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) bits |= (((w >> (8 * k)) & 0xffu) ? 1u : 0u) << (4 * q + k);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j) {
+                const int i = index(i0, j);
+                const uint8_t m = (j < per && i < i1) ? mrow[i] : (uint8_t)1;
+                bits |= (m ? 1u : 0u) << j;
+            }
+        }
+        ok = bits;
+    }
 
     __device__ __forceinline__ static int index(int i0, int j)
     {
@@ -312,6 +356,7 @@ __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
     // issued before the row's settings are known, so that the two overlap
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
+    t.load_mask(a.mask ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
     const uint32_t mode = row_mode(a, b);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         SampCtl c = {};
@@ -332,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
     uint32_t kmax = 0;
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j)
-        if (j < per && Tile<VEC4>::index(i0, j) < i1) kmax = max(kmax, float_key(t.v[j] / T));
+        if (j < per && Tile<VEC4>::index(i0, j) < i1) kmax = max(kmax, float_key(t.scaled(j, T)));
     kmax = block_max<uint32_t, kThreads>(kmax, s_red);
     if (threadIdx.x == 0) a.part_max[(int64_t)b * a.nchunks + blockIdx.x] = kmax;
 }
@@ -358,6 +403,7 @@ __global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
     const int per = a.chunk / kThreads;
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
+    t.load_mask(a.mask ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
     const uint32_t mode = ctl->mode;
     if (!(mode & (MODE_TOPK | MODE_TOPP))) return;
     __shared__ uint32_t s_cnt[kBins];
@@ -375,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) {
         if (j >= per || Tile<VEC4>::index(i0, j) >= i1) continue;
-        const float s = t.v[j] / T;
+        const float s = t.scaled(j, T);
         const int bin = bin_of(s, M);
         if (bin == kBins - 1) {
             // >= 64 below the max: mass exp(-64) is below the fixed-point unit
@@ -487,12 +533,13 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
     const float *g = a.gumbel + (int64_t)b * a.gstride;
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
+    t.load_mask(a.mask ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
     unsigned long long best = 0;
     if (mode & MODE_GREEDY) {
 #pragma unroll
         for (int j = 0; j < kMaxPer; ++j) {
             const int i = Tile<VEC4>::index(i0, j);
-            if (j < per && i < i1) best = max(best, pack_key_index(float_key(t.v[j]), (uint32_t)i));
+            if (j < per && i < i1) best = max(best, pack_key_index(float_key(t.raw(j)), (uint32_t)i));
         }
     } else if (mode & MODE_PLAIN) {
         // every logit is eligible: stream the noise as a tile too
@@ -503,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
         for (int j = 0; j < kMaxPer; ++j) {
             const int i = Tile<VEC4>::index(i0, j);
             if (j < per && i < i1) {
-                const float kappa = t.v[j] / T + gt.v[j];
+                const float kappa = t.scaled(j, T) + gt.v[j];
                 best = max(best, pack_key_index(float_key(kappa), (uint32_t)i));
             }
         }
@@ -517,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
 #pragma unroll
         for (int j = 0; j < kMaxPer; ++j) {
             const int i = Tile<VEC4>::index(i0, j);
-            const float s = t.v[j] / T;
+            const float s = t.scaled(j, T);
             bool ok = false, c = false;
             if (j < per && i < i1) {
                 if (maxima) {
@@ -645,6 +692,7 @@ __device__ void bitonic_sort_desc(unsigned long long *key, uint32_t *pay, int n)
 // that take part (in the threshold bin, maybe kept by top-k).
 struct RowScan {
     const float *z;
+    const uint8_t *m;   // mask row or null
     float T, M;
     int V;
     int jstar;
@@ -652,7 +700,7 @@ struct RowScan {
 
 __device__ __forceinline__ bool in_bin(const RowScan &r, int i, float &s, uint32_t &key)
 {
-    s = r.z[i] / r.T;
+    s = (r.m && !r.m[i]) ? kMasked : r.z[i] / r.T;
     key = float_key(s);
     return bin_of(s, r.M) == r.jstar;
 }
@@ -888,10 +936,18 @@ __global__ __launch_bounds__(kRThreads) void samp_resolve_kernel(const SampArgs 
     if (mode & (MODE_GREEDY | MODE_PLAIN | MODE_TOPP_MAX)) {
         if (threadIdx.x == 0) {
             a.out_ids[b] = (int32_t)unpack_index(best);
-            if (a.flags) ctl->mode = mode | MODE_DONE;
+            if (a.flags) {
+                ctl->mode = mode | MODE_DONE;
+                ctl->tau = (mode & MODE_TOPP_MAX) ? c.max_key : 0u;
+                ctl->kpack = 0;
+            }
         }
         return;
     }
+    // the final cut, kept for the extra outputs: key >= cut_tau and, for
+    // top-k, (key, ~index) >= cut_k
+    uint32_t cut_tau = 0;
+    unsigned long long cut_k = 0;
     const bool topk = (mode & MODE_TOPK) != 0;
     const bool topp = (mode & MODE_TOPP) != 0;
     const uint32_t n = c.ncand;
@@ -948,6 +1004,9 @@ __global__ __launch_bounds__(kRThreads) void samp_resolve_kernel(const SampArgs 
         }
         if (part == 0 && kept && se >= tau) best = max(best, pack_key_index(sh.kap[e], unpack_index(ke)));
         best = block_max<unsigned long long, kRThreads>(best, sh.scan);
+        cut_tau = tau;
+        if (topk)  // the smallest packed key top-k keeps
+            cut_k = ~block_max<unsigned long long, kRThreads>((part == 0 && kept) ? ~ke : 0ull, sh.scan);
     } else if (n <= (uint32_t)kCap) {
         // ---- sort the candidates of the threshold bin ----
         int np = 1;
@@ -1009,10 +1068,13 @@ __global__ __launch_bounds__(kRThreads) void samp_resolve_kernel(const SampArgs 
                 best = max(best, pack_key_index(sh.kap[i], unpack_index(sh.key[i])));
         }
         best = block_max<unsigned long long, kRThreads>(best, sh.scan);
+        cut_tau = tau;
+        if (topk) cut_k = sh.key[r - 1];
     } else {
         // ---- the threshold bin overflowed the list: exact cut from the row ----
         RowScan rs;
         rs.z = a.logits + (int64_t)b * a.lstride;
+        rs.m = a.mask ? a.mask + (int64_t)b * a.mstride : nullptr;
         rs.T = a.temperature[b];
         rs.M = M;
         rs.V = a.vocab;
@@ -1038,11 +1100,173 @@ __global__ __launch_bounds__(kRThreads) void samp_resolve_kernel(const SampArgs 
         }
         const unsigned long long bb = best_in_bin(rs, g, sh, kkey, kcut, tau);
         best = max(best, bb);
+        cut_tau = tau;
+        if (topk) cut_k = pack_key_index(kkey, kcut);
     }
     if (threadIdx.x == 0) {
         a.out_ids[b] = (int32_t)unpack_index(best);
         ctl->mode = mode | MODE_DONE;
         ctl->round2 = 0;
+        ctl->tau = cut_tau;
+        ctl->kpack = cut_k;
+    }
+}
+
+// ---- extra outputs ---------------------------------------------------------
+
+// One workgroup per row, after the draw: the drawn id's probability under
+// the softmax of the kept scaled logits, and the 8 kept ids of largest s
+// (ties to the lower index) with their probabilities; fewer than 8 kept ids
+// are followed by the lowest-index ids outside the kept set (probability
+// 0).  Greedy rows: the distribution is uniform over the tied maxima of the
+// masked raw logits.  The row is read once (max, fp64 sum of exp(s - max)
+// with running rescale, per-thread top 8), plus an ordered index scan when
+// fewer than 8 ids are kept or for greedy ties.
+__global__ __launch_bounds__(kRThreads) void samp_extras_kernel(const SampArgs a)
+{
+    const int b = blockIdx.x;
+    const uint32_t mode = a.flags ? (a.ctl[b].mode & ~MODE_DONE) : row_mode(a, b);
+    const bool greedy = (mode & MODE_GREEDY) != 0;
+    const uint32_t tau = (a.flags && !greedy) ? a.ctl[b].tau : 0u;
+    const unsigned long long kpack = (a.flags && !greedy) ? a.ctl[b].kpack : 0ull;
+    const float T = a.temperature[b];
+    const float *z = a.logits + (int64_t)b * a.lstride;
+    const uint8_t *mk = a.mask ? a.mask + (int64_t)b * a.mstride : nullptr;
+    const int V = a.vocab;
+    const int id = a.out_ids[b];
+
+    __shared__ unsigned long long s_red[kRThreads / 64];
+    __shared__ double s_dred[kRThreads / 64];
+    __shared__ unsigned long long s_top[8];
+    __shared__ int s_idx[8];
+    __shared__ int s_found;
+    __shared__ uint32_t s_wave[kRThreads / 64];
+
+    auto value = [&](int i) -> float {
+        const bool ok = !mk || mk[i];
+        return greedy ? (ok ? z[i] : kMasked) : (ok ? z[i] / T : kMasked);
+    };
+    auto kept = [&](int i, float v) -> bool {
+        if (greedy) return true;
+        const uint32_t k = float_key(v);
+        return k >= tau && (kpack == 0 || pack_key_index(k, (uint32_t)i) >= kpack);
+    };
+
+    // one pass: running max and fp64 sum over the kept, per-thread top 8
+    float mt = -INFINITY;
+    double zt = 0.0;
+    unsigned long long top[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) top[r] = 0;
+    uint32_t nkept = 0;
+    for (int i = threadIdx.x; i < V; i += kRThreads) {
+        const float v = value(i);
+        if (!kept(i, v)) continue;
+        ++nkept;
+        if (v > mt) {
+            zt = (mt == -INFINITY) ? 1.0 : zt * (double)expf(mt - v) + 1.0;
+            mt = v;
+        } else {
+            zt += (double)expf(v - mt);
+        }
+        const unsigned long long key = pack_key_index(float_key(v), (uint32_t)i);
+        if (key > top[7]) {
+            top[7] = key;
+#pragma unroll
+            for (int r = 7; r > 0; --r)
+                if (top[r] > top[r - 1]) {
+                    const unsigned long long x = top[r];
+                    top[r] = top[r - 1];
+                    top[r - 1] = x;
+                }
+        }
+    }
+    const float M = key_float(block_max<uint32_t, kRThreads>(
+        mt == -INFINITY ? 0u : float_key(mt), reinterpret_cast<uint32_t *>(s_red)));
+    const double Z = block_sum<double, kRThreads>(
+        mt == -INFINITY ? 0.0 : zt * exp((double)mt - (double)M), s_dred);
+    const uint32_t total_kept = (uint32_t)block_sum<unsigned long long, kRThreads>(nkept, s_red);
+
+    // the top 8 over the block: 8 rounds of a block max, the owner pops
+    for (int r = 0; r < 8; ++r) {
+        const unsigned long long w = block_max<unsigned long long, kRThreads>(top[0], s_red);
+        if (threadIdx.x == 0) s_top[r] = w;
+        if (w != 0 && top[0] == w) {
+#pragma unroll
+            for (int k = 0; k < 7; ++k) top[k] = top[k + 1];
+            top[7] = 0;
+        }
+    }
+    __syncthreads();
+
+    // first `need` indices (in index order) that satisfy pred, into s_idx[from..]
+    auto first_indices = [&](int from, int need, auto pred) {
+        if (threadIdx.x == 0) s_found = 0;
+        __syncthreads();
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        for (int base = 0; base < V; base += kRThreads) {
+            const int i = base + (int)threadIdx.x;
+            const bool hit = i < V && pred(i);
+            const unsigned long long bal = __ballot(hit);
+            if (lane == 0) s_wave[wave] = (uint32_t)__popcll(bal);
+            __syncthreads();
+            int before = s_found;
+            for (int w = 0; w < wave; ++w) before += (int)s_wave[w];
+            const int rank = before + (int)__popcll(bal & ((1ull << lane) - 1ull));
+            if (hit && rank < need) s_idx[from + rank] = i;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                int tot = 0;
+                for (int w = 0; w < kRThreads / 64; ++w) tot += (int)s_wave[w];
+                s_found += tot;
+            }
+            __syncthreads();
+            if (s_found >= need) break;
+        }
+    };
+
+    if (greedy) {
+        // uniform over the tied maxima: their first 8 indices, then the others
+        const uint32_t ties = (uint32_t)block_sum<unsigned long long, kRThreads>(
+            [&] {
+                uint32_t c = 0;
+                for (int i = threadIdx.x; i < V; i += kRThreads) c += value(i) == M ? 1u : 0u;
+                return (unsigned long long)c;
+            }(),
+            s_red);
+        const int nt = (int)min(ties, 8u);
+        first_indices(0, nt, [&](int i) { return value(i) == M; });
+        if (nt < 8) first_indices(nt, min(8, V) - nt, [&](int i) { return value(i) != M; });
+        if (threadIdx.x < 8) {
+            const int r = threadIdx.x;
+            const bool real = r < min(8, V);
+            const int idx = real ? s_idx[r] : -1;
+            const float pr = (r < nt) ? (float)(1.0 / (double)ties) : 0.f;
+            if (a.out_top_ids) a.out_top_ids[(int64_t)b * 8 + r] = idx;
+            if (a.out_top_probs) a.out_top_probs[(int64_t)b * 8 + r] = real ? pr : 0.f;
+        }
+        if (threadIdx.x == 0 && a.out_prob) a.out_prob[b] = (float)(1.0 / (double)ties);
+        return;
+    }
+
+    const int nk = (int)min(total_kept, 8u);
+    if (nk < 8) first_indices(nk, min(8, V) - nk, [&](int i) { return !kept(i, value(i)); });
+    if (threadIdx.x < 8) {
+        const int r = threadIdx.x;
+        int idx = -1;
+        float pr = 0.f;
+        if (r < nk) {
+            idx = (int)unpack_index(s_top[r]);
+            pr = (float)(exp((double)key_float((uint32_t)(s_top[r] >> 32)) - (double)M) / Z);
+        } else if (r < min(8, V)) {
+            idx = s_idx[r];
+        }
+        if (a.out_top_ids) a.out_top_ids[(int64_t)b * 8 + r] = idx;
+        if (a.out_top_probs) a.out_top_probs[(int64_t)b * 8 + r] = pr;
+    }
+    if (threadIdx.x == 0 && a.out_prob) {
+        const float v = value(id);
+        a.out_prob[b] = (float)(exp((double)v - (double)M) / Z);
     }
 }
 
@@ -1061,6 +1285,8 @@ void launch_passes(const SampArgs &a, const dim3 grid, uint32_t flags, hipStream
         samp_collect_kernel<VEC4, true><<<grid, kThreads, 0, stream>>>(a);
         samp_resolve_kernel<true><<<a.batch, kRThreads, 0, stream>>>(a);
     }
+    if (a.out_prob || a.out_top_ids || a.out_top_probs)
+        samp_extras_kernel<<<a.batch, kRThreads, 0, stream>>>(a);
 }
 
 }  // namespace
@@ -1071,9 +1297,11 @@ size_t sampler_workspace_bytes(int32_t batch, int32_t vocab)
 }
 
 hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_stride,
-                          const float *gumbel, int64_t gumbel_stride, const float *temperature,
-                          const float *top_p, const int32_t *top_k, int32_t batch, int32_t vocab,
-                          uint32_t flags, void *workspace, hipStream_t stream)
+                          const float *gumbel, int64_t gumbel_stride, const uint8_t *mask,
+                          int64_t mask_stride, const float *temperature, const float *top_p,
+                          const int32_t *top_k, int32_t batch, int32_t vocab, uint32_t flags,
+                          float *out_prob, int32_t *out_top_ids, float *out_top_probs,
+                          void *workspace, hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
     const SampLayout L = sampler_layout(batch, vocab);
@@ -1099,10 +1327,16 @@ hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_
     a.kap = reinterpret_cast<uint32_t *>(ws + L.kap_off);
     a.part_max = reinterpret_cast<uint32_t *>(ws + L.pmax_off);
     a.part_best = reinterpret_cast<unsigned long long *>(ws + L.pbest_off);
+    a.mask = mask;
+    a.mstride = mask_stride;
+    a.out_prob = out_prob;
+    a.out_top_ids = out_top_ids;
+    a.out_top_probs = out_top_probs;
 
     const dim3 grid(L.nchunks, batch);
     const bool vec4 = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && logits_stride % 4 == 0 &&
                       (reinterpret_cast<uintptr_t>(gumbel) % 16 == 0) && gumbel_stride % 4 == 0 &&
+                      (!mask || (reinterpret_cast<uintptr_t>(mask) % 4 == 0 && mask_stride % 4 == 0)) &&
                       vocab % 4 == 0;
     if (vec4)
         launch_passes<true>(a, grid, flags, stream);

@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.PROTOTYPES)
@@ -196,3 +196,24 @@ def test_cascade_validation():
     assert call(D=96) == _lib.PKV_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.PKV_ERR_WORKSPACE
     assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
+
+
+def test_sampler_ex_validation():
+    L = _lib.lib()
+    need = L.pkv_sampler_workspace_bytes(4, 1000)
+
+    def call(**kw):
+        a = dict(ids=FAKE, z=FAKE, g=FAKE, m=None, ms=0, t=FAKE, p=FAKE, k=FAKE, B=4, V=1000,
+                 flags=3, prob=None, tid=None, tpr=None, ws=FAKE, wsb=need)
+        a.update(kw)
+        return L.pkv_sample_next_token_ex(a["ids"], a["z"], 0, a["g"], 0, a["m"], a["ms"], a["t"],
+                                          a["p"], a["k"], a["B"], a["V"], a["flags"], a["prob"],
+                                          a["tid"], a["tpr"], a["ws"], a["wsb"], None)
+
+    assert call(m=FAKE, ms=999) == _lib.PKV_ERR_INVALID_ARG     # mask stride below vocab
+    assert call(prob=FAKE + 2) == _lib.PKV_ERR_INVALID_ARG      # misaligned output
+    assert call(tid=FAKE + 1) == _lib.PKV_ERR_INVALID_ARG
+    assert call(flags=4) == _lib.PKV_ERR_INVALID_ARG
+    assert call(z=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
+    assert call(B=0, ids=None, z=None, g=None, t=None, p=None, k=None) == _lib.PKV_OK
