@@ -56,6 +56,11 @@ def lib():
         L.oracle_decode_attention_head.restype = ctypes.c_int
         L.oracle_decode_attention_head.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, I64,
                                                    ctypes.c_double]
+        L.oracle_varlen_attention.restype = ctypes.c_int
+        L.oracle_varlen_attention.argtypes = [P, P, P, P, P, I64, P, P, I64, I64, I64, I64, I64,
+                                              I64, ctypes.c_double]
+        L.oracle_varlen_slot_mapping.restype = None
+        L.oracle_varlen_slot_mapping.argtypes = [P, P, I64, P, P, I64, I64]
         L.oracle_decode_attention.restype = ctypes.c_int
         L.oracle_decode_attention.argtypes = [P, P, P, P, P, I64, P, I64, I64, I64, I64, I64, I64,
                                               ctypes.c_double]
@@ -110,6 +115,38 @@ def kv_store(k_cache, v_cache, k_new, v_new, slots, block_size) -> int:
     assert bs == block_size
     return int(lib().oracle_kv_store(_ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn), _ptr(sl),
                                      sl.shape[0], hkv, d, bs, nb))
+
+
+def varlen_attention(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
+                     scale=0.0) -> np.ndarray:
+    """q uint16 [total_q, Hq, D]; pools uint16 [NB, bs, Hkv, D]; cu_* int32
+    [B+1] -> fp64 [total_q, Hq, D] (causal over cached + new tokens)."""
+    q = _c(q, np.uint16)
+    kc = _c(k_cache, np.uint16)
+    vc = _c(v_cache, np.uint16)
+    bt = _c(block_tables, np.int32)
+    cq = _c(cu_seqlens_q, np.int32)
+    ck = _c(cu_seqlens_k, np.int32)
+    T, Hq, D = q.shape
+    nb, bs, hkv, d2 = kc.shape
+    assert d2 == D and cq[-1] == T
+    out = np.empty((T, Hq, D), np.float64)
+    rc = lib().oracle_varlen_attention(_ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt),
+                                       bt.shape[1], _ptr(cq), _ptr(ck), cq.shape[0] - 1, Hq, hkv,
+                                       D, bs, nb, float(scale))
+    if rc:
+        raise ValueError(f"oracle_varlen_attention failed ({rc})")
+    return out
+
+
+def varlen_slot_mapping(block_tables, cu_seqlens_q, cu_seqlens_k, block_size) -> np.ndarray:
+    bt = _c(block_tables, np.int32)
+    cq = _c(cu_seqlens_q, np.int32)
+    ck = _c(cu_seqlens_k, np.int32)
+    out = np.empty(int(cq[-1]), np.int32)
+    lib().oracle_varlen_slot_mapping(_ptr(out), _ptr(bt), bt.shape[1], _ptr(cq), _ptr(ck),
+                                     cq.shape[0] - 1, block_size)
+    return out
 
 
 def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale=0.0) -> np.ndarray:

@@ -205,6 +205,55 @@ int oracle_decode_attention(double *out, const uint16_t *q,
     return 0;
 }
 
+int oracle_varlen_attention(double *out, const uint16_t *q,
+                            const uint16_t *k_cache, const uint16_t *v_cache,
+                            const int32_t *block_tables, int64_t table_stride,
+                            const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int64_t batch,
+                            int64_t num_q_heads, int64_t num_kv_heads,
+                            int64_t head_dim, int64_t block_size,
+                            int64_t num_blocks, double scale)
+{
+    if (scale <= 0.0)
+        scale = 1.0 / sqrt((double)head_dim);
+    int64_t group = num_q_heads / num_kv_heads;
+    for (int64_t b = 0; b < batch; ++b) {
+        int64_t q_len = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+        int64_t k_len = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+        if (q_len < 0 || k_len < q_len)
+            return -1;
+        int64_t cached = k_len - q_len;
+        for (int64_t j = 0; j < q_len; ++j) {
+            int64_t row = cu_seqlens_q[b] + j;
+            for (int64_t h = 0; h < num_q_heads; ++h) {
+                /* causal: new token j sees every position up to its own */
+                int rc = oracle_decode_attention_head(
+                    out + (row * num_q_heads + h) * head_dim,
+                    q + (row * num_q_heads + h) * head_dim, k_cache, v_cache,
+                    block_tables + b * table_stride, cached + j + 1, num_kv_heads,
+                    h / group, head_dim, block_size, num_blocks, scale);
+                if (rc)
+                    return rc;
+            }
+        }
+    }
+    return 0;
+}
+
+void oracle_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
+                                int64_t table_stride, const int32_t *cu_seqlens_q,
+                                const int32_t *cu_seqlens_k, int64_t batch,
+                                int64_t block_size)
+{
+    for (int64_t b = 0; b < batch; ++b) {
+        int64_t q_len = cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+        int64_t k_len = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+        for (int64_t j = 0; j < q_len; ++j)
+            slot_mapping[cu_seqlens_q[b] + j] = (int32_t)oracle_slot_for_position(
+                block_tables + b * table_stride, table_stride, k_len - q_len + j, block_size);
+    }
+}
+
 int oracle_contiguous_attention(double *out, const uint16_t *q,
                                 const uint16_t *k, const uint16_t *v,
                                 const int32_t *context_lens, int64_t batch,

@@ -81,6 +81,33 @@ int oracle_contiguous_attention(double *out, const uint16_t *q,
                                 int64_t num_kv_heads, int64_t head_dim,
                                 double scale);
 
+/* Varlen multi-query paged attention (nano-vllm page, "prefix cache" and
+ * "prefill and decode": a chunk of new tokens per sequence attends, with a
+ * causal mask, to the sequence's cached tokens and to the new tokens up to
+ * itself).  Sequence i has q_len = cu_seqlens_q[i+1] - cu_seqlens_q[i] new
+ * tokens (rows cu_seqlens_q[i] .. of q and out) and k_len = cu_seqlens_k[i+1]
+ * - cu_seqlens_k[i] >= q_len tokens in the cache (its block table covers
+ * them; the new tokens' K/V are already stored).  New token j sits at
+ * position k_len - q_len + j and attends to positions [0, k_len - q_len + j].
+ * q uint16 (bf16 bits) [total_q][Hq][D]; out fp64 [total_q][Hq][D].
+ * Returns 0, or -1 for a block id out of range or a bad length. */
+int oracle_varlen_attention(double *out, const uint16_t *q,
+                            const uint16_t *k_cache, const uint16_t *v_cache,
+                            const int32_t *block_tables, int64_t table_stride,
+                            const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int64_t batch,
+                            int64_t num_q_heads, int64_t num_kv_heads,
+                            int64_t head_dim, int64_t block_size,
+                            int64_t num_blocks, double scale);
+
+/* Slots of the new tokens of a varlen batch: token j of sequence i is at
+ * position k_len - q_len + j of its block table (-1 where the table entry
+ * is negative or the position is past the table). */
+void oracle_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
+                                int64_t table_stride, const int32_t *cu_seqlens_q,
+                                const int32_t *cu_seqlens_k, int64_t batch,
+                                int64_t block_size);
+
 /* Per-row sampler diagnostics. */
 typedef struct {
     int32_t id;          /* sampled token id */

@@ -552,3 +552,88 @@ def test_masked_draws_follow_renormalised_softmax():
     exp_ = probs * N
     chi2 = float(np.sum((counts[top] - exp_) ** 2 / exp_))
     assert chi2 < 16.3, (chi2, counts[top], exp_)   # 99.9% quantile, 3 dof
+
+
+# ------------------------------------------ varlen multi-query attention --
+
+def _varlen_case(rng, lens_new, lens_cached, H, Hkv, D, bs):
+    """Whole sequences (cached + new tokens) in a fragmented paged cache;
+    returns the dense per-sequence tensors and the varlen arguments."""
+    B = len(lens_new)
+    total = [c + q for c, q in zip(lens_cached, lens_new)]
+    need = [(n + bs - 1) // bs for n in total]
+    nb = sum(need) + 2
+    perm = rng.permutation(nb).astype(np.int32)
+    W = max(need)
+    tables = np.full((B, W), -1, np.int32)
+    kc = _bf16(rng, (nb, bs, Hkv, D))
+    vc = _bf16(rng, (nb, bs, Hkv, D))
+    seqs = []
+    pos = 0
+    for b in range(B):
+        tables[b, :need[b]] = perm[pos:pos + need[b]]
+        pos += need[b]
+        n = total[b]
+        qs, ks, vs = _bf16(rng, (n, H, D)), _bf16(rng, (n, Hkv, D)), _bf16(rng, (n, Hkv, D))
+        for j in range(n):
+            s = oracle.slot_for_position(tables[b], j, bs)
+            kc.reshape(-1, Hkv, D)[s] = ks[j]
+            vc.reshape(-1, Hkv, D)[s] = vs[j]
+        seqs.append((qs, ks, vs))
+    cu_q = np.concatenate([[0], np.cumsum(lens_new)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(total)]).astype(np.int32)
+    q = np.concatenate([seqs[b][0][lens_cached[b]:] for b in range(B)], axis=0)
+    return seqs, q, kc, vc, tables, cu_q, cu_k
+
+
+def test_varlen_rows_equal_dense_causal_attention():
+    """Each new token of a chunk (cached prefix + new tokens, several
+    sequences of different lengths) reproduces its row of full causal
+    attention over the whole sequence, computed as one masked matrix."""
+    rng = np.random.default_rng(140)
+    H, Hkv, D, bs = 6, 2, 8, 4
+    lens_new = [5, 1, 9, 3]
+    lens_cached = [0, 6, 13, 2]
+    seqs, q, kc, vc, tables, cu_q, cu_k = _varlen_case(rng, lens_new, lens_cached, H, Hkv, D, bs)
+    got = oracle.varlen_attention(q, kc, vc, tables, cu_q, cu_k)
+    for b, (qs, ks, vs) in enumerate(seqs):
+        ref = _causal_last_rows(f32_from_bf16_bits(qs).astype(np.float64),
+                                f32_from_bf16_bits(ks).astype(np.float64),
+                                f32_from_bf16_bits(vs).astype(np.float64), 1.0 / math.sqrt(D))
+        np.testing.assert_allclose(got[cu_q[b]:cu_q[b + 1]], ref[lens_cached[b]:], rtol=0,
+                                   atol=1e-12)
+
+
+def test_varlen_chunked_prefill_equals_one_chunk():
+    """A prefill cut into chunks (each later chunk seeing the earlier ones
+    as its cached prefix) gives the same rows as one chunk."""
+    rng = np.random.default_rng(141)
+    H, Hkv, D, bs = 4, 4, 8, 8
+    n = 37
+    seqs, q, kc, vc, tables, cu_q, cu_k = _varlen_case(rng, [n], [0], H, Hkv, D, bs)
+    whole = oracle.varlen_attention(q, kc, vc, tables, cu_q, cu_k)
+    parts = []
+    start = 0
+    for step in (10, 1, 20, 6):
+        cq = np.array([0, step], np.int32)
+        ck = np.array([0, start + step], np.int32)
+        parts.append(oracle.varlen_attention(q[start:start + step], kc, vc, tables, cq, ck))
+        start += step
+    np.testing.assert_array_equal(np.concatenate(parts), whole)
+
+
+def test_varlen_slot_mapping_covers_the_new_positions():
+    rng = np.random.default_rng(142)
+    bs = 4
+    lens_new, lens_cached = [3, 1, 6], [5, 0, 8]
+    seqs, q, kc, vc, tables, cu_q, cu_k = _varlen_case(rng, lens_new, lens_cached, 2, 1, 8, bs)
+    slots = oracle.varlen_slot_mapping(tables, cu_q, cu_k, bs)
+    for b in range(3):
+        for j in range(lens_new[b]):
+            pos = lens_cached[b] + j
+            assert slots[cu_q[b] + j] == tables[b, pos // bs] * bs + pos % bs
+    # one new token per sequence: the decode slot mapping
+    cq = np.arange(4, dtype=np.int32)
+    ck = np.concatenate([[0], np.cumsum([8, 1, 14])]).astype(np.int32)
+    np.testing.assert_array_equal(oracle.varlen_slot_mapping(tables, cq, ck, bs),
+                                  oracle.slot_mapping(tables, np.array([8, 1, 14], np.int32), bs))
