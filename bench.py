@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0,
                     help="independent copies of the pools, cycled step by step so that at "
                          "least 1 GB of cache is touched between reuses (0 = automatic)")
+    ap.add_argument("--varlen", default="",
+                    help="time varlen multi-query (chunked prefill) attention on this "
+                         "workload instead of the decode step (qwen3_prefill)")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="host threads for the oracle baseline (0 = the CPUs this process "
                          "may use, at most 16)")
@@ -104,6 +107,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     pkv.lib()  # fail loudly if the HIP library is missing
+    if args.varlen:
+        run_varlen(args)
+        return
 
     cfg = config_by_name(args.config)
     L = args.layers or cfg.num_layers
@@ -353,6 +359,112 @@ def main():
                      if graph_part_us is not None else "hip_events per launch",
                      "traffic": traffic},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def run_varlen(args):
+    """Chunked prefill: per layer the new tokens' slot mapping, store, and
+    varlen multi-query paged attention; attention FLOP/s against the bf16
+    matrix-core peak (causal pairs x Hq x 4 D flops)."""
+    import torch
+
+    import paged_kv_decode_store_amd as pkv
+    from workloads.varlen import (varlen_attended_pairs, varlen_by_name, varlen_layer_inputs,
+                                  varlen_tables)
+
+    w = varlen_by_name(args.varlen)
+    L = args.layers or w.num_layers
+    Hq, Hkv, D, bs = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    tables, cu_q, cu_k, nb = varlen_tables(w)
+    T = int(cu_q[-1])
+    mq, mk = int(np.diff(cu_q).max()), int(np.diff(cu_k).max())
+    dev = torch.device("cuda")
+
+    def u16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    td = torch.from_numpy(tables).to(dev)
+    cq, ck = torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    kp = [torch.randn((nb, bs, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+          for _ in range(L)]
+    vp = [torch.randn((nb, bs, Hkv, D), generator=gen, device=dev, dtype=torch.bfloat16)
+          for _ in range(L)]
+    lay = [varlen_layer_inputs(w, l) for l in range(L)]
+    q = [u16(x[0]) for x in lay]
+    kn = [u16(x[1]) for x in lay]
+    vn = [u16(x[2]) for x in lay]
+    slots = torch.empty(T, dtype=torch.int32, device=dev)
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    log(f"[bench] varlen {w.name}: {len(w.lens_new)} sequences, {T} new tokens, L={L}")
+
+    def step():
+        pkv.varlen_slot_mapping(td, cq, ck, mq, bs, T, out=slots)
+        for l in range(L):
+            pkv.kv_store(kp[l], vp[l], kn[l], vn[l], slots)
+            pkv.varlen_paged_attention(q[l], kp[l], vp[l], td, cq, ck, mq, mk, out=out)
+
+    def attn_only():
+        for l in range(L):
+            pkv.varlen_paged_attention(q[l], kp[l], vp[l], td, cq, ck, mq, mk, out=out)
+
+    def graph_ms(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    step_ms = graph_ms(step)
+    attn_us = 1e3 * graph_ms(attn_only) / L
+    pairs = varlen_attended_pairs(w)
+    flops = pairs * Hq * 4 * D
+    tflops = flops / (attn_us * 1e-6) / 1e12
+    kv_bytes = int(cu_k[-1]) * Hkv * D * 4
+    io_bytes = kv_bytes + 2 * T * Hq * D * 2
+    res = {
+        "metric": "varlen paged attention TFLOP/s (chunked prefill)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {len(w.lens_new)} sequences, new tokens "
+                   f"{list(w.lens_new)} after cached {list(w.lens_cached)}, GQA {Hq}/{Hkv}, "
+                   f"head_dim {D}, block {bs}, {L} layers",
+                   "causal_pairs_per_head": pairs},
+        "attention_us_per_layer": round(attn_us, 3),
+        "attention_GBps": round(io_bytes / (attn_us * 1e-6) / 1e9, 1),
+        "roofline": {"kernel": f"decode_partial_mfma_kernel<{D}, false, varlen>", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "flops_per_launch": flops,
+                     "avg_launch_us": round(attn_us, 3), "traffic": None},
+        "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
 

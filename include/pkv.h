@@ -250,6 +250,51 @@ int pkv_cascade_decode_attention(void *out, int64_t out_stride, const void *q,
                                  void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* ---- varlen multi-query paged attention (chunked prefill) ----------------
+ * The step before the decode path (nano-vllm page, "prefix cache" and
+ * "prefill and decode": cu_seqlens_q / cu_seqlens_k over a paged cache,
+ * the prompt's new tokens computed together, causally).  Sequence b has
+ * q_len_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] new tokens, packed as rows
+ * cu_seqlens_q[b] .. of q and out, and k_len_b = cu_seqlens_k[b+1] -
+ * cu_seqlens_k[b] >= q_len_b tokens in the cache, the new ones last (their
+ * K/V stored beforehand: pkv_varlen_slot_mapping + pkv_kv_store).  New
+ * token j attends to positions [0, k_len_b - q_len_b + j] through the
+ * sequence's block table.
+ *
+ * pkv_varlen_slot_mapping: slot_mapping int32 [total new tokens], the slot
+ * of token j of sequence b at position k_len_b - q_len_b + j (-1 where the
+ * table entry is negative or the position is past the table).
+ * pkv_varlen_paged_attention:
+ * out, q         bf16 [total_q][num_q_heads][head_dim]; token rows
+ *                out_stride / q_stride elements apart (0 = packed)
+ * cu_seqlens_q, cu_seqlens_k  int32 [batch + 1], non-decreasing from 0
+ * max_seqlen_q   >= every q_len_b (tokens past it are not computed)
+ * max_seqlen_k   >= every k_len_b (positions past it or past the table
+ *                are not attended)
+ * head_dim 64 or 128; block_size a power of two in [16, 4096]; scale <= 0
+ * selects 1/sqrt(head_dim).  No workspace: each workgroup covers its
+ * tokens' whole causal range and writes the normalised output.  A sequence
+ * with q_len_b = 0 or k_len_b < q_len_b writes nothing. */
+int pkv_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
+                            int32_t block_table_stride,
+                            const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t batch,
+                            int32_t max_seqlen_q, int32_t block_size,
+                            hipStream_t stream);
+
+int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q,
+                               int64_t q_stride, const void *k_cache,
+                               const void *v_cache,
+                               const int32_t *block_tables,
+                               int32_t block_table_stride,
+                               const int32_t *cu_seqlens_q,
+                               const int32_t *cu_seqlens_k, int32_t batch,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_seqlen_q,
+                               int32_t max_seqlen_k, float scale,
+                               hipStream_t stream);
+
 /* ---- sampler --------------------------------------------------------------
  * Next token per row (Grok-1 runners chapter, section 8.3 and 8.3.1;
  * nanochat engine page, section 3; nano-vllm page, "run model"):

@@ -21,6 +21,7 @@ __all__ = [
     "decode_attention_reduce", "decode_workspace_bytes", "decode_split_tokens",
     "paged_decode_attention_store", "decode_attention_partial_store",
     "cascade_decode_attention", "cascade_workspace_bytes",
+    "varlen_slot_mapping", "varlen_paged_attention",
     "sample_next_token", "sample_next_token_ex", "sampler_workspace_bytes", "PkvError",
     "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
 ]
@@ -314,3 +315,47 @@ def sample_next_token_ex(logits: torch.Tensor, gumbel: torch.Tensor, temperature
     if not extras:
         return out
     return out, prob, top_ids, top_probs
+
+
+def varlen_slot_mapping(block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                        cu_seqlens_k: torch.Tensor, max_seqlen_q: int, block_size: int,
+                        total_q: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int32 [total_q] slots of the new tokens of a varlen batch."""
+    B = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty(total_q, dtype=torch.int32, device=block_tables.device)
+    _packed(block_tables, "block_tables")
+    check(lib().pkv_varlen_slot_mapping(
+        _dev(out, "slot_mapping", torch.int32), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), B, max_seqlen_q, block_size, _stream()),
+        "pkv_varlen_slot_mapping")
+    return out
+
+
+def varlen_paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                           cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                           scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 [total_q, Hq, D]: each new token of each sequence attends causally
+    to the sequence's cached tokens and to the new tokens up to itself."""
+    T, Hq, D = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if d2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("pools must be [NB, bs, Hkv, D] matching q")
+    if q.stride(2) != 1 or q.stride(1) != D:
+        raise ValueError("q rows must be packed [Hq, D]")
+    _packed(k_cache, "k_cache")
+    _packed(v_cache, "v_cache")
+    _packed(block_tables, "block_tables")
+    B = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    check(lib().pkv_varlen_paged_attention(
+        _dev(out, "out", torch.bfloat16), out.stride(0), _dev(q, "q", torch.bfloat16), q.stride(0),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), B, Hq, hkv, D, bs, nb, max_seqlen_q,
+        max_seqlen_k, scale, _stream()), "pkv_varlen_paged_attention")
+    return out

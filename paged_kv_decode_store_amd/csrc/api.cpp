@@ -395,6 +395,85 @@ int pkv_decode_attention_reduce(void *out, int64_t out_stride, const int32_t *co
     return hip_status(pkv::launch_decode_reduce(a, head_dim, stream), "decode reduce launch");
 }
 
+int pkv_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
+                            int32_t block_table_stride, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                            int32_t block_size, hipStream_t stream)
+{
+    REQUIRE(batch >= 0 && max_seqlen_q >= 0, PKV_ERR_INVALID_ARG,
+            "batch and max_seqlen_q must be >= 0");
+    if (batch == 0 || max_seqlen_q == 0) return PKV_OK;
+    REQUIRE(slot_mapping && block_tables && cu_seqlens_q && cu_seqlens_k, PKV_ERR_INVALID_ARG,
+            "null pointer");
+    REQUIRE(aligned(slot_mapping, 4) && aligned(block_tables, 4) && aligned(cu_seqlens_q, 4) &&
+                aligned(cu_seqlens_k, 4),
+            PKV_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+    REQUIRE(block_table_stride > 0, PKV_ERR_INVALID_ARG, "block_table_stride must be > 0");
+    REQUIRE(pow2(block_size) && block_size <= (1 << 20), PKV_ERR_UNSUPPORTED,
+            "block_size %d must be a power of two", block_size);
+    return hip_status(pkv::launch_varlen_slot_mapping(slot_mapping, block_tables,
+                                                      block_table_stride, cu_seqlens_q,
+                                                      cu_seqlens_k, batch, max_seqlen_q,
+                                                      block_size, stream),
+                      "varlen slot mapping launch");
+}
+
+int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q, int64_t q_stride,
+                               const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, int32_t block_table_stride,
+                               const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
+                               hipStream_t stream)
+{
+    int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   block_table_stride, max_seqlen_k);
+    if (rc) return rc;
+    REQUIRE(max_seqlen_q >= 0, PKV_ERR_INVALID_ARG, "max_seqlen_q must be >= 0");
+    REQUIRE(num_blocks > 0, PKV_ERR_INVALID_ARG, "num_blocks must be > 0");
+    REQUIRE((int64_t)max_seqlen_q * (num_q_heads / num_kv_heads) <= (1 << 30),
+            PKV_ERR_UNSUPPORTED, "max_seqlen_q * group too large");
+    const int64_t row = (int64_t)num_q_heads * head_dim;
+    const int64_t qs = q_stride ? q_stride : row;
+    const int64_t os = out_stride ? out_stride : row;
+    REQUIRE(qs >= row && qs % 8 == 0 && os >= row && os % 8 == 0, PKV_ERR_INVALID_ARG,
+            "q_stride / out_stride must be >= num_q_heads*head_dim and multiples of 8");
+    REQUIRE(isfinite(scale), PKV_ERR_INVALID_ARG, "scale must be finite");
+    if (batch == 0 || max_seqlen_q == 0) return PKV_OK;
+    REQUIRE(out && q && k_cache && v_cache && block_tables && cu_seqlens_q && cu_seqlens_k,
+            PKV_ERR_INVALID_ARG, "null pointer");
+    REQUIRE(aligned(out, 16) && aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16),
+            PKV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+    REQUIRE(aligned(block_tables, 4) && aligned(cu_seqlens_q, 4) && aligned(cu_seqlens_k, 4),
+            PKV_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+    pkv::PartialArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q);
+    a.q_stride = qs;
+    a.k_cache = static_cast<const uint16_t *>(k_cache);
+    a.v_cache = static_cast<const uint16_t *>(v_cache);
+    a.block_tables = block_tables;
+    a.table_stride = block_table_stride;
+    a.batch = batch;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.head_chunks = 1;
+    a.bs_log2 = __builtin_ctz((unsigned)block_size);
+    a.num_blocks = num_blocks;
+    a.max_len = clamp_len(max_seqlen_k, block_table_stride, block_size);
+    a.split_tokens = a.max_len;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
+    a.c = sc * 1.4426950408889634f;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.out = static_cast<uint16_t *>(out);
+    a.out_stride = os;
+    return hip_status(pkv::launch_varlen_attention(a, head_dim, max_seqlen_q, stream),
+                      "varlen attention launch");
+}
+
 size_t pkv_cascade_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t max_context_len,
                                    int32_t num_prefix_blocks, int32_t block_size,

@@ -72,6 +72,15 @@ struct PartialArgs {
     int32_t prefix_len;
     int32_t vq_per_kv;
     int32_t vchunks;        // virtual-query chunks per KV head
+    // varlen multi-query attention: sequence b's new tokens are rows
+    // [cu_q[b], cu_q[b+1]) of q and out, its cache holds cu_k[b+1] - cu_k[b]
+    // tokens (the new ones last); one workgroup per (chunk of 16 (token,
+    // query head) pairs, KV head, sequence), bf16 output written directly
+    const int32_t *cu_q;
+    const int32_t *cu_k;
+    uint16_t *out;
+    int64_t out_stride;
+    int32_t qchunks;        // chunks per sequence (from the longest one)
 };
 
 struct ReduceArgs {
@@ -96,6 +105,14 @@ hipError_t launch_decode_reduce(const ReduceArgs &a, int32_t head_dim, hipStream
 // (`a` describes the prefix launch; 16 virtual queries per workgroup).
 hipError_t launch_decode_partial_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_decode_prefix_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
+// Varlen multi-query paged attention on the matrix-core kernel.
+hipError_t launch_varlen_attention(const PartialArgs &a, int32_t head_dim, int32_t max_seqlen_q,
+                                   hipStream_t stream);
+hipError_t launch_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
+                                      int32_t table_stride, const int32_t *cu_seqlens_q,
+                                      const int32_t *cu_seqlens_k, int32_t batch,
+                                      int32_t max_seqlen_q, int32_t block_size,
+                                      hipStream_t stream);
 // Group sizes from which the partial step runs on the matrix cores (the VALU
 // kernel is ALU-bound beyond group 2 on MI355X).
 constexpr int32_t kMfmaMinGroup = 3;

@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.PROTOTYPES)
@@ -217,3 +217,30 @@ def test_sampler_ex_validation():
     assert call(z=None) == _lib.PKV_ERR_INVALID_ARG
     assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
     assert call(B=0, ids=None, z=None, g=None, t=None, p=None, k=None) == _lib.PKV_OK
+
+
+def test_varlen_validation():
+    L = _lib.lib()
+
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cq=FAKE, ck=FAKE, B=4, Hq=16, Hkv=8,
+                 D=128, bs=256, mq=512, mk=4096, qs=0, scale=0.0)
+        a.update(kw)
+        return L.pkv_varlen_paged_attention(a["out"], 0, a["q"], a["qs"], a["k"], a["v"], a["bt"],
+                                            16, a["cq"], a["ck"], a["B"], a["Hq"], a["Hkv"],
+                                            a["D"], a["bs"], 600, a["mq"], a["mk"], a["scale"],
+                                            None)
+
+    assert call(cq=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(out=FAKE + 8) == _lib.PKV_ERR_INVALID_ARG
+    assert call(D=96) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(Hq=12) == _lib.PKV_ERR_INVALID_ARG
+    assert call(qs=16 * 128 - 8) == _lib.PKV_ERR_INVALID_ARG
+    assert call(mq=-1) == _lib.PKV_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == _lib.PKV_ERR_INVALID_ARG
+    assert call(mq=0, out=None, q=None) == _lib.PKV_OK
+    assert L.pkv_varlen_slot_mapping(None, FAKE, 4, FAKE, FAKE, 3, 10, 16, None) == \
+        _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_varlen_slot_mapping(FAKE, FAKE, 4, FAKE, FAKE, 3, 10, 24, None) == \
+        _lib.PKV_ERR_UNSUPPORTED
+    assert L.pkv_varlen_slot_mapping(None, None, 4, None, None, 0, 10, 16, None) == _lib.PKV_OK
