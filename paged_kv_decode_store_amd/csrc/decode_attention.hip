@@ -256,6 +256,25 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
     if (gw >= a.batch * a.num_q_heads) return;
     const int b = gw / a.num_q_heads;
     const int h = gw - b * a.num_q_heads;
+    // The first kSpec slots' partials and every lane's (m, l) are requested
+    // together with the row length, before it is known how many are in use
+    // (slots past the row's count hold stale data inside the workspace and
+    // are masked below): one memory round trip instead of three.
+    constexpr int kSpec = 8;
+    const int S = a.num_splits;
+    const int64_t base = ((int64_t)b * a.num_q_heads + h) * S;
+    const float *ml = a.part_ml + 2 * base;
+    const float *po = a.part_o + base * D + lane * DPL;
+    float mv = -INFINITY, lv = 0.f;
+    if (lane < S) {
+        mv = ml[2 * lane];
+        lv = ml[2 * lane + 1];
+    }
+    float v[kSpec][DPL];
+#pragma unroll
+    for (int k = 0; k < kSpec; ++k)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) v[k][j] = k < S ? po[(int64_t)k * D + j] : 0.f;
     const int n = min(max(a.context_lens[b], 0), a.max_len);
     const int tail = max(n - a.prefix_len, 0);
     const int ns = n == 0 ? 0 : a.prefix_splits + (tail + a.split_tokens - 1) / a.split_tokens;
@@ -266,32 +285,38 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
         for (int j = 0; j < DPL; ++j) orow[j] = 0;
         return;
     }
-    const int64_t base = ((int64_t)b * a.num_q_heads + h) * a.num_splits;
-    const float *ml = a.part_ml + 2 * base;
-    float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
+    float M = lane < ns ? mv : -INFINITY;
+    for (int s2 = lane + 64; s2 < ns; s2 += 64) M = fmaxf(M, ml[2 * s2]);
     M = wave_max(M);
-    float L = 0.f;
-    for (int s = lane; s < ns; s += 64) L += ml[2 * s + 1] * __builtin_amdgcn_exp2f(ml[2 * s] - M);
+    float L = lane < ns ? lv * __builtin_amdgcn_exp2f(mv - M) : 0.f;
+    for (int s2 = lane + 64; s2 < ns; s2 += 64) L += ml[2 * s2 + 1] * __builtin_amdgcn_exp2f(ml[2 * s2] - M);
     L = wave_sum(L);
     float acc[DPL];
 #pragma unroll
     for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
-    const float *po = a.part_o + base * D + lane * DPL;
-    // four splits per step so that their loads are in flight together
-    int s = 0;
+#pragma unroll
+    for (int k = 0; k < kSpec; ++k) {
+        const float mk = __shfl(mv, k);   // split k's max, held by lane k
+        if (k < ns) {
+            const float w = __builtin_amdgcn_exp2f(mk - M);
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) acc[j] += w * v[k][j];
+        }
+    }
+    // the remaining splits, four per step so that their loads are in flight together
+    int s = kSpec;
     for (; s + 4 <= ns; s += 4) {
-        float w[4], v[4][DPL];
+        float w[4], u[4][DPL];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             w[k] = __builtin_amdgcn_exp2f(ml[2 * (s + k)] - M);
 #pragma unroll
-            for (int j = 0; j < DPL; ++j) v[k][j] = po[(int64_t)(s + k) * D + j];
+            for (int j = 0; j < DPL; ++j) u[k][j] = po[(int64_t)(s + k) * D + j];
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int j = 0; j < DPL; ++j) acc[j] += w[k] * v[k][j];
+            for (int j = 0; j < DPL; ++j) acc[j] += w[k] * u[k][j];
     }
     for (; s < ns; ++s) {
         const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
