@@ -44,13 +44,20 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     const int gi = lane / LPT;
     const int li = lane % LPT;
 
+    // Consecutive workgroups go to different XCDs, so without a rotation
+    // XCD j would stream only KV head j.  Heads sit at fixed offsets inside
+    // each token row, and on MI355X some offsets stream measurably slower
+    // (~25% for two of eight 256-byte offsets), which left the XCDs holding
+    // those heads finishing last; rotating the head by the split index gives
+    // every XCD every head.
     int x = blockIdx.x;
     const int hc = x % a.head_chunks;
     x /= a.head_chunks;
-    const int kvh = x % a.num_kv_heads;
+    const int kv_slot = x % a.num_kv_heads;
     x /= a.num_kv_heads;
     const int b = x % a.batch;
     const int s = x / a.batch;
+    const int kvh = (kv_slot + s) % a.num_kv_heads;
 
     const int n_row = a.context_lens[b];
     const int n = min(max(n_row, 0), a.max_len);

@@ -120,6 +120,9 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
         x /= a.num_kv_heads;
         b = x % a.batch;
         s = x / a.batch;
+        // the KV head rotates with the split: every XCD streams every head
+        // (see the VALU partial kernel)
+        kvh = (kvh + s) % a.num_kv_heads;
     }
 
     int n, t_begin, t_end, pos_new = -1;
