@@ -346,12 +346,17 @@ int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_conte
     // Measured on MI355X: the VALU partial kernel runs best with roughly
     // 1-2k non-empty workgroups.  Rows are assumed half full on average, so
     // the split aims at B * Hkv * max_len / 2 positions spread over ~2048
-    // workgroups.  The matrix-core kernel (group >= kMfmaMinGroup) streams
-    // best with long splits, >= 2048 positions per workgroup (Grok-shaped:
-    // 5.6 TB/s at 2048 vs 4.5 at 512; long contexts: flat from 2k to 3k).
+    // workgroups (Qwen3-shaped: flat from 256 to 512 positions).  The
+    // matrix-core kernel (group >= kMfmaMinGroup) holds only two or three
+    // workgroups per CU and streams best with long splits: 3/8192 of
+    // B * Hkv * max_len positions each, at least 1024 (Grok-shaped, one
+    // 2048-position row per KV head: 46 us at 1024 vs 50 at 2048 and 54 at
+    // 512; long contexts: 576 us at 3072 vs 590 at 2048 and 626 at 1024).
     if (max_context_len <= 0 || batch <= 0 || num_kv_heads <= 0) return kRound;
-    int64_t split = (int64_t)batch * num_kv_heads * max_context_len / 4096;
-    const int64_t lo = group >= kMfmaMinGroup ? 2048 : 128;
+    const bool mfma = group >= kMfmaMinGroup;
+    const int64_t work = (int64_t)batch * num_kv_heads * max_context_len;
+    int64_t split = mfma ? work * 3 / 8192 : work / 4096;
+    const int64_t lo = mfma ? 1024 : 128;
     if (split < lo) split = lo;
     if (split > 8192) split = 8192;
     split = ((split + kRound - 1) / kRound) * kRound;
