@@ -460,7 +460,7 @@ def run_varlen(args):
                    "causal_pairs_per_head": pairs},
         "attention_us_per_layer": round(attn_us, 3),
         "attention_GBps": round(io_bytes / (attn_us * 1e-6) / 1e9, 1),
-        "roofline": {"kernel": f"decode_partial_mfma_kernel<{D}, false, varlen>", "bound": "mfma",
+        "roofline": {"kernel": f"varlen_attention_kernel<{D}>", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "flops_per_launch": flops,
                      "avg_launch_us": round(attn_us, 3), "traffic": None},

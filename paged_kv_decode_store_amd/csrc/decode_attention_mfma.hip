@@ -76,9 +76,9 @@ __device__ __forceinline__ uint32_t pair_of(uint32_t x, uint32_t y)
     return __builtin_amdgcn_perm(y, x, H ? 0x07060302u : 0x05040100u);
 }
 
-// Launch modes of the kernel: the decode partial step, the cascade's prefix
-// step, and varlen multi-query attention.
-enum : int { kDecode = 0, kPrefix = 1, kVarlen = 2 };
+// Launch modes of the kernel: the decode partial step and the cascade's
+// prefix step.
+enum : int { kDecode = 0, kPrefix = 1 };
 
 template <int D, bool FUSED, int MODE>
 __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const PartialArgs a)
@@ -86,7 +86,6 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(!FUSED || MODE == kDecode, "only the decode step stores");
     constexpr bool PREFIX = MODE == kPrefix;
-    constexpr bool VARLEN = MODE == kVarlen;
     constexpr int KD = D / 4;       // K dims per lane (one position)
     constexpr int KW = KD / 2;      // their packed words
     constexpr int KP = KD / 8;      // their 16-byte pieces: piece w is dims 8*(4*w + kb) + [0, 8)
@@ -107,12 +106,6 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
         kvh = x % a.num_kv_heads;
         s = x / a.num_kv_heads;
         b = 0;
-    } else if constexpr (VARLEN) {
-        hc = x % a.qchunks;
-        x /= a.qchunks;
-        kvh = x % a.num_kv_heads;
-        b = x / a.num_kv_heads;
-        s = 0;
     } else {
         hc = x % a.head_chunks;
         x /= a.head_chunks;
@@ -126,24 +119,10 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
     }
 
     int n, t_begin, t_end, pos_new = -1;
-    int q_len = 0, cached = 0;   // varlen: new tokens and cached tokens of sequence b
     if constexpr (PREFIX) {
         t_begin = s * a.split_tokens;
         t_end = min(a.prefix_len, t_begin + a.split_tokens);
         n = t_end;
-    } else if constexpr (VARLEN) {
-        q_len = a.cu_q[b + 1] - a.cu_q[b];
-        const int k_len = a.cu_k[b + 1] - a.cu_k[b];
-        if (q_len <= 0 || k_len < q_len) return;
-        cached = k_len - q_len;
-        const int j_first = (hc * kMQ) / a.group;
-        if (j_first >= q_len) return;
-        const int j_last = min(q_len - 1, (hc * kMQ + kMQ - 1) / a.group);
-        // causal: the chunk's last token sees positions up to its own
-        t_begin = 0;
-        t_end = min(cached + j_last + 1, a.max_len);
-        n = t_end;
-        if (t_end <= 0) return;
     } else {
         const int n_row = a.context_lens[b];
         n = min(max(n_row, 0), a.max_len);
@@ -156,18 +135,12 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
 
     // this lane's query: column ln of the workgroup's 16
     const int qv = hc * kMQ + ln;
-    const bool qreal = PREFIX ? qv < a.vq_per_kv : (VARLEN ? qv / a.group < q_len : qv < a.group);
+    const bool qreal = PREFIX ? qv < a.vq_per_kv : qv < a.group;
     int qrow, qhead, lim;
     if constexpr (PREFIX) {
         qrow = qreal ? qv / a.group : 0;
         qhead = kvh * a.group + (qreal ? qv % a.group : 0);
         lim = qreal ? min(t_end, min(max(a.context_lens[qrow], 0), a.max_len)) : 0;
-    } else if constexpr (VARLEN) {
-        // (token, query head) pairs, token-major, so a chunk's tokens are adjacent
-        const int j = qv / a.group;
-        qrow = qreal ? a.cu_q[b] + j : 0;
-        qhead = kvh * a.group + qv % a.group;
-        lim = qreal ? min(t_end, cached + j + 1) : 0;
     } else {
         qrow = b;
         qhead = kvh * a.group + (qreal ? qv : 0);
@@ -325,9 +298,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
         s_l[wave][ln] = lsum;
     }
     __syncthreads();
-    const int nq = PREFIX ? min(kMQ, a.vq_per_kv - hc * kMQ)
-                          : VARLEN ? min(kMQ, q_len * a.group - hc * kMQ)
-                                   : min(kMQ, a.group - hc * kMQ);
+    const int nq = PREFIX ? min(kMQ, a.vq_per_kv - hc * kMQ) : min(kMQ, a.group - hc * kMQ);
     for (int idx = threadIdx.x; idx < nq * D; idx += kMWaves * 64) {
         const int h = idx / D;
         const int d = idx - h * D;
@@ -343,13 +314,6 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
             O += s_o[w][h][d] * e;
         }
         const int v = hc * kMQ + h;
-        if constexpr (VARLEN) {
-            // one pass over the whole causal range: the normalised output
-            const int64_t row = a.cu_q[b] + v / a.group;
-            const int head = kvh * a.group + v % a.group;
-            a.out[row * a.out_stride + (int64_t)head * D + d] = (uint16_t)bf16_round(O / L);
-            continue;
-        }
         int64_t pidx;
         if constexpr (PREFIX) {
             const int rb = v / a.group, rh = kvh * a.group + v % a.group;
@@ -374,9 +338,6 @@ hipError_t launch_mfma_d(const PartialArgs &a, hipStream_t stream)
         const int64_t grid = (int64_t)((a.prefix_len + a.split_tokens - 1) / a.split_tokens) *
                              a.num_kv_heads * m.vchunks;
         decode_partial_mfma_kernel<D, false, kPrefix><<<(unsigned)grid, kMWaves * 64, 0, stream>>>(m);
-    } else if constexpr (MODE == kVarlen) {
-        const int64_t grid = (int64_t)a.qchunks * a.num_kv_heads * a.batch;
-        decode_partial_mfma_kernel<D, false, kVarlen><<<(unsigned)grid, kMWaves * 64, 0, stream>>>(m);
     } else {
         m.head_chunks = (a.group + kMQ - 1) / kMQ;
         const int64_t grid = (int64_t)(a.num_splits - a.split_base) * a.batch * a.num_kv_heads *
@@ -427,17 +388,6 @@ hipError_t launch_decode_prefix_mfma(const PartialArgs &a, int32_t head_dim, hip
     if (a.batch == 0 || a.prefix_len <= 0) return hipSuccess;
     if (head_dim == 128) return launch_mfma_d<128, kPrefix>(a, stream);
     if (head_dim == 64) return launch_mfma_d<64, kPrefix>(a, stream);
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_varlen_attention(const PartialArgs &a, int32_t head_dim, int32_t max_seqlen_q,
-                                   hipStream_t stream)
-{
-    if (a.batch == 0 || max_seqlen_q <= 0) return hipSuccess;
-    PartialArgs m = a;
-    m.qchunks = (int32_t)(((int64_t)max_seqlen_q * a.group + kMQ - 1) / kMQ);
-    if (head_dim == 128) return launch_mfma_d<128, kVarlen>(m, stream);
-    if (head_dim == 64) return launch_mfma_d<64, kVarlen>(m, stream);
     return hipErrorInvalidValue;
 }
 
