@@ -66,6 +66,22 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi)
     return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
 }
 
+// max / sum of x over lanes l and l ^ 32.  v_permlane32_swap(x, x) yields
+// (x[l], x[l^32]) for l < 32 and (x[l^32], x[l]) above, so one register
+// exchange replaces an LDS permute; both lanes get the identical result.
+__device__ __forceinline__ float xor32_max(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Low (H = 0) or high (H = 1) bf16 of x and of y as one packed pair.
 template <int H>
 __device__ __forceinline__ uint32_t pair16(uint32_t x, uint32_t y)
@@ -294,27 +310,43 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
         }
         const unsigned char *st_base = slot(it & 1);
 
+        if (t0 < t_end) {
+            // scores of the whole tile, the blocks' MFMA chains interleaved;
+            // sts[kb] item 4q + r = query c at position t0 + 32kb + 8q + 4h + r
+            f16_t sts[NKB];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            if (t0 + 32 * kb >= t_end) break;
-            // scores: item 4q + r = query c at position t0 + 32kb + 8q + 4h + r
-            f16_t st = f16_t{};
+            for (int kb = 0; kb < NKB; ++kb) sts[kb] = f16_t{};
 #pragma unroll
             for (int w = 0; w < QS; ++w)
-                st = mfma32(as_bf8(*reinterpret_cast<const u4_t *>(
-                                st_base + k_lds + (32 * kb * T::K_RS + 16 * w) * 2)),
-                            as_bf8(qop[w]), st);
-            if (t0 + 32 * kb + 32 > wave_lim) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int pos = t0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-                    if (pos >= lim) st[i] = -INFINITY;
-                }
+                for (int kb = 0; kb < NKB; ++kb)
+                    sts[kb] = mfma32(as_bf8(*reinterpret_cast<const u4_t *>(
+                                         st_base + k_lds + (32 * kb * T::K_RS + 16 * w) * 2)),
+                                     as_bf8(qop[w]), sts[kb]);
+            // causal mask (also covers every position past t_end)
+            if (t0 + KT > wave_lim) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int pos = t0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+                        if (pos >= lim) sts[kb][i] = -INFINITY;
+                    }
             }
-            float mx = st[0];
+            // one max per tile (tree reductions keep the chains short)
+            float m8[8];
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st[i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            for (int i = 0; i < 8; ++i) {
+                m8[i] = fmaxf(sts[0][2 * i], sts[0][2 * i + 1]);
+#pragma unroll
+                for (int kb = 1; kb < NKB; ++kb)
+                    m8[i] = fmaxf(m8[i], fmaxf(sts[kb][2 * i], sts[kb][2 * i + 1]));
+            }
+#pragma unroll
+            for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+                for (int i = 0; i < w; ++i) m8[i] = fmaxf(m8[i], m8[i + w]);
+            const float mx = xor32_max(m8[0]);
             if (__any(mx > mr + thr)) {
                 const float mn = fmaxf(mr, mx);
                 const float ref = (mn == -INFINITY) ? 0.f : mn;
@@ -325,28 +357,38 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
                 mr = mn;
             }
             const float mc = (mr == -INFINITY) ? 0.f : mr * cs;
-            float p[16];
+
+            // Branch-free from here, so block kb's P.V MFMAs and block kb+1's
+            // exponentials share one scheduling region.  O^T += V^T P^T per
+            // 16-position step u; slots (h, e) are position 16u + 8(e/4) +
+            // 4h + e%4, i.e. word pairs 8u + 2h + {0,1} and 8u + 4 + 2h + {0,1}.
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(fmaf(st[i], cs, -mc));
-                lsum += p[i];
-            }
-            // O^T += V^T P^T over the block's two 16-position steps; slots
-            // (h, e) are position 16u + 8(e/4) + 4h + e%4, i.e. word pairs
-            // 8u + 2h + {0,1} and 8u + 4 + 2h + {0,1}
+            for (int kb = 0; kb < NKB; ++kb) {
+                float p[16];
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int u = 2 * kb + half;
-                u4_t pw;
+                for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sts[kb][i], cs, -mc));
+                float s8[8];
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    pw[m] = pack2_bf16(p[8 * half + 2 * m], p[8 * half + 2 * m + 1]);
-                const bf8_t pb = as_bf8(pw);
+                for (int i = 0; i < 8; ++i) s8[i] = p[2 * i] + p[2 * i + 1];
 #pragma unroll
-                for (int j = 0; j < NOB; ++j) {
-                    const u2_t lo = *reinterpret_cast<const u2_t *>(st_base + v_lds(j, u, 0));
-                    const u2_t hi = *reinterpret_cast<const u2_t *>(st_base + v_lds(j, u, 1));
-                    o[j] = mfma32(as_bf8(u4_t{lo.x, lo.y, hi.x, hi.y}), pb, o[j]);
+                for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+                    for (int i = 0; i < w; ++i) s8[i] += s8[i + w];
+                lsum += s8[0];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int u = 2 * kb + half;
+                    u4_t pw;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        pw[m] = pack2_bf16(p[8 * half + 2 * m], p[8 * half + 2 * m + 1]);
+                    const bf8_t pb = as_bf8(pw);
+#pragma unroll
+                    for (int j = 0; j < NOB; ++j) {
+                        const u2_t lo = *reinterpret_cast<const u2_t *>(st_base + v_lds(j, u, 0));
+                        const u2_t hi = *reinterpret_cast<const u2_t *>(st_base + v_lds(j, u, 1));
+                        o[j] = mfma32(as_bf8(u4_t{lo.x, lo.y, hi.x, hi.y}), pb, o[j]);
+                    }
                 }
             }
         }
@@ -382,7 +424,7 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     }
 
     // normalise and write: O^T block j item 4q + r = dim 32j + 8q + 4h + r
-    lsum += __shfl_xor(lsum, 32);
+    lsum = xor32_sum(lsum);
     if (!real) return;
     const float inv = 1.0f / lsum;
     uint16_t *orow = a.out + (int64_t)(q0 + jq) * a.out_stride + (int64_t)head * D + 4 * h;
