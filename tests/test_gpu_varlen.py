@@ -72,8 +72,13 @@ def _reference(q, kp, vp, kn, vn, tables, cu_q, cu_k, bs, rows=None):
     return s_ref, kref, vref, None
 
 
+# Block sizes below the 64-position tile (128 at head_dim 64) take the
+# per-position block-id path, the others one block id per tile; 64 at head_dim
+# 128 and 128 at head_dim 64 are the boundary cases.
 @pytest.mark.parametrize("D,Hq,Hkv,bs", [(128, 4, 2, 16), (64, 6, 2, 32), (128, 8, 8, 256),
-                                         (128, 16, 1, 16), (64, 12, 4, 64), (128, 9, 3, 16)])
+                                         (128, 16, 1, 16), (64, 12, 4, 64), (128, 9, 3, 16),
+                                         (128, 6, 2, 64), (64, 8, 2, 128), (64, 4, 4, 256),
+                                         (128, 48, 8, 256)])
 def test_varlen_matches_oracle(D, Hq, Hkv, bs):
     rng = np.random.default_rng(D + 7 * Hq + 3 * Hkv + bs)
     lens_cached = [0, 5, 40, 0, 300, 17, 64]
@@ -82,6 +87,24 @@ def test_varlen_matches_oracle(D, Hq, Hkv, bs):
     say(f"varlen D={D} Hq={Hq} Hkv={Hkv} bs={bs} cached={lens_cached} new={lens_new}")
     slots, kc, vc, got = _prefill(*args, bs)
     s_ref, kref, vref, ref = _reference(*args, bs)
+    assert np.array_equal(slots, s_ref)
+    assert np.array_equal(kc, kref) and np.array_equal(vc, vref)
+    err = np.abs(got - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+def test_varlen_empty_sequence_and_long_prefix():
+    """A sequence with no new tokens between others (its rows do not exist,
+    the rest are unaffected), a prefix spanning many tiles with a chunk that
+    ends inside a tile, and a chunk longer than one 128-row tile."""
+    rng = np.random.default_rng(77)
+    lens_cached = [10, 20, 0, 1500, 129]
+    lens_new = [3, 0, 70, 37, 200]
+    args = _case(rng, lens_cached, lens_new, 8, 4, 128, 256)
+    say(f"varlen empty/long cached={lens_cached} new={lens_new}")
+    slots, kc, vc, got = _prefill(*args, 256)
+    s_ref, kref, vref, ref = _reference(*args, 256)
     assert np.array_equal(slots, s_ref)
     assert np.array_equal(kc, kref) and np.array_equal(vc, vref)
     err = np.abs(got - ref).max()
