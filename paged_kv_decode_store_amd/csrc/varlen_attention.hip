@@ -98,13 +98,15 @@ struct VarlenTile {
     static constexpr int PIECES = D / 8;          // 16-byte pieces per K/V row
     static constexpr int KSTEP = kVGroupThreads / PIECES;  // positions between a thread's K pieces
     static constexpr int K_RS = D + 8;            // K row stride in LDS (bf16)
-    // V^T rows (one per dim) of KT/2 position-pair words, padded, with the
-    // word column XORed by 2 * ((row >> V_SWZ) & 15): with this stride and
-    // swizzle both the transposing stores (lanes spread over dims) and the
-    // operand reads (lanes spread over dims, other columns) hit 32 distinct
-    // banks per 16 lanes
-    static constexpr int V_RS = D == 128 ? 36 : 72;
-    static constexpr int V_SWZ = D == 128 ? 3 : 2;
+    // V^T rows (one per dim) of KT/2 position-pair words, padded to KT/2 + 2
+    // words, with the word column XORed by V_XOR * (row / 32).  Found by an
+    // exhaustive search over strides and swizzle tables under 64 banks of
+    // 4 bytes (32 lanes per cycle for 8-byte accesses): both the operand
+    // reads (32 lanes on 32 consecutive dims, one column) and the
+    // transposing stores (lanes spread over dims and position pairs) are
+    // then bank-conflict free.
+    static constexpr int V_RS = KT / 2 + 2;
+    static constexpr int V_XOR = D == 128 ? 4 : 8;
     static constexpr int K_BYTES = KT * K_RS * 2;
     static constexpr int V_BYTES = D * V_RS * 4;
     static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
@@ -112,7 +114,7 @@ struct VarlenTile {
     // tile): 4 K pieces (positions t/PIECES + i*KSTEP) and 4 V pieces
     // (positions 4*(t/PIECES) + i, dims 8*(t%PIECES) + [0, 8)) per thread
     static_assert(KT * PIECES == 4 * kVGroupThreads, "4 K pieces per thread");
-    static_assert(V_RS >= KT / 2 && 2 * 15 < KT / 2, "swizzle stays inside a row");
+    static_assert(V_XOR * (D / 32 - 1) < KT / 2 && V_XOR % 2 == 0, "swizzle stays inside a row");
 };
 
 // UB: every tile lies inside one block (block_size >= KT), so a tile's
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
                 w1 = pair16<0>(vr[2][wi], vr[3][wi]);
             }
             const int row = piece * 8 + d;
-            const int col = (2 * kq) ^ (2 * ((row >> T::V_SWZ) & 15));
+            const int col = (2 * kq) ^ (T::V_XOR * (row >> 5));
             *reinterpret_cast<u2_t *>(vs + row * T::V_RS + col) = u2_t{w0, w1};
         }
     };
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     const int k_lds = (c * T::K_RS + 8 * h) * 2;
     auto v_lds = [&](int j, int u, int e) -> int {
         const int row = 32 * j + c;
-        const int col = (8 * u + 2 * h + 4 * e) ^ (2 * ((row >> T::V_SWZ) & 15));
+        const int col = (8 * u + 2 * h + 4 * e) ^ (T::V_XOR * j);
         return T::K_BYTES + (row * T::V_RS + col) * 4;
     };
 
@@ -400,7 +402,9 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     // merge the odd-tile group into the even-tile group: wave w + 4 holds
     // the same (query, dims) items as wave w, for the other tiles
     {
-        float *xo = reinterpret_cast<float *>(smem) + (wave * 64 + lane) * (NOB * 16 + 2);
+        // one odd-strided record per lane (NOB*16 outputs, max, sum): the 64
+        // lanes of each access land in distinct banks
+        float *xo = reinterpret_cast<float *>(smem) + (wave * 64 + lane) * (NOB * 16 + 3);
         if (wgroup == 1) {
 #pragma unroll
             for (int j = 0; j < NOB; ++j)
