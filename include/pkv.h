@@ -112,7 +112,11 @@ int pkv_kv_store(void *k_cache, void *v_cache, const void *k_new,
  *                depends on batch, heads and max_context_len only, never on
  *                device data, so a query and the launch always agree)
  * workspace      device scratch of at least pkv_decode_workspace_bytes(...)
- *                bytes, 256-byte aligned; contents on entry are ignored. */
+ *                bytes, 256-byte aligned; contents on entry are ignored.
+ * When the split geometry gives every row a single split, the combined
+ * entry points (pkv_paged_decode_attention and its _store form) launch
+ * only the partial step, which writes the normalised output itself; the
+ * result is the same bit for bit as partial + reduce. */
 int32_t pkv_decode_split_tokens(int32_t batch, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t max_context_len,
                                 int32_t split_tokens);

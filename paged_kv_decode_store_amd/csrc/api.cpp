@@ -240,6 +240,9 @@ int setup_partial(pkv::PartialArgs &a, const void *q, int64_t q_stride, const vo
                   void *workspace, size_t workspace_bytes, bool fused,
                   const pkv::SplitGeometry *geometry = nullptr)
 {
+    // every field not set below is zero: in particular `out` stays null, so
+    // the partial kernels write partials, not the direct output
+    memset(&a, 0, sizeof a);
     int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                    block_table_stride, max_context_len);
     if (rc) return rc;
@@ -311,6 +314,48 @@ int setup_partial(pkv::PartialArgs &a, const void *q, int64_t q_stride, const vo
     a.vq_per_kv = 0;
     a.vchunks = 1;
     return PKV_OK;
+}
+
+// Partial step then reduce step, or, when the split geometry gives every row
+// a single split, only the partial step writing the normalised output
+// itself (the reduce of one partial is that partial divided by its sum, so
+// the result is the same bit for bit).  Every argument of both steps is
+// checked before anything is enqueued.
+int decode_attention_combined(void *out, int64_t out_stride, const void *q, int64_t q_stride,
+                              const void *k_cache, const void *v_cache, const void *k_new,
+                              const void *v_new, int64_t new_token_stride,
+                              const int32_t *block_tables, int32_t block_table_stride,
+                              const int32_t *context_lens, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, int32_t max_context_len, float scale,
+                              int32_t split_tokens, void *workspace, size_t workspace_bytes,
+                              bool fused, hipStream_t stream)
+{
+    const int64_t os = out_stride ? out_stride : (int64_t)num_q_heads * head_dim;
+    if (batch > 0) {
+        REQUIRE(out && aligned(out, 16), PKV_ERR_INVALID_ARG,
+                "out must be non-null and 16-byte aligned");
+    }
+    REQUIRE(num_q_heads > 0 && (os >= (int64_t)num_q_heads * head_dim) && os % 8 == 0,
+            PKV_ERR_INVALID_ARG, "out_stride must be >= num_q_heads*head_dim and a multiple of 8");
+    pkv::PartialArgs a;
+    int rc = setup_partial(a, q, q_stride, k_cache, v_cache, k_new, v_new, new_token_stride,
+                           block_tables, block_table_stride, context_lens, batch, num_q_heads,
+                           num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale,
+                           split_tokens, workspace, workspace_bytes, fused);
+    if (rc || batch == 0) return rc;
+    if (a.num_splits == 1) {
+        a.out = static_cast<uint16_t *>(out);
+        a.out_stride = os;
+        return hip_status(pkv::launch_decode_partial(a, head_dim, stream),
+                          "decode attention (single split) launch");
+    }
+    rc = hip_status(pkv::launch_decode_partial(a, head_dim, stream), "decode partial launch");
+    if (rc) return rc;
+    return pkv_decode_attention_reduce(out, out_stride, context_lens, batch, num_q_heads,
+                                       num_kv_heads, head_dim, block_table_stride, block_size,
+                                       max_context_len, split_tokens, workspace, workspace_bytes,
+                                       stream);
 }
 
 }  // namespace
@@ -562,25 +607,11 @@ int pkv_paged_decode_attention(void *out, int64_t out_stride, const void *q, int
                                int32_t split_tokens, void *workspace, size_t workspace_bytes,
                                hipStream_t stream)
 {
-    // validate the reduce's own arguments first so that nothing is enqueued
-    // when either step would be refused
-    const int64_t os = out_stride ? out_stride : (int64_t)num_q_heads * head_dim;
-    if (batch > 0) {
-        REQUIRE(out && aligned(out, 16), PKV_ERR_INVALID_ARG,
-                "out must be non-null and 16-byte aligned");
-    }
-    REQUIRE(num_q_heads > 0 && (os >= (int64_t)num_q_heads * head_dim) && os % 8 == 0,
-            PKV_ERR_INVALID_ARG, "out_stride must be >= num_q_heads*head_dim and a multiple of 8");
-    int rc = pkv_decode_attention_partial(q, q_stride, k_cache, v_cache, block_tables,
-                                          block_table_stride, context_lens, batch, num_q_heads,
-                                          num_kv_heads, head_dim, block_size, num_blocks,
-                                          max_context_len, scale, split_tokens, workspace,
-                                          workspace_bytes, stream);
-    if (rc) return rc;
-    return pkv_decode_attention_reduce(out, out_stride, context_lens, batch, num_q_heads,
-                                       num_kv_heads, head_dim, block_table_stride, block_size,
-                                       max_context_len, split_tokens, workspace, workspace_bytes,
-                                       stream);
+    return decode_attention_combined(out, out_stride, q, q_stride, k_cache, v_cache, nullptr,
+                                     nullptr, 0, block_tables, block_table_stride, context_lens,
+                                     batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     num_blocks, max_context_len, scale, split_tokens, workspace,
+                                     workspace_bytes, false, stream);
 }
 
 int pkv_paged_decode_attention_store(void *out, int64_t out_stride, const void *q,
@@ -593,22 +624,11 @@ int pkv_paged_decode_attention_store(void *out, int64_t out_stride, const void *
                                      int32_t max_context_len, float scale, int32_t split_tokens,
                                      void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    const int64_t os = out_stride ? out_stride : (int64_t)num_q_heads * head_dim;
-    if (batch > 0) {
-        REQUIRE(out && aligned(out, 16), PKV_ERR_INVALID_ARG,
-                "out must be non-null and 16-byte aligned");
-    }
-    REQUIRE(num_q_heads > 0 && (os >= (int64_t)num_q_heads * head_dim) && os % 8 == 0,
-            PKV_ERR_INVALID_ARG, "out_stride must be >= num_q_heads*head_dim and a multiple of 8");
-    int rc = pkv_decode_attention_partial_store(
-        q, q_stride, k_cache, v_cache, k_new, v_new, new_token_stride, block_tables,
-        block_table_stride, context_lens, batch, num_q_heads, num_kv_heads, head_dim, block_size,
-        num_blocks, max_context_len, scale, split_tokens, workspace, workspace_bytes, stream);
-    if (rc) return rc;
-    return pkv_decode_attention_reduce(out, out_stride, context_lens, batch, num_q_heads,
-                                       num_kv_heads, head_dim, block_table_stride, block_size,
-                                       max_context_len, split_tokens, workspace, workspace_bytes,
-                                       stream);
+    return decode_attention_combined(out, out_stride, q, q_stride, k_cache, v_cache, k_new, v_new,
+                                     new_token_stride, block_tables, block_table_stride,
+                                     context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                     block_size, num_blocks, max_context_len, scale, split_tokens,
+                                     workspace, workspace_bytes, true, stream);
 }
 
 size_t pkv_sampler_workspace_bytes(int32_t batch, int32_t vocab)

@@ -62,11 +62,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     const int n_row = a.context_lens[b];
     const int n = min(max(n_row, 0), a.max_len);
     const int t_begin = a.pos_base + s * a.split_tokens;
-    if (t_begin >= n) return;
+    const int h0 = kvh * a.group + hc * G;
+    if (t_begin >= n) {
+        // direct output (one split per row): an empty row's output is zero
+        if (a.out && s == 0)
+            for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64)
+                a.out[(int64_t)b * a.out_stride + (int64_t)h0 * D + idx] = 0;
+        return;
+    }
     // fused store: the row's new position, if it lies inside the attended range
     const int pos_new = (FUSED && n_row >= 1 && n_row <= n) ? n_row - 1 : -1;
     const int t_end = min(n, t_begin + a.split_tokens);
-    const int h0 = kvh * a.group + hc * G;
     const float c = a.c;
 
     uint4 qv[G];
@@ -244,6 +250,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
             const float e = __builtin_amdgcn_exp2f((s_m[w][h] - ref) * c);
             L += s_l[w][h] * e;
             O += s_o[w][h][d] * e;
+        }
+        if (a.out) {
+            // direct output: the only split of the row is already the result
+            a.out[(int64_t)b * a.out_stride + (int64_t)(h0 + h) * D + d] = (uint16_t)bf16_round(O / L);
+            continue;
         }
         const int64_t pidx = pbase + (int64_t)h * a.num_splits;
         a.part_o[pidx * D + d] = O;

@@ -127,7 +127,15 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
         const int n_row = a.context_lens[b];
         n = min(max(n_row, 0), a.max_len);
         t_begin = a.pos_base + s * a.split_tokens;
-        if (t_begin >= n) return;
+        if (t_begin >= n) {
+            // direct output (one split per row): an empty row's output is zero
+            if (a.out && s == 0) {
+                const int nq0 = min(kMQ, a.group - hc * kMQ);
+                const int64_t o0 = (int64_t)b * a.out_stride + (int64_t)(kvh * a.group + hc * kMQ) * D;
+                for (int idx = threadIdx.x; idx < nq0 * D; idx += kMWaves * 64) a.out[o0 + idx] = 0;
+            }
+            return;
+        }
         if (FUSED && n_row >= 1 && n_row <= n) pos_new = n_row - 1;
         t_end = min(n, t_begin + a.split_tokens);
     }
@@ -314,6 +322,12 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
             O += s_o[w][h][d] * e;
         }
         const int v = hc * kMQ + h;
+        if (!PREFIX && a.out) {
+            // direct output: the only split of the row is already the result
+            a.out[(int64_t)b * a.out_stride + (int64_t)(kvh * a.group + v) * D + d] =
+                (uint16_t)bf16_round(O / L);
+            continue;
+        }
         int64_t pidx;
         if constexpr (PREFIX) {
             const int rb = v / a.group, rh = kvh * a.group + v % a.group;
