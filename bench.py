@@ -475,7 +475,7 @@ def partial_kernel_name(cfg, D, fused, cascade):
         return "cascade: decode_partial_mfma_kernel (prefix) + tail partial kernel + reduce"
     f = "true" if fused else "false"
     if cfg.group >= 3:  # the library's matrix-core threshold
-        return f"decode_partial_mfma_kernel<{D}, {f}, false>"
+        return f"decode_partial_mfma_kernel<{D}, {f}, 0>"  # mode 0: the decode step
     g = max(x for x in range(1, 9) if cfg.group % x == 0)
     return f"decode_partial_kernel<{D}, {g}, {f}>"
 
