@@ -398,17 +398,24 @@ def run_varlen(args):
     vn = [u16(x[2]) for x in lay]
     slots = torch.empty(T, dtype=torch.int32, device=dev)
     out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
-    log(f"[bench] varlen {w.name}: {len(w.lens_new)} sequences, {T} new tokens, L={L}")
+    B = len(w.lens_new)
+    split = pkv.varlen_split_tokens(B, Hq, Hkv, mq, mk, args.split)
+    need = pkv.varlen_workspace_bytes(T, B, Hq, Hkv, D, mq, mk, args.split)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    log(f"[bench] varlen {w.name}: {B} sequences, {T} new tokens, L={L}, split {split} "
+        f"({'partials + merge' if need else 'one split'})")
 
     def step():
         pkv.varlen_slot_mapping(td, cq, ck, mq, bs, T, out=slots)
         for l in range(L):
             pkv.kv_store(kp[l], vp[l], kn[l], vn[l], slots)
-            pkv.varlen_paged_attention(q[l], kp[l], vp[l], td, cq, ck, mq, mk, out=out)
+            pkv.varlen_paged_attention(q[l], kp[l], vp[l], td, cq, ck, mq, mk,
+                                       split_tokens=args.split, out=out, workspace=ws)
 
     def attn_only():
         for l in range(L):
-            pkv.varlen_paged_attention(q[l], kp[l], vp[l], td, cq, ck, mq, mk, out=out)
+            pkv.varlen_paged_attention(q[l], kp[l], vp[l], td, cq, ck, mq, mk,
+                                       split_tokens=args.split, out=out, workspace=ws)
 
     def graph_ms(fn):
         side = torch.cuda.Stream()
@@ -457,7 +464,8 @@ def run_varlen(args):
         "config": {"workload": f"{w.name}: {len(w.lens_new)} sequences, new tokens "
                    f"{list(w.lens_new)} after cached {list(w.lens_cached)}, GQA {Hq}/{Hkv}, "
                    f"head_dim {D}, block {bs}, {L} layers",
-                   "causal_pairs_per_head": pairs},
+                   "causal_pairs_per_head": pairs, "split_tokens": split,
+                   "merge_step": bool(need)},
         "attention_us_per_layer": round(attn_us, 3),
         "attention_GBps": round(io_bytes / (attn_us * 1e-6) / 1e9, 1),
         "roofline": {"kernel": f"varlen_attention_kernel<{D}>", "bound": "mfma",

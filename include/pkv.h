@@ -270,21 +270,39 @@ int pkv_cascade_decode_attention(void *out, int64_t out_stride, const void *q,
  * table entry is negative or the position is past the table).
  * pkv_varlen_paged_attention:
  * out, q         bf16 [total_q][num_q_heads][head_dim]; token rows
- *                out_stride / q_stride elements apart (0 = packed)
+ *                out_stride / q_stride elements apart (0 = packed);
+ *                total_q = cu_seqlens_q[batch] (rows of q and out)
  * cu_seqlens_q, cu_seqlens_k  int32 [batch + 1], non-decreasing from 0
  * max_seqlen_q   >= every q_len_b (tokens past it are not computed)
  * max_seqlen_k   >= every k_len_b (positions past it or past the table
  *                are not attended)
  * head_dim 64 or 128; block_size a power of two in [16, 4096]; scale <= 0
- * selects 1/sqrt(head_dim).  No workspace: each workgroup covers its
- * tokens' whole causal range and writes the normalised output.  A sequence
- * with q_len_b = 0 or k_len_b < q_len_b writes nothing. */
+ * selects 1/sqrt(head_dim).
+ * split_tokens   positions per workgroup of a tile's causal range: 0 =
+ *                automatic (pkv_varlen_split_tokens: from batch, heads and
+ *                the maximum lengths only), else a positive multiple of
+ *                256.  Ranges needing one split are written directly;
+ *                longer ones go through fp32 partials in the workspace and
+ *                a log-sum-exp merge.
+ * workspace      >= pkv_varlen_workspace_bytes(...) bytes, 256-byte
+ *                aligned; may be null when that size is 0 (every range fits
+ *                one split).  Contents on entry are ignored.
+ * A sequence with q_len_b = 0 or k_len_b < q_len_b writes nothing. */
 int pkv_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
                             int32_t block_table_stride,
                             const int32_t *cu_seqlens_q,
                             const int32_t *cu_seqlens_k, int32_t batch,
                             int32_t max_seqlen_q, int32_t block_size,
                             hipStream_t stream);
+
+int32_t pkv_varlen_split_tokens(int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t max_seqlen_q,
+                                int32_t max_seqlen_k, int32_t split_tokens);
+
+size_t pkv_varlen_workspace_bytes(int32_t total_q, int32_t batch,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seqlen_q,
+                                  int32_t max_seqlen_k, int32_t split_tokens);
 
 int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q,
                                int64_t q_stride, const void *k_cache,
@@ -293,10 +311,12 @@ int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q,
                                int32_t block_table_stride,
                                const int32_t *cu_seqlens_q,
                                const int32_t *cu_seqlens_k, int32_t batch,
-                               int32_t num_q_heads, int32_t num_kv_heads,
-                               int32_t head_dim, int32_t block_size,
-                               int64_t num_blocks, int32_t max_seqlen_q,
-                               int32_t max_seqlen_k, float scale,
+                               int32_t total_q, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               float scale, int32_t split_tokens,
+                               void *workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
 /* ---- sampler --------------------------------------------------------------

@@ -23,6 +23,7 @@ __all__ = [
     "cascade_decode_attention", "cascade_workspace_bytes",
     "varlen_slot_mapping", "varlen_paged_attention",
     "sample_next_token", "sample_next_token_ex", "sampler_workspace_bytes", "PkvError",
+    "varlen_split_tokens", "varlen_workspace_bytes",
     "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
 ]
 
@@ -333,10 +334,26 @@ def varlen_slot_mapping(block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor,
     return out
 
 
+def varlen_split_tokens(batch: int, num_q_heads: int, num_kv_heads: int, max_seqlen_q: int,
+                        max_seqlen_k: int, split_tokens: int = 0) -> int:
+    return int(lib().pkv_varlen_split_tokens(batch, num_q_heads, num_kv_heads, max_seqlen_q,
+                                             max_seqlen_k, split_tokens))
+
+
+def varlen_workspace_bytes(total_q: int, batch: int, num_q_heads: int, num_kv_heads: int,
+                           head_dim: int, max_seqlen_q: int, max_seqlen_k: int,
+                           split_tokens: int = 0) -> int:
+    return int(lib().pkv_varlen_workspace_bytes(total_q, batch, num_q_heads, num_kv_heads,
+                                                head_dim, max_seqlen_q, max_seqlen_k,
+                                                split_tokens))
+
+
 def varlen_paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor,
                            cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
-                           scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                           scale: float = 0.0, split_tokens: int = 0,
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16 [total_q, Hq, D]: each new token of each sequence attends causally
     to the sequence's cached tokens and to the new tokens up to itself."""
     T, Hq, D = q.shape
@@ -351,11 +368,15 @@ def varlen_paged_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     B = cu_seqlens_q.numel() - 1
     if out is None:
         out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    need = varlen_workspace_bytes(T, B, Hq, hkv, D, max_seqlen_q, max_seqlen_k, split_tokens)
+    ws = _workspace(need, q.device, workspace) if need else None
     check(lib().pkv_varlen_paged_attention(
         _dev(out, "out", torch.bfloat16), out.stride(0), _dev(q, "q", torch.bfloat16), q.stride(0),
         _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
-        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), B, Hq, hkv, D, bs, nb, max_seqlen_q,
-        max_seqlen_k, scale, _stream()), "pkv_varlen_paged_attention")
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32), B, T, Hq, hkv, D, bs, nb, max_seqlen_q,
+        max_seqlen_k, scale, split_tokens,
+        _dev(ws, "workspace", torch.uint8) if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream()), "pkv_varlen_paged_attention")
     return out

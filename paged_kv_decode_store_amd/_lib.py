@@ -53,9 +53,11 @@ PROTOTYPES = {
                                                     _P, _I32, _I32, _I32, _I32, _I32, _I64, _I32,
                                                     _F, _I32, _P, _SZ, _P]),
     "pkv_varlen_slot_mapping": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _P]),
+    "pkv_varlen_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_varlen_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_varlen_paged_attention": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _P, _I32, _P, _P,
-                                                  _I32, _I32, _I32, _I32, _I32, _I64, _I32, _I32,
-                                                  _F, _P]),
+                                                  _I32, _I32, _I32, _I32, _I32, _I32, _I64, _I32,
+                                                  _I32, _F, _I32, _P, _SZ, _P]),
     "pkv_sampler_workspace_bytes": (_SZ, [_I32, _I32]),
     "pkv_sample_next_token": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _U32,
                                              _P, _SZ, _P]),

@@ -316,6 +316,57 @@ int setup_partial(pkv::PartialArgs &a, const void *q, int64_t q_stride, const vo
     return PKV_OK;
 }
 
+// Varlen attention: positions per split of a row tile's causal range.  Given
+// a positive multiple of 256, that; otherwise only as many splits as bring
+// the workgroup count up to about one per CU of the 256 on MI355X, assuming
+// every sequence at the maximum lengths (the host never reads cu_seqlens),
+// with at least 1024 positions per split.  Measured on the Qwen3-shaped
+// chunk (256 row tiles already), splitting further costs more than it
+// balances: 1024-position splits took 55.5 us + 13.9 us of merge against
+// 48.3 us unsplit.  Never longer than max_seqlen_k needs (then one split:
+// no workspace).
+int32_t varlen_effective_split(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t split_tokens)
+{
+    const int64_t cap = ((int64_t)(max_seqlen_k > 0 ? max_seqlen_k : 1) + 255) / 256 * 256;
+    int64_t spl = split_tokens;
+    if (spl <= 0) {
+        const int64_t g = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
+        const int64_t tiles = ((int64_t)max_seqlen_q * g + 127) / 128;
+        const int64_t jobs = (int64_t)batch * num_kv_heads * tiles;
+        spl = ((int64_t)max_seqlen_k * jobs + 255) / 256;
+        if (spl < 1024) spl = 1024;
+        spl = (spl + 1023) / 1024 * 1024;
+    }
+    if (spl > cap) spl = cap;
+    return (int32_t)spl;
+}
+
+struct VarlenGeometry {
+    int32_t split_tokens;
+    int32_t num_splits;
+    size_t part_o_bytes, total_bytes;
+};
+
+VarlenGeometry varlen_geometry(int32_t total_q, int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen_q,
+                               int32_t max_len, int32_t split_tokens)
+{
+    VarlenGeometry g;
+    g.split_tokens = varlen_effective_split(batch, num_q_heads, num_kv_heads, max_seqlen_q,
+                                            max_len, split_tokens);
+    const int64_t ml = max_len > 0 ? max_len : 0;
+    g.num_splits = (int32_t)((ml + g.split_tokens - 1) / g.split_tokens);
+    if (g.num_splits < 1) g.num_splits = 1;
+    g.part_o_bytes = g.total_bytes = 0;
+    if (g.num_splits > 1) {
+        const size_t units = (size_t)(total_q > 0 ? total_q : 0) * num_q_heads * g.num_splits;
+        g.part_o_bytes = (units * head_dim * sizeof(float) + 255) & ~(size_t)255;
+        g.total_bytes = g.part_o_bytes + ((units * 2 * sizeof(float) + 255) & ~(size_t)255);
+    }
+    return g;
+}
+
 // Partial step then reduce step, or, when the split geometry gives every row
 // a single split, only the partial step writing the normalised output
 // itself (the reduce of one partial is that partial divided by its sum, so
@@ -463,19 +514,45 @@ int pkv_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
                       "varlen slot mapping launch");
 }
 
+int32_t pkv_varlen_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t split_tokens)
+{
+    if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seqlen_q < 0 ||
+        max_seqlen_k < 0 || split_tokens < 0 || split_tokens % 256)
+        return 0;
+    return varlen_effective_split(batch, num_q_heads, num_kv_heads, max_seqlen_q, max_seqlen_k,
+                                  split_tokens);
+}
+
+size_t pkv_varlen_workspace_bytes(int32_t total_q, int32_t batch, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen_q,
+                                  int32_t max_seqlen_k, int32_t split_tokens)
+{
+    if (total_q < 0 || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_seqlen_q < 0 || max_seqlen_k < 0 || split_tokens < 0 || split_tokens % 256)
+        return 0;
+    return varlen_geometry(total_q, batch, num_q_heads, num_kv_heads, head_dim, max_seqlen_q,
+                           max_seqlen_k, split_tokens)
+        .total_bytes;
+}
+
 int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q, int64_t q_stride,
                                const void *k_cache, const void *v_cache,
                                const int32_t *block_tables, int32_t block_table_stride,
                                const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
-                               int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                               int32_t max_seqlen_q, int32_t max_seqlen_k, float scale,
-                               hipStream_t stream)
+                               int32_t batch, int32_t total_q, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                               float scale, int32_t split_tokens, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream)
 {
     int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                    block_table_stride, max_seqlen_k);
     if (rc) return rc;
-    REQUIRE(max_seqlen_q >= 0, PKV_ERR_INVALID_ARG, "max_seqlen_q must be >= 0");
+    REQUIRE(max_seqlen_q >= 0 && total_q >= 0, PKV_ERR_INVALID_ARG,
+            "max_seqlen_q and total_q must be >= 0");
+    REQUIRE(split_tokens >= 0 && split_tokens % 256 == 0, PKV_ERR_INVALID_ARG,
+            "split_tokens must be 0 or a positive multiple of 256");
     REQUIRE(num_blocks > 0, PKV_ERR_INVALID_ARG, "num_blocks must be > 0");
     REQUIRE((int64_t)max_seqlen_q * (num_q_heads / num_kv_heads) <= (1 << 30),
             PKV_ERR_UNSUPPORTED, "max_seqlen_q * group too large");
@@ -485,13 +562,22 @@ int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q, int
     REQUIRE(qs >= row && qs % 8 == 0 && os >= row && os % 8 == 0, PKV_ERR_INVALID_ARG,
             "q_stride / out_stride must be >= num_q_heads*head_dim and multiples of 8");
     REQUIRE(isfinite(scale), PKV_ERR_INVALID_ARG, "scale must be finite");
-    if (batch == 0 || max_seqlen_q == 0) return PKV_OK;
+    if (batch == 0 || max_seqlen_q == 0 || total_q == 0) return PKV_OK;
     REQUIRE(out && q && k_cache && v_cache && block_tables && cu_seqlens_q && cu_seqlens_k,
             PKV_ERR_INVALID_ARG, "null pointer");
     REQUIRE(aligned(out, 16) && aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16),
             PKV_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
     REQUIRE(aligned(block_tables, 4) && aligned(cu_seqlens_q, 4) && aligned(cu_seqlens_k, 4),
             PKV_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+    const int32_t max_len = clamp_len(max_seqlen_k, block_table_stride, block_size);
+    const VarlenGeometry g = varlen_geometry(total_q, batch, num_q_heads, num_kv_heads, head_dim,
+                                             max_seqlen_q, max_len, split_tokens);
+    if (g.num_splits > 1) {
+        REQUIRE(workspace && aligned(workspace, 256), PKV_ERR_WORKSPACE,
+                "workspace must be non-null and 256-byte aligned");
+        REQUIRE(workspace_bytes >= g.total_bytes, PKV_ERR_WORKSPACE,
+                "workspace too small: %zu < %zu bytes", workspace_bytes, g.total_bytes);
+    }
     pkv::PartialArgs a;
     memset(&a, 0, sizeof a);
     a.q = static_cast<const uint16_t *>(q);
@@ -507,14 +593,20 @@ int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q, int
     a.head_chunks = 1;
     a.bs_log2 = __builtin_ctz((unsigned)block_size);
     a.num_blocks = num_blocks;
-    a.max_len = clamp_len(max_seqlen_k, block_table_stride, block_size);
-    a.split_tokens = a.max_len;
+    a.max_len = max_len;
+    a.split_tokens = g.split_tokens;
+    a.num_splits = g.num_splits;
+    if (g.num_splits > 1) {
+        a.part_o = static_cast<float *>(workspace);
+        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + g.part_o_bytes);
+    }
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
     a.c = sc * 1.4426950408889634f;
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
     a.out = static_cast<uint16_t *>(out);
     a.out_stride = os;
+    a.total_q = total_q;
     return hip_status(pkv::launch_varlen_attention(a, head_dim, max_seqlen_q, stream),
                       "varlen attention launch");
 }

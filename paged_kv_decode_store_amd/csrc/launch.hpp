@@ -81,6 +81,7 @@ struct PartialArgs {
     uint16_t *out;
     int64_t out_stride;
     int32_t qchunks;        // chunks per sequence (from the longest one)
+    int32_t total_q;        // rows of q / out (the merge step's grid)
 };
 
 struct ReduceArgs {

@@ -27,6 +27,13 @@
 //                 LDS transposed into words of two adjacent positions at
 //                 one dim, so each A operand is two 8-byte LDS reads.
 //
+// Long causal ranges are split over several workgroups (split_tokens
+// positions each, like the split-KV decode): a row tile whose range needs
+// one split writes its normalised output directly, the others write fp32
+// partials (max in log2 units, sum, unnormalised output) that a merge
+// kernel combines by log-sum-exp.  This keeps all CUs busy when few tiles
+// carry long cached prefixes and balances tiles of unequal length.
+//
 // O^T leaves every query's running output in the lanes that own that
 // query's scores, so the online-softmax rescale is lane-local.  It is also
 // lazy: the reference max only moves when a row's max exceeds it by more
@@ -46,6 +53,7 @@ typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
 typedef float f16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef float f4v_t __attribute__((ext_vector_type(4)));
 
 constexpr int kVRowWaves = 4;                  // waves covering a tile's rows
 constexpr int kVRowsW = 32;                    // rows (token, head) per wave
@@ -142,7 +150,9 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     // share that XCD's L2 copy of the pair's K/V.
     const int pairs = a.batch * a.num_kv_heads;
     const int pair = blockIdx.x % pairs;
-    const int tile = a.qchunks - 1 - (int)(blockIdx.x / pairs);
+    const int rest = (int)(blockIdx.x / pairs);
+    const int tile = a.qchunks - 1 - rest % a.qchunks;
+    const int sidx = rest / a.qchunks;    // split of the tile's causal range
     const int b = pair / a.num_kv_heads;
     const int kvh = pair - b * a.num_kv_heads;
     const int g = a.group;
@@ -155,9 +165,13 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     const int row0 = tile * kVRows;
     if (row0 >= q_len * g) return;
     const int j_last = min(q_len - 1, (row0 + kVRows - 1) / g);
-    const int t_end = min(cached + j_last + 1, a.max_len);
-    if (t_end <= 0) return;
-    const int ntiles = (t_end + KT - 1) / KT;
+    const int t_full = min(cached + j_last + 1, a.max_len);   // the tile's causal range
+    if (t_full <= 0) return;
+    const int nsplit = (t_full + a.split_tokens - 1) / a.split_tokens;
+    if (sidx >= nsplit) return;
+    const int t_lo = sidx * a.split_tokens;                    // this split: [t_lo, t_end)
+    const int t_end = min(t_full, t_lo + a.split_tokens);
+    const int ntiles = (t_end - t_lo + KT - 1) / KT;
     const int nsteps = (ntiles + kVGroups - 1) / kVGroups;   // tiles per group
 
     // this lane's query row
@@ -295,11 +309,12 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     Ids ids;
     u4_t kr[4], vr[4];
     // group g's tiles are g, g + 2, g + 4, ...
-    const int tfirst = wgroup * KT;
+    const int tfirst = t_lo + wgroup * KT;
+    const int tlast = t_lo + (ntiles - 1) * KT;
     constexpr int TSTRIDE = kVGroups * KT;
-    tile_ids(min(tfirst, (ntiles - 1) * KT), ids);
+    tile_ids(min(tfirst, tlast), ids);
     load_tile(tfirst, ids, kr, vr);
-    if (nsteps > 1) tile_ids(min(tfirst + TSTRIDE, (ntiles - 1) * KT), ids);
+    if (nsteps > 1) tile_ids(min(tfirst + TSTRIDE, tlast), ids);
     if (tfirst < t_end) store_tile(slot(0), tfirst, kr, vr);
     __syncthreads();
 
@@ -308,7 +323,7 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
         const bool more = it + 1 < nsteps;
         if (more) {
             load_tile(t0 + TSTRIDE, ids, kr, vr);
-            if (it + 2 < nsteps) tile_ids(min(t0 + 2 * TSTRIDE, (ntiles - 1) * KT), ids);
+            if (it + 2 < nsteps) tile_ids(min(t0 + 2 * TSTRIDE, tlast), ids);
         }
         const unsigned char *st_base = slot(it & 1);
 
@@ -425,11 +440,30 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
         for (int j = 0; j < NOB; ++j)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[j][i] = o[j][i] * a1 + xo[j * 16 + i] * a2;
+        mr = mn;   // (o, lsum) are now relative to the merged reference
     }
 
-    // normalise and write: O^T block j item 4q + r = dim 32j + 8q + 4h + r
+    // O^T block j item 4q + r = dim 32j + 8q + 4h + r
     lsum = xor32_sum(lsum);
     if (!real) return;
+    if (nsplit > 1) {
+        // partial of split sidx: output relative to 2^(mr * c), its sum, and
+        // mr * c (log2 units; -inf when no position of the split is visible)
+        const int64_t prow = ((int64_t)(q0 + jq) * a.num_q_heads + head) * a.num_splits + sidx;
+        float *po = a.part_o + prow * D + 4 * h;
+#pragma unroll
+        for (int j = 0; j < NOB; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f4v_t *>(po + 32 * j + 8 * q) =
+                    f4v_t{o[j][4 * q], o[j][4 * q + 1], o[j][4 * q + 2], o[j][4 * q + 3]};
+        if (h == 0) {
+            a.part_ml[2 * prow] = mr == -INFINITY ? -INFINITY : mr * cs;
+            a.part_ml[2 * prow + 1] = lsum;
+        }
+        return;
+    }
+    // the only split: normalise and write bf16
     const float inv = 1.0f / lsum;
     uint16_t *orow = a.out + (int64_t)(q0 + jq) * a.out_stride + (int64_t)head * D + 4 * h;
 #pragma unroll
@@ -442,14 +476,72 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
         }
 }
 
+// Merge of a split row tile's partials: one wave per (token row, query
+// head).  The row's sequence is found by binary search in cu_q, its tile and
+// causal range are recomputed exactly as the attention kernel derived them,
+// and rows whose tile needed a single split (already written) are skipped.
+// O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, bf16 (round to nearest
+// even).
+template <int D>
+__global__ __launch_bounds__(256) void varlen_merge_kernel(const PartialArgs a)
+{
+    constexpr int DPL = D / 64;   // output dims per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gw >= (int64_t)a.total_q * a.num_q_heads) return;
+    const int r = (int)(gw / a.num_q_heads);
+    const int head = (int)(gw - (int64_t)r * a.num_q_heads);
+    int lo = 0, hi = a.batch;   // the last b with cu_q[b] <= r
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu_q[mid] <= r) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int q0 = a.cu_q[b];
+    const int q_len = a.cu_q[b + 1] - q0;
+    const int k_len = a.cu_k[b + 1] - a.cu_k[b];
+    if (q_len <= 0 || k_len < q_len || r - q0 >= q_len) return;
+    const int g = a.group;
+    const int v = (r - q0) * g + head % g;
+    const int tile = v / kVRows;
+    const int j_last = min(q_len - 1, (tile * kVRows + kVRows - 1) / g);
+    const int t_full = min(k_len - q_len + j_last + 1, a.max_len);
+    const int ns = t_full <= 0 ? 0 : (t_full + a.split_tokens - 1) / a.split_tokens;
+    if (ns <= 1) return;
+    const int64_t base = ((int64_t)r * a.num_q_heads + head) * a.num_splits;
+    const float *ml = a.part_ml + 2 * base;
+    float M = -INFINITY;
+    for (int s2 = lane; s2 < ns; s2 += 64) M = fmaxf(M, ml[2 * s2]);
+    M = wave_max(M);   // split 0 always holds position 0, so M is finite
+    float L = 0.f;
+    for (int s2 = lane; s2 < ns; s2 += 64) L += ml[2 * s2 + 1] * __builtin_amdgcn_exp2f(ml[2 * s2] - M);
+    L = wave_sum(L);
+    float acc[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
+    const float *po = a.part_o + base * D + lane * DPL;
+    for (int s2 = 0; s2 < ns; ++s2) {
+        const float w = __builtin_amdgcn_exp2f(ml[2 * s2] - M);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[j] += w * po[(int64_t)s2 * D + j];
+    }
+    uint16_t *orow = a.out + (int64_t)r * a.out_stride + (int64_t)head * D + lane * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) orow[j] = (uint16_t)bf16_round(acc[j] / L);
+}
+
 template <int D>
 hipError_t launch_varlen_d(const PartialArgs &a, hipStream_t stream)
 {
-    const int64_t grid = (int64_t)a.qchunks * a.batch * a.num_kv_heads;
+    const int64_t grid = (int64_t)a.num_splits * a.qchunks * a.batch * a.num_kv_heads;
     if ((1 << a.bs_log2) >= VarlenTile<D>::KT)
         varlen_attention_kernel<D, true><<<(unsigned)grid, kVThreads, 0, stream>>>(a);
     else
         varlen_attention_kernel<D, false><<<(unsigned)grid, kVThreads, 0, stream>>>(a);
+    if (a.num_splits > 1) {
+        const int64_t rows = (int64_t)a.total_q * a.num_q_heads;
+        varlen_merge_kernel<D><<<(unsigned)((rows + 3) / 4), 256, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.PROTOTYPES)
@@ -222,15 +222,37 @@ def test_sampler_ex_validation():
 def test_varlen_validation():
     L = _lib.lib()
 
+    # one sequence, 512 new tokens after a long prefix: 64 row tiles, so the
+    # automatic choice splits each causal range in 4
+    need = L.pkv_varlen_workspace_bytes(512, 1, 16, 8, 128, 512, 65536, 0)
+
     def call(**kw):
-        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cq=FAKE, ck=FAKE, B=4, Hq=16, Hkv=8,
-                 D=128, bs=256, mq=512, mk=4096, qs=0, scale=0.0)
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cq=FAKE, ck=FAKE, B=1, T=512, Hq=16,
+                 Hkv=8, D=128, bs=256, mq=512, mk=65536, qs=0, scale=0.0, split=0, ws=FAKE,
+                 wsb=need)
         a.update(kw)
         return L.pkv_varlen_paged_attention(a["out"], 0, a["q"], a["qs"], a["k"], a["v"], a["bt"],
-                                            16, a["cq"], a["ck"], a["B"], a["Hq"], a["Hkv"],
-                                            a["D"], a["bs"], 600, a["mq"], a["mk"], a["scale"],
-                                            None)
+                                            256, a["cq"], a["ck"], a["B"], a["T"], a["Hq"],
+                                            a["Hkv"], a["D"], a["bs"], 600, a["mq"], a["mk"],
+                                            a["scale"], a["split"], a["ws"], a["wsb"], None)
 
+    # automatic split: only up to about one workgroup per CU, >= 1024
+    # positions, never longer than the longest range needs (then no workspace)
+    assert L.pkv_varlen_split_tokens(1, 16, 8, 512, 65536, 0) == 16384
+    assert L.pkv_varlen_split_tokens(4, 16, 8, 512, 2048, 0) == 2048
+    assert L.pkv_varlen_split_tokens(2, 16, 8, 512, 8192, 0) == 4096
+    assert L.pkv_varlen_split_tokens(7, 4, 2, 64, 364, 0) == 512
+    assert L.pkv_varlen_split_tokens(4, 16, 8, 512, 4096, 512) == 512
+    assert L.pkv_varlen_split_tokens(4, 16, 8, 512, 4096, 100) == 0
+    assert need == (512 * 16 * 4 * 128 * 4) + (512 * 16 * 4 * 2 * 4)
+    assert L.pkv_varlen_workspace_bytes(2048, 4, 16, 8, 128, 512, 2048, 0) == 0
+    assert L.pkv_varlen_workspace_bytes(7, 7, 4, 2, 128, 64, 364, 0) == 0
+    assert call(ws=None) == _lib.PKV_ERR_WORKSPACE
+    assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == _lib.PKV_ERR_WORKSPACE
+    assert call(split=100) == _lib.PKV_ERR_INVALID_ARG
+    assert call(T=-1) == _lib.PKV_ERR_INVALID_ARG
+    assert call(T=0, out=None, q=None) == _lib.PKV_OK
     assert call(cq=None) == _lib.PKV_ERR_INVALID_ARG
     assert call(out=FAKE + 8) == _lib.PKV_ERR_INVALID_ARG
     assert call(D=96) == _lib.PKV_ERR_UNSUPPORTED

@@ -49,8 +49,9 @@ def _case(rng, lens_cached, lens_new, Hq, Hkv, D, bs, spare=3):
     return q, kp, vp, kn, vn, tables, cu_q, cu_k
 
 
-def _prefill(q, kp, vp, kn, vn, tables, cu_q, cu_k, bs):
-    """GPU: slots of the new tokens, store, varlen attention."""
+def _prefill(q, kp, vp, kn, vn, tables, cu_q, cu_k, bs, split=0):
+    """GPU: slots of the new tokens, store, varlen attention (split_tokens
+    `split`: 0 automatic, else positions per split of a tile's range)."""
     lens_new = np.diff(cu_q)
     lens_k = np.diff(cu_k)
     mq, mk = int(lens_new.max()), int(lens_k.max())
@@ -58,7 +59,7 @@ def _prefill(q, kp, vp, kn, vn, tables, cu_q, cu_k, bs):
     td, cq, ck = dev_i32(tables), dev_i32(cu_q), dev_i32(cu_k)
     slots = pkv.varlen_slot_mapping(td, cq, ck, mq, bs, int(cu_q[-1]))
     pkv.kv_store(kc, vc, dev_u16(kn), dev_u16(vn), slots)
-    out = pkv.varlen_paged_attention(dev_u16(q), kc, vc, td, cq, ck, mq, mk)
+    out = pkv.varlen_paged_attention(dev_u16(q), kc, vc, td, cq, ck, mq, mk, split_tokens=split)
     torch.cuda.synchronize()
     return slots.cpu().numpy(), host_u16(kc), host_u16(vc), bf16_out_to_f64(out)
 
@@ -79,13 +80,16 @@ def _reference(q, kp, vp, kn, vn, tables, cu_q, cu_k, bs, rows=None):
                                          (128, 16, 1, 16), (64, 12, 4, 64), (128, 9, 3, 16),
                                          (128, 6, 2, 64), (64, 8, 2, 128), (64, 4, 4, 256),
                                          (128, 48, 8, 256)])
-def test_varlen_matches_oracle(D, Hq, Hkv, bs):
+@pytest.mark.parametrize("split", [0, 256])
+def test_varlen_matches_oracle(D, Hq, Hkv, bs, split):
+    """split 256: ranges longer than 256 positions go through partials and
+    the log-sum-exp merge (the automatic choice keeps these in one split)."""
     rng = np.random.default_rng(D + 7 * Hq + 3 * Hkv + bs)
     lens_cached = [0, 5, 40, 0, 300, 17, 64]
     lens_new = [1, 33, 7, 50, 2, 64, 1]
     args = _case(rng, lens_cached, lens_new, Hq, Hkv, D, bs)
-    say(f"varlen D={D} Hq={Hq} Hkv={Hkv} bs={bs} cached={lens_cached} new={lens_new}")
-    slots, kc, vc, got = _prefill(*args, bs)
+    say(f"varlen D={D} Hq={Hq} Hkv={Hkv} bs={bs} split={split} cached={lens_cached} new={lens_new}")
+    slots, kc, vc, got = _prefill(*args, bs, split)
     s_ref, kref, vref, ref = _reference(*args, bs)
     assert np.array_equal(slots, s_ref)
     assert np.array_equal(kc, kref) and np.array_equal(vc, vref)
@@ -94,7 +98,8 @@ def test_varlen_matches_oracle(D, Hq, Hkv, bs):
     assert err <= ATTN_TOL
 
 
-def test_varlen_empty_sequence_and_long_prefix():
+@pytest.mark.parametrize("split", [0, 512])
+def test_varlen_empty_sequence_and_long_prefix(split):
     """A sequence with no new tokens between others (its rows do not exist,
     the rest are unaffected), a prefix spanning many tiles with a chunk that
     ends inside a tile, and a chunk longer than one 128-row tile."""
@@ -102,11 +107,29 @@ def test_varlen_empty_sequence_and_long_prefix():
     lens_cached = [10, 20, 0, 1500, 129]
     lens_new = [3, 0, 70, 37, 200]
     args = _case(rng, lens_cached, lens_new, 8, 4, 128, 256)
-    say(f"varlen empty/long cached={lens_cached} new={lens_new}")
-    slots, kc, vc, got = _prefill(*args, 256)
+    say(f"varlen empty/long split={split} cached={lens_cached} new={lens_new}")
+    slots, kc, vc, got = _prefill(*args, 256, split)
     s_ref, kref, vref, ref = _reference(*args, 256)
     assert np.array_equal(slots, s_ref)
     assert np.array_equal(kc, kref) and np.array_equal(vc, vref)
+    err = np.abs(got - ref).max()
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_TOL
+
+
+def test_varlen_long_prefix_automatic_split():
+    """One sequence, 100 new tokens after a 6000-token cached prefix: only 8
+    row tiles, so the automatic choice splits the causal range (6 splits of
+    1024 positions) and merges."""
+    rng = np.random.default_rng(91)
+    lens_cached, lens_new = [6000], [100]
+    Hq, Hkv, D, bs = 8, 2, 128, 256
+    assert pkv.varlen_split_tokens(1, Hq, Hkv, 100, 6100) == 1024
+    args = _case(rng, lens_cached, lens_new, Hq, Hkv, D, bs)
+    say("varlen long prefix, automatic split")
+    slots, kc, vc, got = _prefill(*args, bs)
+    s_ref, kref, vref, ref = _reference(*args, bs)
+    assert np.array_equal(slots, s_ref)
     err = np.abs(got - ref).max()
     say(f"  max abs err {err:.3e}")
     assert err <= ATTN_TOL

@@ -34,10 +34,13 @@ class VarlenWorkload:
 
 # Qwen3-0.6B-shaped chunked prefill: 4 sequences, 512 new tokens each, after
 # cached prefixes of 0 / 256 / 1024 / 1536 tokens (GQA 16/8, D 128, block 256,
-# 28 layers).
+# 28 layers); and one long-prefix chunk (4 layers).
 VARLEN_WORKLOADS = [
     VarlenWorkload("qwen3_prefill", (0, 256, 1024, 1536), (512, 512, 512, 512), 16, 8, 128, 256,
                    28, 42 + 1000 * 6),
+    # one sequence, a 512-token chunk after a 16384-token cached prefix: only
+    # 64 (row tile, KV head) pairs, so the causal ranges are split
+    VarlenWorkload("qwen3_long_prefix", (16384,), (512,), 16, 8, 128, 256, 4, 42 + 1000 * 7),
 ]
 
 
