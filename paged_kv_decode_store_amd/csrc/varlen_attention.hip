@@ -6,8 +6,8 @@
 // [0, k_len - q_len + j].  Rows of the computation are (token, query head)
 // pairs of one KV head, token-major, so the GQA group's heads share every
 // K/V tile.  A workgroup owns 128 such rows of one sequence and KV head and
-// streams the whole causal range of its last token in tiles of KT
-// positions, staged through LDS.  Its eight waves form two groups of four
+// streams the causal range of its last token (or one split of it, below) in
+// tiles of KT positions, staged through LDS.  Its eight waves form two groups of four
 // (32 rows per wave) that take the even and the odd tiles, so each SIMD
 // runs two waves whose memory, LDS and matrix-core latencies overlap; the
 // two groups' softmax states are merged through LDS at the end.
@@ -144,10 +144,10 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     const int c = lane & 31;          // query of this lane (S^T / O^T column)
     const int h = lane >> 5;          // half of the contraction slots
 
-    // Longest causal ranges first: the grid's slowest index walks the row
-    // tiles from the last one.  Tiles of one (sequence, KV head) pair sit
-    // B*Hkv workgroups apart, i.e. on one XCD when B*Hkv % 8 == 0, so they
-    // share that XCD's L2 copy of the pair's K/V.
+    // Grid order (fastest first): (sequence, KV head) pair, row tile from
+    // the last one (longest causal range first), split.  Tiles of one pair
+    // sit B*Hkv workgroups apart, i.e. on one XCD when B*Hkv % 8 == 0, so
+    // they share that XCD's L2 copy of the pair's K/V.
     const int pairs = a.batch * a.num_kv_heads;
     const int pair = blockIdx.x % pairs;
     const int rest = (int)(blockIdx.x / pairs);
