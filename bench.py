@@ -91,7 +91,7 @@ def unique_positions(n, tables, bs):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

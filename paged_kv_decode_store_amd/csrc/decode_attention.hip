@@ -355,9 +355,10 @@ int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_conte
                           int32_t group)
 {
     // Measured on MI355X: the VALU partial kernel runs best with roughly
-    // 1-2k non-empty workgroups.  Rows are assumed half full on average, so
-    // the split aims at B * Hkv * max_len / 2 positions spread over ~2048
-    // workgroups (Qwen3-shaped: flat from 256 to 512 positions).  The
+    // 1-2k non-empty workgroups, about 9/32768 of B * Hkv * max_len
+    // positions each (Qwen3-shaped, 3 repeats each: 88.4 us per layer at
+    // 576 positions, 89.1 at 448, 90.5 at 512, 91.3 at 640, 92.2 at 768,
+    // 5.0 TB/s at 1024).  The
     // matrix-core kernel (group >= kMfmaMinGroup) holds only two or three
     // workgroups per CU and streams best with long splits: 3/8192 of
     // B * Hkv * max_len positions each, at least 1024 (Grok-shaped, one
@@ -366,7 +367,7 @@ int32_t auto_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_conte
     if (max_context_len <= 0 || batch <= 0 || num_kv_heads <= 0) return kRound;
     const bool mfma = group >= kMfmaMinGroup;
     const int64_t work = (int64_t)batch * num_kv_heads * max_context_len;
-    int64_t split = mfma ? work * 3 / 8192 : work / 4096;
+    int64_t split = mfma ? work * 3 / 8192 : work * 9 / 32768;
     const int64_t lo = mfma ? 1024 : 128;
     if (split < lo) split = lo;
     if (split > 8192) split = 8192;

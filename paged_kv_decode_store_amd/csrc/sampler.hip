@@ -874,7 +874,8 @@ __device__ unsigned long long kept_mass_in_bin(const RowScan &r, ResolveShared &
     return block_sum<unsigned long long, kRThreads>(m, sh.scan);
 }
 
-// Round 2 set-up: the nucleus cut of a top-k row lies above its top-k bin.
+// Second collect/resolve pass, set-up: the nucleus cut of a top-k row lies
+// above its top-k bin.
 // Every logit in bins above `jk` is in the top-k set, so the nucleus over
 // that set is found like a plain nucleus with total mass Zk.
 __device__ void setup_round2(const SampArgs &a, SampCtl *ctl, ResolveShared &sh, int b, int jk,
