@@ -3,12 +3,12 @@
 //
 // Row-parallel passes split each row into chunks of `chunk` logits, one
 // 256-thread workgroup per (chunk, row).  Each thread first loads its whole
-// share of the chunk into registers (float4 when rows are 16-byte aligned)
-// and recomputes s = z / T (IEEE division) and the order-preserving 32-bit
-// key of s.
+// share of the chunk into registers (float4 when rows are 16-byte aligned).
+// The scaled logit is s = z / T, an IEEE fp32 division; since that division
+// is monotone in z for T > 0, only the bins pass divides every logit.
 //
 // Rows with a top-k or nucleus filter take three passes over their logits:
-//   max     the row max M of s
+//   max     the row max M of s, as (max allowed z) / T
 //   bins    a histogram over 2048 value bins of width 1/32 below M
 //           (bin = floor(fl(M - s) * 32), the last bin catching everything
 //           >= 64 below M), with counts and the mass exp(s - M) in 2^-40
@@ -17,7 +17,10 @@
 //   collect every logit in a bin above the threshold bin is eligible: its
 //           Gumbel key fl32(s + g) joins a max of the packed 64-bit
 //           (key, ~index) (ties to the lowest index); the logits of the
-//           threshold bin itself are appended to a per-row candidate list
+//           threshold bin itself are appended to a per-row candidate list.
+//           Both classes are upper sets of z, so a logit is classified by
+//           two thresholds on z that `select` finds by bisection, and s is
+//           computed only for the logits that join the list.
 // and two per-row kernels: `select` finds the threshold bin from the
 // histogram, `resolve` ranks the candidates (by counting when there are at
 // most 512, else by a bitonic sort in LDS) and fixes the exact cut inside
@@ -54,6 +57,7 @@ constexpr int kList = 1024;             // compacted noise reads per collect wor
 constexpr uint32_t kCandBit = 0x80000000u;
 constexpr uint32_t kKeptBit = 0x40000000u;
 constexpr uint32_t kIndexMask = 0x3fffffffu;  // vocab < 2^30
+constexpr uint32_t kSlotMasked = 0x80000000u; // list entry of a forbidden logit
 
 enum : uint32_t {
     MODE_GREEDY = 1,     // T <= 0: lowest index of the max raw logit
@@ -180,6 +184,43 @@ __device__ __forceinline__ int bin_of(float s, float M)
     return d < (float)(kBins - 1) ? (int)d : kBins - 1;
 }
 
+// One wave: the smallest z, in key order over the non-NaN floats, at which a
+// monotone predicate (false below some z, true from there up) holds; -inf if
+// it holds everywhere, NaN if nowhere.  64 probes per step narrow the key
+// interval (lo, hi] about 64-fold, so a 32-bit key takes six steps.
+template <typename Pred>
+__device__ float wave_first_z(Pred pred)
+{
+    const float inf = __builtin_huge_valf();
+    if (pred(-inf)) return -inf;
+    if (!pred(inf)) return __builtin_nanf("");
+    uint32_t lo = float_key(-inf), hi = float_key(inf);  // pred(lo) false, pred(hi) true
+    const int lane = (int)threadIdx.x & 63;
+    while (hi - lo > 1u) {
+        const uint32_t probe = lo + (uint32_t)(((unsigned long long)(hi - lo) * (unsigned)(lane + 1)) >> 6);
+        const unsigned long long t = __ballot(pred(key_float(probe)));  // lane 63 probes hi: true
+        const int f = __builtin_ctzll(t);
+        const uint32_t nlo = (uint32_t)__shfl((int)probe, f > 0 ? f - 1 : 0);
+        hi = (uint32_t)__shfl((int)probe, f);
+        if (f > 0) lo = nlo;
+    }
+    return key_float(hi);
+}
+
+// Thresholds on the raw logit z equivalent to "bin of z / T below j"
+// (out[0]) and "bin of z / T at most j" (out[1]): division by T > 0 is
+// monotone and bin_of is monotone in s, so each class is an upper set of z.
+// (-0 and +0 fall in the same bin, so a float comparison with the threshold
+// decides as the bin does.)  Wave 0 finds the first, wave 1 the second.
+__device__ void z_thresholds(float T, float M, int j, float *out)
+{
+    const int w = (int)threadIdx.x >> 6;
+    if (w > 1) return;
+    const int lim = w == 0 ? j : j + 1;
+    const float z0 = wave_first_z([=](float z) { return bin_of(z / T, M) < lim; });
+    if ((threadIdx.x & 63) == 0) out[w] = z0;
+}
+
 // Block-wide reductions and scans: within each wave by lane shuffles, then
 // one exchange of the per-wave results through `scratch` (>= NT / 64
 // entries).  Every thread gets the result; `scratch` is free again on return.
@@ -280,8 +321,7 @@ struct Tile {
 #pragma unroll
             for (int q = 0; q < kMaxPer / 4; ++q) {
                 const int i = index(i0, 4 * q);
-                uint32_t w = 0x01010101u;
-                if (4 * q < per && i < i1) w = *reinterpret_cast<const uint32_t *>(mrow + i);
+                const uint32_t w = *reinterpret_cast<const uint32_t *>(mrow + ((4 * q < per && i < i1) ? i : i0));
 #pragma unroll
                 for (int k = 0; k < 4; ++k) bits |= (((w >> (8 * k)) & 0xffu) ? 1u : 0u) << (4 * q + k);
             }
@@ -289,7 +329,7 @@ struct Tile {
 #pragma unroll
             for (int j = 0; j < kMaxPer; ++j) {
                 const int i = index(i0, j);
-                const uint8_t m = (j < per && i < i1) ? mrow[i] : (uint8_t)1;
+                const uint8_t m = mrow[(j < per && i < i1) ? i : i0];
                 bits |= (m ? 1u : 0u) << j;
             }
         }
@@ -304,14 +344,24 @@ struct Tile {
             return i0 + j * kThreads + (int)threadIdx.x;
     }
 
+    // a chunk of kMaxPer logits per thread, all inside the row
+    __device__ __forceinline__ static bool full(int i0, int i1, int per)
+    {
+        return per == kMaxPer && i1 - i0 == kMaxPer * kThreads;
+    }
+
+    // Every load is issued, in one straight run: an element outside the chunk
+    // reads the chunk's first logits instead and is never used.  With no
+    // branch between the loads and their use, each use waits only for its
+    // own load.
     __device__ __forceinline__ void load(const float *__restrict__ row, int i0, int i1, int per)
     {
         if constexpr (VEC4) {
 #pragma unroll
             for (int q = 0; q < kMaxPer / 4; ++q) {
                 const int i = index(i0, 4 * q);
-                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (4 * q < per && i < i1) f = *reinterpret_cast<const float4 *>(row + i);
+                const int ic = (4 * q < per && i < i1) ? i : i0;
+                const float4 f = *reinterpret_cast<const float4 *>(row + ic);
                 v[4 * q] = f.x;
                 v[4 * q + 1] = f.y;
                 v[4 * q + 2] = f.z;
@@ -321,11 +371,26 @@ struct Tile {
 #pragma unroll
             for (int j = 0; j < kMaxPer; ++j) {
                 const int i = index(i0, j);
-                v[j] = (j < per && i < i1) ? row[i] : 0.f;
+                v[j] = row[(j < per && i < i1) ? i : i0];
             }
         }
     }
 };
+
+// Calls f(j) for each element j of this thread's share of the chunk
+// [i0, i1): without per-element range checks for a full chunk.
+template <bool VEC4, typename F>
+__device__ __forceinline__ void for_each_elem(int i0, int i1, int per, F f)
+{
+    if (Tile<VEC4>::full(i0, i1, per)) {
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) f(j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j)
+            if (j < per && Tile<VEC4>::index(i0, j) < i1) f(j);
+    }
+}
 
 // What a row needs, from its own settings and the enabled filters.
 __device__ __forceinline__ uint32_t row_mode(const SampArgs &a, int b)
@@ -374,10 +439,21 @@ __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
     }
     __shared__ uint32_t s_red[kThreads / 64];
     const float T = a.temperature[b];
-    uint32_t kmax = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j)
-        if (j < per && Tile<VEC4>::index(i0, j) < i1) kmax = max(kmax, float_key(t.scaled(j, T)));
+    // Division by T > 0 is monotone, so the largest s = z / T is the largest
+    // allowed z divided by T: one division per thread instead of per logit.
+    // Forbidden logits count as kMasked.
+    // The running max is a float select (a NaN z never wins it); float_key
+    // maps -0 and +0 to one key, so this equals the max over keys of s for
+    // every NaN-free row.
+    float zmax = -__builtin_huge_valf();
+    uint32_t seen = 0;  // bit j: element j is in the chunk
+    for_each_elem<VEC4>(i0, i1, per, [&](int j) {
+        const float z = ((t.ok >> j) & 1u) ? t.v[j] : -__builtin_huge_valf();
+        zmax = z > zmax ? z : zmax;
+        seen |= 1u << j;
+    });
+    uint32_t kmax = float_key(zmax / T);
+    if (~t.ok & seen) kmax = max(kmax, float_key(kMasked));
     kmax = block_max<uint32_t, kThreads>(kmax, s_red);
     if (threadIdx.x == 0) a.part_max[(int64_t)b * a.nchunks + blockIdx.x] = kmax;
 }
@@ -416,25 +492,25 @@ __global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
     }
     const float M = key_float(row_max_key<kThreads>(a, b, reinterpret_cast<uint32_t *>(s_red)));
     const bool want_mass = (mode & MODE_TOPP) != 0;
+    const bool want_cnt = (mode & MODE_TOPK) != 0;  // nucleus-only rows need masses alone
     unsigned long long zloc = 0;
     uint32_t tail = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-        if (j >= per || Tile<VEC4>::index(i0, j) >= i1) continue;
+    for_each_elem<VEC4>(i0, i1, per, [&](int j) {
         const float s = t.scaled(j, T);
         const int bin = bin_of(s, M);
-        if (bin == kBins - 1) {
-            // >= 64 below the max: mass exp(-64) is below the fixed-point unit
-            ++tail;
-            continue;
+        // >= 64 below the max (the last bin): counted per thread, its mass
+        // exp(-64) is below the fixed-point unit
+        const bool last = bin == kBins - 1;
+        tail += last ? 1u : 0u;
+        if (!last) {
+            if (want_cnt) atomicAdd(&s_cnt[bin], 1u);
+            if (want_mass) {
+                const unsigned long long w = mass_fixed(s, M);
+                atomicAdd(&s_mass[bin], w);
+                zloc += w;
+            }
         }
-        atomicAdd(&s_cnt[bin], 1u);
-        if (want_mass) {
-            const unsigned long long w = mass_fixed(s, M);
-            if (w) atomicAdd(&s_mass[bin], w);
-            zloc += w;
-        }
-    }
+    });
     __syncthreads();
     for (int d = threadIdx.x; d < kBins - 1; d += kThreads) {
         if (s_cnt[d]) atomicAdd(&a.cnt[(int64_t)b * kBins + d], s_cnt[d]);
@@ -465,19 +541,20 @@ __global__ __launch_bounds__(kRThreads) void samp_select_kernel(const SampArgs a
     if (threadIdx.x == 0) ctl->max_key = max_key;
     if (mode & MODE_TOPP_MAX) return;
     const int d0 = (int)threadIdx.x * BPT;
+    const bool topk = (mode & MODE_TOPK) != 0;
     uint32_t cnt[BPT];
     unsigned long long mass[BPT];
     unsigned long long own_c = 0, own_m = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-        cnt[j] = a.cnt[(int64_t)b * kBins + d0 + j];
+        cnt[j] = topk ? a.cnt[(int64_t)b * kBins + d0 + j] : 0u;
         mass[j] = a.mass[(int64_t)b * kBins + d0 + j];
         own_c += cnt[j];
         own_m += mass[j];
     }
-    unsigned long long above_c = block_scan_inclusive<unsigned long long, kRThreads>(own_c, s_red) - own_c;
     unsigned long long above_m = block_scan_inclusive<unsigned long long, kRThreads>(own_m, s_red) - own_m;
-    if (mode & MODE_TOPK) {
+    if (topk) {
+        unsigned long long above_c = block_scan_inclusive<unsigned long long, kRThreads>(own_c, s_red) - own_c;
         const unsigned long long k = ctl->k;
 #pragma unroll
         for (int j = 0; j < BPT; ++j) {
@@ -489,30 +566,33 @@ __global__ __launch_bounds__(kRThreads) void samp_select_kernel(const SampArgs a
             above_c += cnt[j];
             above_m += mass[j];
         }
-        return;
-    }
-    // nucleus only
-    const double limit = (double)a.top_p[b] * (double)ctl->Z;
-    long long cand = -1;
-    unsigned long long cand_above = 0;
+    } else {
+        // Nucleus only (no counts kept): a bin whose logits all have mass 0
+        // (below 2^-40 of the max's) has the whole Z above it, which exceeds
+        // p Z for p < 1, so the non-empty bins that can qualify are exactly
+        // those with mass.
+        const double limit = (double)a.top_p[b] * (double)ctl->Z;
+        long long cand = -1;
+        unsigned long long cand_above = 0;
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        if (cnt[j] && (double)above_m <= limit) {
-            cand = d0 + j;
-            cand_above = above_m;
+        for (int j = 0; j < BPT; ++j) {
+            if (mass[j] && (double)above_m <= limit) {
+                cand = d0 + j;
+                cand_above = above_m;
+            }
+            above_m += mass[j];
         }
-        above_m += mass[j];
-    }
-    const long long best = block_max<long long, kRThreads>(cand, reinterpret_cast<long long *>(s_red));
-    if (cand >= 0 && cand == best) {
-        ctl->jstar = (uint32_t)cand;
-        ctl->A = cand_above;
+        const long long best = block_max<long long, kRThreads>(cand, reinterpret_cast<long long *>(s_red));
+        if (cand >= 0 && cand == best) {
+            ctl->jstar = (uint32_t)cand;
+            ctl->A = cand_above;
+        }
     }
 }
 
 // Eligible logits above the threshold bin join the Gumbel argmax; logits of
 // the threshold bin are appended to the candidate list.  The noise is read
-// only where it is needed: the (index, s) pairs that need it are compacted
+// only where it is needed: the (index, z) pairs that need it are compacted
 // in LDS and their noise fetched together, kList pairs per round.  ROUND2:
 // only rows waiting for a second round work.
 template <bool VEC4, bool ROUND2>
@@ -536,24 +616,19 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
     t.load_mask(a.mask ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
     unsigned long long best = 0;
     if (mode & MODE_GREEDY) {
-#pragma unroll
-        for (int j = 0; j < kMaxPer; ++j) {
-            const int i = Tile<VEC4>::index(i0, j);
-            if (j < per && i < i1) best = max(best, pack_key_index(float_key(t.raw(j)), (uint32_t)i));
-        }
+        for_each_elem<VEC4>(i0, i1, per, [&](int j) {
+            const uint32_t i = (uint32_t)Tile<VEC4>::index(i0, j);
+            best = max(best, pack_key_index(float_key(t.raw(j)), i));
+        });
     } else if (mode & MODE_PLAIN) {
         // every logit is eligible: stream the noise as a tile too
         const float T = a.temperature[b];
         Tile<VEC4> gt;
         gt.load(g, i0, i1, per);
-#pragma unroll
-        for (int j = 0; j < kMaxPer; ++j) {
-            const int i = Tile<VEC4>::index(i0, j);
-            if (j < per && i < i1) {
-                const float kappa = t.scaled(j, T) + gt.v[j];
-                best = max(best, pack_key_index(float_key(kappa), (uint32_t)i));
-            }
-        }
+        for_each_elem<VEC4>(i0, i1, per, [&](int j) {
+            const float kappa = t.scaled(j, T) + gt.v[j];
+            best = max(best, pack_key_index(float_key(kappa), (uint32_t)Tile<VEC4>::index(i0, j)));
+        });
     } else {
         const float T = a.temperature[b];
         const uint32_t max_key = ctl->max_key;
@@ -561,23 +636,38 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
         const int jstar = (int)ctl->jstar;
         const bool maxima = (mode & MODE_TOPP_MAX) != 0;
         uint32_t kept = 0, incand = 0;
+        if (maxima) {
+            // p <= 0: the logits whose s equals the row max (t.v becomes s)
 #pragma unroll
-        for (int j = 0; j < kMaxPer; ++j) {
-            const int i = Tile<VEC4>::index(i0, j);
-            const float s = t.scaled(j, T);
-            bool ok = false, c = false;
-            if (j < per && i < i1) {
-                if (maxima) {
-                    ok = float_key(s) == max_key;
-                } else {
-                    const int bin = bin_of(s, M);
-                    ok = bin < jstar;
-                    c = bin == jstar;
-                }
+            for (int j = 0; j < kMaxPer; ++j) {
+                const float s = t.scaled(j, T);
+                const bool ok = j < per && Tile<VEC4>::index(i0, j) < i1 && float_key(s) == max_key;
+                t.v[j] = s;
+                kept |= (ok ? 1u : 0u) << j;
             }
-            t.v[j] = s;
-            kept |= (ok ? 1u : 0u) << j;
-            incand |= (c ? 1u : 0u) << j;
+        } else {
+            // The class of an allowed logit follows from z itself, so z / T
+            // is computed only for the logits that go to the list (t.v stays
+            // z).  The two thresholds are found while the tile loads are in
+            // flight.  Forbidden logits (s = kMasked) and NaN ones (bin
+            // kBins - 1) take their bin's class.
+            __shared__ float s_zt[2];
+            z_thresholds(T, M, jstar, s_zt);
+            __syncthreads();
+            const float z_elig = s_zt[0], z_cand = s_zt[1];
+            const int bm = bin_of(kMasked, M);
+            const bool ok_m = bm < jstar, c_m = bm == jstar;
+            const bool ok_n = kBins - 1 < jstar, c_n = kBins - 1 == jstar;
+            for_each_elem<VEC4>(i0, i1, per, [&](int j) {
+                const float z = t.v[j];
+                const bool allowed = (t.ok >> j) & 1u;
+                const bool nan = !(z == z);
+                const bool ge_elig = z >= z_elig, ge_cand = z >= z_cand;
+                const bool ok = !allowed ? ok_m : (nan ? ok_n : ge_elig);
+                const bool c = !allowed ? c_m : (nan ? c_n : (!ge_elig && ge_cand));
+                kept |= (ok ? 1u : 0u) << j;
+                incand |= (c ? 1u : 0u) << j;
+            });
         }
         const uint32_t need = kept | incand;
         const uint32_t nc = __popc(incand), nn = __popc(need);
@@ -585,60 +675,81 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
         // both totals stay below 2^16
         const uint32_t incl = block_scan_inclusive<uint32_t, kThreads>((nc << 16) | nn,
                                                                        reinterpret_cast<uint32_t *>(s_red));
+        // The last thread claims the workgroup's candidate slots; the claim's
+        // result is needed only when the candidates are written, so its
+        // latency overlaps the list building and the noise reads.
+        uint32_t claimed = 0;
         if (threadIdx.x == kThreads - 1) {
             s_tot = incl;
-            if (incl >> 16) s_base = atomicAdd(&ctl->ncand, incl >> 16);
+            if (incl >> 16) claimed = atomicAdd(&ctl->ncand, incl >> 16);
         }
         __syncthreads();
-        const uint32_t tot = s_tot;
-        const uint32_t tot_n = tot & 0xffffu;
-        uint32_t slot = ((tot >> 16) ? s_base : 0u) + (incl >> 16) - nc;
+        const uint32_t tot_n = s_tot & 0xffffu;
         unsigned long long *cand = a.cand + (int64_t)b * kCap;
         uint32_t *kap = a.kap + (int64_t)b * kCap;
-        // rounds of at most kList list entries: each thread's entries hold
-        // the consecutive list positions [pos0, pos0 + nn)
-        const uint32_t pos0 = (incl & 0xffffu) - nn;
-        for (uint32_t base = 0; base < tot_n; base += (uint32_t)kList) {
-            if (base) __syncthreads();  // the previous round's entries are consumed
-            uint32_t pos = pos0, sl = slot;
+        // s of a listed logit: z / T, or kMasked (the maxima rows hold s)
+        auto scaled_entry = [&](float v, bool masked) {
+            return maxima ? v : (masked ? kMasked : v / T);
+        };
+        // candidate `lc` of this workgroup: its key and Gumbel key go to slot cbase + lc
+        auto put_cand = [&](uint32_t cs, float sv, uint32_t kk, uint32_t i) {
+            if (cs < (uint32_t)kCap) {
+                cand[cs] = pack_key_index(float_key(sv), i);
+                kap[cs] = kk;
+            }
+        };
+        uint32_t lc = (incl >> 16) - nc;  // this thread's first candidate, within the workgroup
+        if (tot_n <= (uint32_t)kList) {
+            // one list: this thread's entries take positions [pos0, pos0 + nn)
+            uint32_t pos = (incl & 0xffffu) - nn;
 #pragma unroll
             for (int j = 0; j < kMaxPer; ++j) {
                 if (!((need >> j) & 1u)) continue;
                 const bool c = (incand >> j) & 1u;
-                if (pos - base < (uint32_t)kList) {
-                    const uint32_t i = (uint32_t)Tile<VEC4>::index(i0, j);
-                    s_idx[pos - base] = i | (c ? kCandBit : 0u) | (((kept >> j) & 1u) ? kKeptBit : 0u);
-                    s_s[pos - base] = t.v[j];
-                    s_slot[pos - base] = sl;
-                }
+                const uint32_t i = (uint32_t)Tile<VEC4>::index(i0, j);
+                s_idx[pos] = i | (c ? kCandBit : 0u) | (((kept >> j) & 1u) ? kKeptBit : 0u);
+                s_s[pos] = t.v[j];
+                s_slot[pos] = lc | (((t.ok >> j) & 1u) ? 0u : kSlotMasked);
                 ++pos;
-                sl += c ? 1u : 0u;
+                lc += c ? 1u : 0u;
             }
             __syncthreads();
-            const uint32_t cnt = min((uint32_t)kList, tot_n - base);
             constexpr int R = kList / kThreads;
             float gv[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const uint32_t q = (uint32_t)(r * kThreads) + threadIdx.x;
-                gv[r] = q < cnt ? g[s_idx[q] & kIndexMask] : 0.f;
+                gv[r] = q < tot_n ? g[s_idx[q] & kIndexMask] : 0.f;
             }
+            if (threadIdx.x == kThreads - 1) s_base = claimed;
+            __syncthreads();
+            const uint32_t cbase = s_base;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const uint32_t q = (uint32_t)(r * kThreads) + threadIdx.x;
-                if (q >= cnt) continue;
+                if (q >= tot_n) continue;
                 const uint32_t e = s_idx[q];
                 const uint32_t i = e & kIndexMask;
-                const float sv = s_s[q];
+                const uint32_t sq = s_slot[q];
+                const float sv = scaled_entry(s_s[q], (sq & kSlotMasked) != 0);
                 const uint32_t kk = float_key(sv + gv[r]);
                 if (e & kKeptBit) best = max(best, pack_key_index(kk, i));
-                if (e & kCandBit) {
-                    const uint32_t cs = s_slot[q];
-                    if (cs < (uint32_t)kCap) {
-                        cand[cs] = pack_key_index(float_key(sv), i);
-                        kap[cs] = kk;
-                    }
-                }
+                if (e & kCandBit) put_cand(cbase + (sq & ~kSlotMasked), sv, kk, i);
+            }
+        } else {
+            // more entries than the list holds: each thread reads the noise
+            // of its own entries
+            if (threadIdx.x == kThreads - 1) s_base = claimed;
+            __syncthreads();
+            const uint32_t cbase = s_base;
+#pragma unroll
+            for (int j = 0; j < kMaxPer; ++j) {
+                if (!((need >> j) & 1u)) continue;
+                const uint32_t i = (uint32_t)Tile<VEC4>::index(i0, j);
+                const float sv = scaled_entry(t.v[j], !((t.ok >> j) & 1u));
+                const uint32_t kk = float_key(sv + g[i]);
+                if ((kept >> j) & 1u) best = max(best, pack_key_index(kk, i));
+                if ((incand >> j) & 1u) put_cand(cbase + lc++, sv, kk, i);
             }
         }
     }
