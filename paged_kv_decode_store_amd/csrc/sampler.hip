@@ -146,6 +146,26 @@ struct SampArgs {
 // The runner's value for forbidden tokens (their scaled logit is replaced).
 constexpr float kMasked = -1e10f;
 
+// s = z / T, the IEEE fp32 quotient, by one double product: fl64(z) *
+// fl64(1 / T) is within 2^-52 (relative) of z / T, while the quotient of two
+// fp32 numbers, when not exactly an fp32 number, lies more than 2^-49
+// (relative) from every fp32 rounding boundary, except for a tie in the
+// subnormal range.  Rounding the product to fp32 therefore gives the
+// correctly rounded quotient for every |z| >= 2^-125 T; below that the
+// division itself runs (a branch that real logits essentially never take).
+// Every place that computes s this way or by division gets the same value.
+struct Scaler {
+    float T, tiny;
+    double inv;
+    __device__ explicit Scaler(float t) : T(t), tiny(t * 0x1p-125f), inv(1.0 / (double)t) {}
+    __device__ __forceinline__ float operator()(float z) const
+    {
+        float s = (float)((double)z * inv);
+        if (__builtin_expect(fabsf(z) < tiny, 0)) s = z / T;
+        return s;
+    }
+};
+
 __device__ __forceinline__ unsigned long long pack_key_index(uint32_t key, uint32_t i)
 {
     return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - i);
@@ -305,9 +325,9 @@ struct Tile {
     uint32_t ok = 0xffffffffu;  // bit j: element j is allowed by the mask
 
     // s of element j: z / T, or kMasked where the mask forbids it
-    __device__ __forceinline__ float scaled(int j, float T) const
+    __device__ __forceinline__ float scaled(int j, const Scaler &sc) const
     {
-        return ((ok >> j) & 1u) ? v[j] / T : kMasked;
+        return ((ok >> j) & 1u) ? sc(v[j]) : kMasked;
     }
     // greedy value of element j: the raw logit, or kMasked
     __device__ __forceinline__ float raw(int j) const { return ((ok >> j) & 1u) ? v[j] : kMasked; }
@@ -356,9 +376,16 @@ struct Tile {
     // own load.
     __device__ __forceinline__ void load(const float *__restrict__ row, int i0, int i1, int per)
     {
+        load_range<0, kMaxPer>(row, i0, i1, per);
+    }
+
+    // elements [J0, J0 + NJ) only (multiples of 4)
+    template <int J0, int NJ>
+    __device__ __forceinline__ void load_range(const float *__restrict__ row, int i0, int i1, int per)
+    {
         if constexpr (VEC4) {
 #pragma unroll
-            for (int q = 0; q < kMaxPer / 4; ++q) {
+            for (int q = J0 / 4; q < (J0 + NJ) / 4; ++q) {
                 const int i = index(i0, 4 * q);
                 const int ic = (4 * q < per && i < i1) ? i : i0;
                 const float4 f = *reinterpret_cast<const float4 *>(row + ic);
@@ -369,7 +396,7 @@ struct Tile {
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < kMaxPer; ++j) {
+            for (int j = J0; j < J0 + NJ; ++j) {
                 const int i = index(i0, j);
                 v[j] = row[(j < per && i < i1) ? i : i0];
             }
@@ -411,7 +438,7 @@ __device__ __forceinline__ uint32_t row_mode(const SampArgs &a, int b)
 // First pass of filtered sampling: per-chunk max of s.  Chunk 0 of each row
 // also sets up the row's control block, and the chunks of a filtered row
 // clear its histogram between them.
-template <bool VEC4>
+template <bool VEC4, bool MASK>
 __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
@@ -421,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
     // issued before the row's settings are known, so that the two overlap
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
-    t.load_mask(a.mask ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
+    t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
     const uint32_t mode = row_mode(a, b);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         SampCtl c = {};
@@ -469,7 +496,7 @@ __device__ uint32_t row_max_key(const SampArgs &a, int b, uint32_t *scratch)
 }
 
 // Counts (and, for the nucleus, masses) per value bin below the row max.
-template <bool VEC4>
+template <bool VEC4, bool MASK>
 __global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
@@ -479,13 +506,14 @@ __global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
     const int per = a.chunk / kThreads;
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
-    t.load_mask(a.mask ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
+    t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
     const uint32_t mode = ctl->mode;
     if (!(mode & (MODE_TOPK | MODE_TOPP))) return;
     __shared__ uint32_t s_cnt[kBins];
     __shared__ unsigned long long s_mass[kBins];
     __shared__ unsigned long long s_red[kThreads / 64];
     const float T = a.temperature[b];
+    const Scaler sc(T);
     for (int d = threadIdx.x; d < kBins; d += kThreads) {
         s_cnt[d] = 0;
         s_mass[d] = 0;
@@ -496,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
     unsigned long long zloc = 0;
     uint32_t tail = 0;
     for_each_elem<VEC4>(i0, i1, per, [&](int j) {
-        const float s = t.scaled(j, T);
+        const float s = t.scaled(j, sc);
         const int bin = bin_of(s, M);
         // >= 64 below the max (the last bin): counted per thread, its mass
         // exp(-64) is below the fixed-point unit
@@ -595,13 +623,12 @@ __global__ __launch_bounds__(kRThreads) void samp_select_kernel(const SampArgs a
 // only where it is needed: the (index, z) pairs that need it are compacted
 // in LDS and their noise fetched together, kList pairs per round.  ROUND2:
 // only rows waiting for a second round work.
-template <bool VEC4, bool ROUND2>
+template <bool VEC4, bool MASK, bool ROUND2>
 __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
     SampCtl *ctl = a.ctl + b;
     if (ROUND2 && !ctl->round2) return;
-    const uint32_t mode = a.flags ? ctl->mode : row_mode(a, b);
     __shared__ unsigned long long s_red[kThreads / 64];
     __shared__ uint32_t s_tot, s_base;
     __shared__ uint32_t s_idx[kList];   // index | kCandBit
@@ -611,9 +638,12 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
     const int i1 = min(a.vocab, i0 + a.chunk);
     const int per = a.chunk / kThreads;
     const float *g = a.gumbel + (int64_t)b * a.gstride;
+    // the tile is requested before the row's settings are read, so that
+    // the two overlap
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
-    t.load_mask(a.mask ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
+    t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
+    const uint32_t mode = a.flags ? ctl->mode : row_mode(a, b);
     unsigned long long best = 0;
     if (mode & MODE_GREEDY) {
         for_each_elem<VEC4>(i0, i1, per, [&](int j) {
@@ -621,29 +651,44 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
             best = max(best, pack_key_index(float_key(t.raw(j)), i));
         });
     } else if (mode & MODE_PLAIN) {
-        // every logit is eligible: stream the noise as a tile too
+        // every logit is eligible: stream the noise as a tile too, half a
+        // tile at a time (fewer registers live)
         const float T = a.temperature[b];
+        const Scaler sc(T);
         Tile<VEC4> gt;
-        gt.load(g, i0, i1, per);
+        auto first_half = [&](int j) {
+            if (j >= kMaxPer / 2) return;
+            const float kappa = t.scaled(j, sc) + gt.v[j];
+            best = max(best, pack_key_index(float_key(kappa), (uint32_t)Tile<VEC4>::index(i0, j)));
+        };
+        gt.template load_range<0, kMaxPer / 2>(g, i0, i1, per);
+        for_each_elem<VEC4>(i0, i1, per, first_half);
+        gt.template load_range<kMaxPer / 2, kMaxPer / 2>(g, i0, i1, per);
         for_each_elem<VEC4>(i0, i1, per, [&](int j) {
-            const float kappa = t.scaled(j, T) + gt.v[j];
+            if (j < kMaxPer / 2) return;
+            const float kappa = t.scaled(j, sc) + gt.v[j];
             best = max(best, pack_key_index(float_key(kappa), (uint32_t)Tile<VEC4>::index(i0, j)));
         });
     } else {
         const float T = a.temperature[b];
+        const Scaler sc(T);
         const uint32_t max_key = ctl->max_key;
         const float M = key_float(max_key);
         const int jstar = (int)ctl->jstar;
         const bool maxima = (mode & MODE_TOPP_MAX) != 0;
         uint32_t kept = 0, incand = 0;
+        // The class bits are shifted in from the top element down, one
+        // dependent step each, so no element's bit waits in a register of
+        // its own.
+        const bool full = Tile<VEC4>::full(i0, i1, per);
         if (maxima) {
             // p <= 0: the logits whose s equals the row max (t.v becomes s)
 #pragma unroll
-            for (int j = 0; j < kMaxPer; ++j) {
-                const float s = t.scaled(j, T);
-                const bool ok = j < per && Tile<VEC4>::index(i0, j) < i1 && float_key(s) == max_key;
+            for (int j = kMaxPer - 1; j >= 0; --j) {
+                const bool in = full | ((j < per) & (Tile<VEC4>::index(i0, j) < i1));
+                const float s = t.scaled(j, sc);
                 t.v[j] = s;
-                kept |= (ok ? 1u : 0u) << j;
+                kept = (kept << 1) | ((in & (float_key(s) == max_key)) ? 1u : 0u);
             }
         } else {
             // The class of an allowed logit follows from z itself, so z / T
@@ -658,16 +703,18 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
             const int bm = bin_of(kMasked, M);
             const bool ok_m = bm < jstar, c_m = bm == jstar;
             const bool ok_n = kBins - 1 < jstar, c_n = kBins - 1 == jstar;
-            for_each_elem<VEC4>(i0, i1, per, [&](int j) {
+#pragma unroll
+            for (int j = kMaxPer - 1; j >= 0; --j) {
+                const bool in = full | ((j < per) & (Tile<VEC4>::index(i0, j) < i1));
                 const float z = t.v[j];
                 const bool allowed = (t.ok >> j) & 1u;
                 const bool nan = !(z == z);
                 const bool ge_elig = z >= z_elig, ge_cand = z >= z_cand;
                 const bool ok = !allowed ? ok_m : (nan ? ok_n : ge_elig);
-                const bool c = !allowed ? c_m : (nan ? c_n : (!ge_elig && ge_cand));
-                kept |= (ok ? 1u : 0u) << j;
-                incand |= (c ? 1u : 0u) << j;
-            });
+                const bool c = !allowed ? c_m : (nan ? c_n : (!ge_elig & ge_cand));
+                kept = (kept << 1) | ((in & ok) ? 1u : 0u);
+                incand = (incand << 1) | ((in & c) ? 1u : 0u);
+            }
         }
         const uint32_t need = kept | incand;
         const uint32_t nc = __popc(incand), nn = __popc(need);
@@ -1382,19 +1429,21 @@ __global__ __launch_bounds__(kRThreads) void samp_extras_kernel(const SampArgs a
     }
 }
 
-template <bool VEC4>
+// MASK: a vocabulary mask is given (without one, the row-parallel passes
+// are compiled with every logit allowed).
+template <bool VEC4, bool MASK>
 void launch_passes(const SampArgs &a, const dim3 grid, uint32_t flags, hipStream_t stream)
 {
     if (flags) {
-        samp_max_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
-        samp_bins_kernel<VEC4><<<grid, kThreads, 0, stream>>>(a);
+        samp_max_kernel<VEC4, MASK><<<grid, kThreads, 0, stream>>>(a);
+        samp_bins_kernel<VEC4, MASK><<<grid, kThreads, 0, stream>>>(a);
         samp_select_kernel<<<a.batch, kRThreads, 0, stream>>>(a);
     }
-    samp_collect_kernel<VEC4, false><<<grid, kThreads, 0, stream>>>(a);
+    samp_collect_kernel<VEC4, MASK, false><<<grid, kThreads, 0, stream>>>(a);
     samp_resolve_kernel<false><<<a.batch, kRThreads, 0, stream>>>(a);
     if ((flags & 3u) == 3u) {
         // top-k then nucleus: rows whose nucleus cut lies above their top-k bin
-        samp_collect_kernel<VEC4, true><<<grid, kThreads, 0, stream>>>(a);
+        samp_collect_kernel<VEC4, MASK, true><<<grid, kThreads, 0, stream>>>(a);
         samp_resolve_kernel<true><<<a.batch, kRThreads, 0, stream>>>(a);
     }
     if (a.out_prob || a.out_top_ids || a.out_top_probs)
@@ -1451,9 +1500,11 @@ hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_
                       (!mask || (reinterpret_cast<uintptr_t>(mask) % 4 == 0 && mask_stride % 4 == 0)) &&
                       vocab % 4 == 0;
     if (vec4)
-        launch_passes<true>(a, grid, flags, stream);
+        a.mask ? launch_passes<true, true>(a, grid, flags, stream)
+               : launch_passes<true, false>(a, grid, flags, stream);
     else
-        launch_passes<false>(a, grid, flags, stream);
+        a.mask ? launch_passes<false, true>(a, grid, flags, stream)
+               : launch_passes<false, false>(a, grid, flags, stream);
     return hipGetLastError();
 }
 

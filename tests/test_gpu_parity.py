@@ -492,3 +492,28 @@ def test_sampler_random_mixed_settings(seed):
     bad, amb, _ = _sample_and_compare(z, g, t, p, k)
     assert not bad, bad
     assert amb <= 1
+
+
+def test_sampler_subnormal_scaled_logits():
+    """Scaled logits z / T in and around the fp32 subnormal range (where the
+    kernels divide instead of rounding a double product), huge and tiny
+    temperatures, and many equal scaled values (ties go to the lowest
+    index)."""
+    rng = np.random.default_rng(61)
+    B, V = 6, 20000
+    tiny = np.float32(2.0 ** -149)
+    z = np.empty((B, V), np.float32)
+    z[0] = rng.integers(-2000, 2000, V).astype(np.float32) * tiny
+    z[1] = rng.integers(-50, 50, V).astype(np.float32) * tiny
+    z[2] = rng.standard_normal(V, dtype=np.float32)
+    z[3] = rng.standard_normal(V, dtype=np.float32) * np.float32(1e-38)
+    z[4] = rng.standard_normal(V, dtype=np.float32) * 3
+    z[4, ::3] = rng.integers(-9, 9, len(z[4, ::3])).astype(np.float32) * tiny
+    z[5] = rng.standard_normal(V, dtype=np.float32)
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = np.array([10.0, 6.0, 3e38, 0.5, 10.0, 1e-30], np.float32)
+    p = np.array([1.0, 1.0, 1.0, 1.0, 0.95, 1.0], np.float32)
+    k = np.array([50, 100, 1000, 10, 0, 0], np.int32)
+    bad, amb, infos = _sample_and_compare(z, g, t, p, k)
+    assert not bad, bad
+    assert [i.kept for i in infos[:4]] == k[:4].tolist()
