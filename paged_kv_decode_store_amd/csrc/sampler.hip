@@ -504,6 +504,12 @@ __global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
     const int i0 = blockIdx.x * a.chunk;
     const int i1 = min(a.vocab, i0 + a.chunk);
     const int per = a.chunk / kThreads;
+    // The chunk maxima are requested before the tile: loads complete in
+    // order, so waiting for them then does not wait for the tile, whose
+    // elements are used as they arrive.  (Clamped, not range-checked: a
+    // repeated maximum changes no max.)
+    const uint32_t *pm = a.part_max + (int64_t)b * a.nchunks;
+    uint32_t kpm = pm[min((int)threadIdx.x, a.nchunks - 1)];
     Tile<VEC4> t;
     t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
     t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
@@ -518,7 +524,8 @@ __global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
         s_cnt[d] = 0;
         s_mass[d] = 0;
     }
-    const float M = key_float(row_max_key<kThreads>(a, b, reinterpret_cast<uint32_t *>(s_red)));
+    for (int c = threadIdx.x + kThreads; c < a.nchunks; c += kThreads) kpm = max(kpm, pm[c]);
+    const float M = key_float(block_max<uint32_t, kThreads>(kpm, reinterpret_cast<uint32_t *>(s_red)));
     const bool want_mass = (mode & MODE_TOPP) != 0;
     const bool want_cnt = (mode & MODE_TOPK) != 0;  // nucleus-only rows need masses alone
     unsigned long long zloc = 0;
@@ -565,18 +572,26 @@ __global__ __launch_bounds__(kRThreads) void samp_select_kernel(const SampArgs a
     const uint32_t mode = ctl->mode;
     if (!(mode & (MODE_TOPK | MODE_TOPP | MODE_TOPP_MAX))) return;
     __shared__ unsigned long long s_red[kRThreads / 64];
-    const uint32_t max_key = row_max_key<kRThreads>(a, b, reinterpret_cast<uint32_t *>(s_red));
-    if (threadIdx.x == 0) ctl->max_key = max_key;
-    if (mode & MODE_TOPP_MAX) return;
+    // The histogram is requested before the row max is reduced, so that the
+    // two round trips overlap; both arrays are read unconditionally (a
+    // branch at a load makes the compiler wait for it), the counts are used
+    // by top-k rows only and neither by p <= 0 rows.
     const int d0 = (int)threadIdx.x * BPT;
     const bool topk = (mode & MODE_TOPK) != 0;
     uint32_t cnt[BPT];
     unsigned long long mass[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        cnt[j] = a.cnt[(int64_t)b * kBins + d0 + j];
+        mass[j] = a.mass[(int64_t)b * kBins + d0 + j];
+    }
+    const uint32_t max_key = row_max_key<kRThreads>(a, b, reinterpret_cast<uint32_t *>(s_red));
+    if (threadIdx.x == 0) ctl->max_key = max_key;
+    if (mode & MODE_TOPP_MAX) return;
     unsigned long long own_c = 0, own_m = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-        cnt[j] = topk ? a.cnt[(int64_t)b * kBins + d0 + j] : 0u;
-        mass[j] = a.mass[(int64_t)b * kBins + d0 + j];
+        if (!topk) cnt[j] = 0;
         own_c += cnt[j];
         own_m += mass[j];
     }
