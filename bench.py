@@ -242,9 +242,11 @@ def main():
             if with_reduce:
                 reduce()
 
-    def graph_time_ms(fn):
-        """Capture R consecutive calls fn(c), c = 0..R-1 (one per pool copy),
-        as one HIP graph; return the replayed time per call in ms."""
+    def graph_time_ms(fn, ncalls=None):
+        """Capture R consecutive calls fn(c), c = 0..R-1 (one per pool copy;
+        `ncalls` of them if given), as one HIP graph; return the replayed time
+        per call in ms."""
+        nc = R if ncalls is None else ncalls
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -253,19 +255,19 @@ def main():
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for c in range(R):
+            for c in range(nc):
                 fn(c)
-        for _ in range(max(1, args.warmup // R)):
+        for _ in range(max(1, args.warmup // nc)):
             graph.replay()
         torch.cuda.synchronize()
-        reps = max(1, args.steps // R)
+        reps = max(1, args.steps // nc)
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
         for _ in range(reps):
             graph.replay()
         g1.record()
         torch.cuda.synchronize()
-        return g0.elapsed_time(g1) / (reps * R)
+        return g0.elapsed_time(g1) / (reps * nc)
 
     # HIP-graph replay, as a serving engine runs a decode step: removes the
     # host launch gaps between kernels.  Three graphs: the whole step, the
@@ -277,6 +279,20 @@ def main():
         graph_part_us = 1e3 * graph_time_ms(lambda c: attention_only(c, with_reduce=False)) / L
         log(f"[bench] graph replays: {graph_ms_per_step:.4f} ms per step, attention "
             f"{graph_attn_us:.2f} us per layer, partial {graph_part_us:.2f} us per launch")
+    # The sampler alone as a graph replay (as the step graph runs it), over
+    # enough copies of the logits (up to 64) that each draw reads its logits
+    # from HBM as it would after a step's attention.
+    graph_samp_us = None
+    samp_copies = 1
+    if not args.no_graph:
+        samp_copies = int(min(64, max(1, -(-(1 << 30) // (logits.numel() * 4)))))
+        lcopies = [logits] + [logits.clone() for _ in range(samp_copies - 1)]
+        graph_samp_us = 1e3 * graph_time_ms(
+            lambda c: pkv.sample_next_token(lcopies[c], gumbel, t, p, k, flags=flags, out=ids,
+                                            workspace=sws), ncalls=samp_copies)
+        del lcopies
+        log(f"[bench] sampler graph replay: {graph_samp_us:.2f} us per draw "
+            f"({samp_copies} logits copies)")
     warm_attn_us = None
     if R > 1 and not args.no_graph:
         # the same pools every time: what a cache-resident workload reaches
@@ -298,7 +314,8 @@ def main():
     part_bytes = kv_bytes + q_bytes + store_bytes
     part_gbs = part_bytes / (part_avg_us * 1e-6) / 1e9
     ms_per_step = graph_ms_per_step if graph_ms_per_step is not None else eager_ms_per_step
-    samp_avg_us = 1e3 * float(np.mean(samp_ms))
+    samp_eager_us = 1e3 * float(np.mean(samp_ms))
+    samp_avg_us = graph_samp_us if graph_samp_us is not None else samp_eager_us
     traffic = read_traffic(cfg.name, fused)
 
     cpu = None
@@ -341,6 +358,9 @@ def main():
         "attention_timing": "hip_graph_replay" if graph_attn_us is not None else "hip_events",
         "eager_event_us_per_layer": {"partial": round(part_ev_us, 3), "reduce": round(red_ev_us, 3)},
         "sampler_us": round(samp_avg_us, 3),
+        "sampler_timing": (f"hip_graph_replay over {samp_copies} logits copies"
+                           if graph_samp_us is not None else "hip_events in the eager step"),
+        "sampler_us_eager_step": round(samp_eager_us, 3),
         "kv_bytes_per_layer": {"unique": kv_bytes, "logical": kv_logical},
         "logical_GBps": round((kv_logical + q_bytes + o_bytes) / (attn_us_layer * 1e-6) / 1e9, 2),
         "cache": {"pool_copies_cycled": R,
