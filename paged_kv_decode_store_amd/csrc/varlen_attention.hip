@@ -39,7 +39,8 @@
 // lazy: the reference max only moves when a row's max exceeds it by more
 // than 2^8 in probability (or on the first tile), so the exponentials stay
 // bounded by 256 and the rescale is rare.  P enters the product rounded to
-// bf16, the softmax sum uses the unrounded values.
+// bf16, and the softmax sum adds the same rounded values (packed dot
+// products with (1, 1)), so numerator and denominator use one P.
 #include <math.h>
 
 #include "launch.hpp"
@@ -287,12 +288,14 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     };
 
     // LDS operand addresses (bytes from a stage's start): K row 32kb + c,
-    // dims 8(2w + h); V^T row 32j + c, position-pair columns 8u + 2h (+4)
+    // dims 8(2w + h); V^T row 32j + c, position-pair columns
+    // (8u + 2h + 4e) ^ (V_XOR j).  The swizzle touches bits 2-3 of the word
+    // column and 2h only bit 1, so the column is ((8u + 4e) ^ (V_XOR j)) +
+    // 2h: a per-lane base plus a constant, i.e. an immediate offset.
     const int k_lds = (c * T::K_RS + 8 * h) * 2;
+    const int v_lane = T::K_BYTES + (c * T::V_RS + 2 * h) * 4;
     auto v_lds = [&](int j, int u, int e) -> int {
-        const int row = 32 * j + c;
-        const int col = (8 * u + 2 * h + 4 * e) ^ (T::V_XOR * j);
-        return T::K_BYTES + (row * T::V_RS + col) * 4;
+        return v_lane + (32 * j * T::V_RS + ((8 * u + 4 * e) ^ (T::V_XOR * j))) * 4;
     };
 
     f16_t o[NOB];
@@ -384,22 +387,27 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
                 float p[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sts[kb][i], cs, -mc));
-                float s8[8];
+                u4_t pw[2];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) s8[i] = p[2 * i] + p[2 * i + 1];
+                for (int half = 0; half < 2; ++half)
 #pragma unroll
-                for (int w = 4; w >= 1; w >>= 1)
+                    for (int m = 0; m < 4; ++m)
+                        pw[half][m] = pack2_bf16(p[8 * half + 2 * m], p[8 * half + 2 * m + 1]);
+                // the softmax sum, from the same bf16 values that enter P.V
+                // (one dot product with the pair (1, 1), bits 0x3f803f80, per
+                // packed pair; both operands are passed as 32-bit words: a
+                // bf16-vector constant here made the compiler read one pair
+                // four times)
+                float ps[2] = {0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < w; ++i) s8[i] += s8[i + w];
-                lsum += s8[0];
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) ps[half] = dot2_bf16(pw[half][m], 0x3f803f80u, ps[half]);
+                lsum += ps[0] + ps[1];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int u = 2 * kb + half;
-                    u4_t pw;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        pw[m] = pack2_bf16(p[8 * half + 2 * m], p[8 * half + 2 * m + 1]);
-                    const bf8_t pb = as_bf8(pw);
+                    const bf8_t pb = as_bf8(pw[half]);
 #pragma unroll
                     for (int j = 0; j < NOB; ++j) {
                         const u2_t lo = *reinterpret_cast<const u2_t *>(st_base + v_lds(j, u, 0));
