@@ -9,8 +9,10 @@
 // streams the causal range of its last token (or one split of it, below) in
 // tiles of KT positions, staged through LDS.  Its eight waves form two groups of four
 // (32 rows per wave) that take the even and the odd tiles, so each SIMD
-// runs two waves whose memory, LDS and matrix-core latencies overlap; the
-// two groups' softmax states are merged through LDS at the end.
+// runs two waves whose memory, LDS and matrix-core latencies overlap; each
+// group stages its own tiles and synchronises only its own four waves per
+// step (an arrival counter in LDS), so the groups are not held in lock-step;
+// their softmax states are merged through LDS at the end.
 //
 // Per tile and wave, two products on v_mfma_f32_32x32x16_bf16 (the gfx950
 // double-rate bf16 form):
@@ -306,6 +308,29 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     const float cs = a.c;
     const float thr = 8.0f / cs;
 
+    // Per-step synchronisation of one wave group only (its four waves stage
+    // and read the group's own LDS slots), so that the two groups sharing
+    // each SIMD are not held in lock-step by a workgroup-wide barrier.  An
+    // arrival counter per group in LDS: each wave adds one and waits for
+    // four arrivals per step so far.  The wait is bounded (every wave of a
+    // group runs the same number of steps, so all arrive; the cap only
+    // guards against a defect turning into a hang).
+    __shared__ uint32_t s_gbar[kVGroups];
+    if (threadIdx.x < kVGroups) s_gbar[threadIdx.x] = 0;
+    uint32_t gen = 0;
+    auto group_sync = [&]() {
+        ++gen;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0) __hip_atomic_fetch_add(&s_gbar[wgroup], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const uint32_t target = gen * kVRowWaves;
+        for (uint32_t spin = 0; spin < (1u << 22); ++spin) {
+            const uint32_t seen = __hip_atomic_load(&s_gbar[wgroup], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (__builtin_amdgcn_readfirstlane(seen) >= target) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    };
+
     // stage st, this group's tile slot
     auto slot = [&](int st) { return smem + (st * kVGroups + wgroup) * T::STAGE_BYTES; };
 
@@ -419,8 +444,9 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
         }
 
         if (more && t0 + TSTRIDE < t_end) store_tile(slot((it & 1) ^ 1), t0 + TSTRIDE, kr, vr);
-        __syncthreads();
+        group_sync();
     }
+    __syncthreads();   // both groups are done with their slots, which the merge reuses
 
     // merge the odd-tile group into the even-tile group: wave w + 4 holds
     // the same (query, dims) items as wave w, for the other tiles
