@@ -517,3 +517,22 @@ def test_sampler_subnormal_scaled_logits():
     bad, amb, infos = _sample_and_compare(z, g, t, p, k)
     assert not bad, bad
     assert [i.kept for i in infos[:4]] == k[:4].tolist()
+
+
+@pytest.mark.parametrize("B,V", [(3, 1 << 24), (1, (1 << 24) - 3)])
+def test_sampler_maximum_vocab(B, V):
+    """The largest supported vocabulary (2^24) and an odd one just below it
+    (single-float loads): thousands of chunks per row, more than the per-row
+    kernels have threads, so their loops over the chunks' maxima and best
+    keys run several rounds; nucleus, top-k and top-k then nucleus rows."""
+    rng = np.random.default_rng(77 + B)
+    z = (rng.standard_normal((B, V), dtype=np.float32) * 3).astype(np.float32)
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = np.array([0.8, 1.0, 0.5][:B], np.float32)
+    p = np.array([0.95, 1.0, 0.9][:B], np.float32)
+    k = np.array([0, 50, 1000][:B], np.int32)
+    z[-1, V - 1] = 14.0           # a high logit at the very end of the last row
+    say(f"sampler B={B} V={V}")
+    bad, amb, infos = _sample_and_compare(z, g, t, p, k)
+    assert not bad, bad
+    assert amb == 0
