@@ -374,13 +374,14 @@ struct Tile {
     // reads the chunk's first logits instead and is never used.  With no
     // branch between the loads and their use, each use waits only for its
     // own load.
+    template <bool NT = false>
     __device__ __forceinline__ void load(const float *__restrict__ row, int i0, int i1, int per)
     {
-        load_range<0, kMaxPer>(row, i0, i1, per);
+        load_range<0, kMaxPer, NT>(row, i0, i1, per);
     }
 
     // elements [J0, J0 + NJ) only (multiples of 4)
-    template <int J0, int NJ>
+    template <int J0, int NJ, bool NT = false>
     __device__ __forceinline__ void load_range(const float *__restrict__ row, int i0, int i1, int per)
     {
         if constexpr (VEC4) {
@@ -388,7 +389,9 @@ struct Tile {
             for (int q = J0 / 4; q < (J0 + NJ) / 4; ++q) {
                 const int i = index(i0, 4 * q);
                 const int ic = (4 * q < per && i < i1) ? i : i0;
-                const float4 f = *reinterpret_cast<const float4 *>(row + ic);
+                typedef float f32x4 __attribute__((ext_vector_type(4)));
+                const f32x4 *src = reinterpret_cast<const f32x4 *>(row + ic);
+                const f32x4 f = NT ? __builtin_nontemporal_load(src) : *src;
                 v[4 * q] = f.x;
                 v[4 * q + 1] = f.y;
                 v[4 * q + 2] = f.z;
@@ -398,7 +401,8 @@ struct Tile {
 #pragma unroll
             for (int j = J0; j < J0 + NJ; ++j) {
                 const int i = index(i0, j);
-                v[j] = row[(j < per && i < i1) ? i : i0];
+                const float *src = row + ((j < per && i < i1) ? i : i0);
+                v[j] = NT ? __builtin_nontemporal_load(src) : *src;
             }
         }
     }
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
     const int per = a.chunk / kThreads;
     // issued before the row's settings are known, so that the two overlap
     Tile<VEC4> t;
-    t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
+    t.template load<true>(a.logits + (int64_t)b * a.lstride, i0, i1, per);
     t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
     const uint32_t mode = row_mode(a, b);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a
     // the tile is requested before the row's settings are read, so that
     // the two overlap
     Tile<VEC4> t;
-    t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
+    t.template load<true>(a.logits + (int64_t)b * a.lstride, i0, i1, per);
     t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
     const uint32_t mode = a.flags ? ctl->mode : row_mode(a, b);
     unsigned long long best = 0;
