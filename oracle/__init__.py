@@ -38,11 +38,15 @@ class SampleExtras(ctypes.Structure):
 
 
 def lib():
+    """The oracle library.  PKV_ORACLE_LIB names another build of the same
+    source to load instead (the tests use it to run the pins against copies
+    with planted mistakes, or built with sanitizers)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        path = os.environ.get("PKV_ORACLE_LIB") or LIB_PATH
+        if path == LIB_PATH and not os.path.exists(LIB_PATH):
             build_oracle()
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         L.oracle_block_bytes.restype = I64

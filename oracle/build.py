@@ -14,14 +14,17 @@ LIB_PATH = os.path.join(HERE, "liboracle.so")
 SRC = os.path.join(HERE, "pkv_oracle.c")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, src: str = SRC, out: str = LIB_PATH,
+          extra_flags=()) -> str:
+    """Compiles `src` (the oracle, or a test's modified copy of it) into
+    `out`; `extra_flags` go to gcc as they are (e.g. sanitizers)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", LIB_PATH + ".tmp", SRC, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", *extra_flags, "-o", out + ".tmp", src, "-lm"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -8,7 +8,15 @@ import numpy as np
 import torch
 
 ATTN_TOL = 1e-2          # max-abs error of bf16 attention output vs fp64 oracle
-AMBIGUOUS_MARGIN = 1e-5  # nucleus rows this close to a mass boundary may differ
+# A nucleus row whose sampled id differs from the oracle's is excused only
+# when the oracle's cut lies within this distance (in normalised mass) of a
+# boundary of the threshold value's tie group: there the two sides' rounding
+# may legitimately choose different cuts.  The GPU's own error on the
+# quantity it compares is far below this (the bound is derived with the
+# sampler's design notes), so 1e-6 leaves room without excusing real
+# mistakes.  The seeded workload rows are held to bit-exact ids with no row
+# excused at all.
+AMBIGUOUS_MARGIN = 1e-6
 
 
 def say(*a):

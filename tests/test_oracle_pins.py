@@ -207,6 +207,20 @@ def test_attention_closed_forms():
             for j in range(n)]
     mean = np.mean(np.stack(rows).astype(np.float64), axis=0)
     np.testing.assert_allclose(oe[0], mean, rtol=0, atol=1e-13)
+    # softmax is shift invariant: the same equal keys at a scale that puts
+    # every score near 1e4 (exp overflows fp64 without subtracting the max)
+    # still give the mean of V; and two distinct scores 1e4 apart give the V
+    # of the larger one alone
+    oe_big = oracle.decode_attention(q, kc_eq, vc, table, np.array([n], np.int32), scale=1e4)
+    np.testing.assert_allclose(oe_big[0], mean, rtol=0, atol=1e-13)
+    kc2 = np.zeros_like(kc)                       # score 0 at position 0
+    one = bf16_bits_from_f32(np.ones(D, np.float32))
+    kc2[0, 1] = one                               # position 1: q . 1 at slot 1
+    q2 = np.broadcast_to(one, (1, 2, D)).copy()   # q . 1 = D = 8 > 0
+    o2 = oracle.decode_attention(q2, kc2, vc, np.array([[0]], np.int32), np.array([2], np.int32),
+                                 scale=1250.0)   # scores 0 and 1e4
+    for h in range(2):
+        np.testing.assert_array_equal(o2[0, h], f32_from_bf16_bits(vc[0, 1, h]).astype(np.float64))
 
 
 def test_gqa_equals_mha_with_repeated_heads():
@@ -375,6 +389,100 @@ def test_nucleus_page_rule_matches_definition_on_tiny_vocab():
         assert info.kept == len(kept_def)
         checked += 1
     assert checked > 300
+
+
+def test_top_k_then_nucleus_takes_the_nucleus_of_the_top_k_set():
+    """Runners chapter 8.3 masks to the top k, then filters by top-p: the
+    nucleus is taken over the softmax of the kept k tokens.  z = [2, 1 x 9],
+    T = 1, k = 2 keeps {0, 1} (the 1.0 tie goes to the lower index); over
+    that set token 0 holds e/(e+1) = 0.731 > p = 0.5 of the mass, so the
+    nucleus is {0} alone.  Over all ten tokens token 0 holds only
+    e/(e+9) = 0.232, so a nucleus over the whole vocabulary would keep the
+    1.0 group too, i.e. both tokens of the top-k set."""
+    z = np.array([2.0] + [1.0] * 9, np.float32)
+    g = np.array([-5.0, 5.0] + [0.0] * 8, np.float32)  # noise favours index 1
+    info = oracle.sample_row(z, g, 1.0, 0.5, 2)
+    assert info.kept == 1 and info.id == 0 and info.tau == 2.0
+    # the same row with the top-k set's own mass boundary on the other side:
+    # p = 0.75 > e/(e+1) needs both kept tokens
+    info = oracle.sample_row(z, g, 1.0, 0.75, 2)
+    assert info.kept == 2 and info.id == 1
+    # closed form of the margin over the top-k set: the cut sits in the
+    # group {2.0} whose strictly-below mass is 1/(e+1) and through-mass 1
+    e = math.e
+    target = 1.0 - float(np.float32(0.5))
+    m_exact = min(target - 1 / (e + 1), 1.0 - target)
+    info = oracle.sample_row(z, g, 1.0, 0.5, 2)
+    assert abs(info.margin - m_exact) < 1e-12
+
+
+def test_nucleus_margin_closed_forms():
+    """margin = distance from the cut's target 1 - p to the nearer mass
+    boundary of the threshold value's tie group (mass strictly below tau,
+    mass up to and including tau), in normalised mass."""
+    g0 = np.zeros(8, np.float32)
+    # eight equal logits: masses 1/8 each; 1 - p = 0.3125 lies inside the
+    # one tie group [0, 1], 3/8 of the way along the cumsum (its third
+    # member reaches it first): distance 0.3125 to the lower edge 0, 0.6875
+    # to the upper edge 1
+    info = oracle.sample_row(np.zeros(8, np.float32), g0, 1.0, 0.6875, 0)
+    assert info.kept == 8 and info.tau == 0.0
+    assert info.margin == 0.3125
+    # s = [1, 1, 1, 0, 0]: masses a = 1/(3e+2) for the zeros, b = e/(3e+2)
+    # for the ones; ascending cumsum a, 2a, 2a+b, 2a+2b, 1.  1 - p at 2a +
+    # 1.2 b is reached first at the second 1 (index 3), inside the group
+    # {1} whose edges are 2a (below) and 1 (through).
+    e = math.e
+    a, b = 1 / (3 * e + 2), e / (3 * e + 2)
+    p = np.float32(1.0 - (2 * a + 1.2 * b))
+    target = 1.0 - float(p)
+    s = np.array([1.0, 1.0, 1.0, 0.0, 0.0], np.float32)
+    info = oracle.sample_row(s, np.zeros(5, np.float32), 1.0, p, 0)
+    assert info.kept == 3 and info.tau == 1.0
+    m1, m2 = target - 2 * a, 1.0 - target
+    assert m1 < m2
+    assert abs(info.margin - m1) < 1e-12
+    # upper edge nearer: 1 - p at 1.25 a lies inside the group {0}, whose
+    # edges are 0 and 2a; the nearer one is 2a, 0.75 a away
+    p2 = np.float32(1.0 - 1.25 * a)
+    target2 = 1.0 - float(p2)
+    info = oracle.sample_row(s, np.zeros(5, np.float32), 1.0, p2, 0)
+    assert info.kept == 5 and info.tau == 0.0
+    assert abs(info.margin - min(target2 - 0.0, 2 * a - target2)) < 1e-12
+
+
+def test_nucleus_margin_is_the_distance_to_a_change_of_the_kept_set():
+    """What the margin means: moving p by 0.9 x margin either way keeps the
+    kept set, while moving it 1.1 x margin towards the nearer boundary
+    changes it.  Random small rows with ties; rows whose cut lies in the
+    lowest or the highest kept value group are skipped: the lower edge of
+    the lowest group (mass 0) and the upper edge of the highest (mass 1)
+    cannot be crossed by any 0 < p < 1, so there the margin is only a
+    conservative bound."""
+    rng = np.random.default_rng(28)
+    checked = 0
+    for trial in range(1000):
+        V = int(rng.integers(3, 12))
+        s = (rng.integers(-3, 4, size=V) * 0.5).astype(np.float32)
+        p = np.float32(rng.uniform(0.05, 0.95))
+        k = int(rng.integers(0, V + 1)) if trial % 2 else 0
+        base = oracle.sample_row(s, np.zeros(V, np.float32), 1.0, p, k)
+        m = base.margin
+        kept_vals = np.sort(s)[::-1][:k] if 0 < k < V else s
+        if m < 1e-4 or base.tau in (kept_vals.min(), kept_vals.max()):
+            continue
+        for sign in (1.0, -1.0):
+            q = np.float32(float(p) + sign * 0.9 * m)
+            info = oracle.sample_row(s, np.zeros(V, np.float32), 1.0, q, k)
+            assert info.kept == base.kept, (s, p, k, m, sign)
+        changed = []
+        for sign in (1.0, -1.0):
+            q = np.float32(min(max(float(p) + sign * 1.1 * m, 1e-6), 1.0))
+            info = oracle.sample_row(s, np.zeros(V, np.float32), 1.0, q, k)
+            changed.append(info.kept != base.kept)
+        assert any(changed), (s, p, k, m)
+        checked += 1
+    assert checked > 250
 
 
 def test_sampled_distribution_matches_softmax_on_eligible_set():
