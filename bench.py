@@ -99,6 +99,7 @@ def main():
 
     sys.path.insert(0, ROOT)
     import paged_kv_decode_store_amd as pkv
+    from paged_kv_decode_store_amd.step import CascadeArgs, SamplerArgs, decode_step
     from workloads import config_by_name, host_inputs
     from workloads.device import device_pool
     from workloads.generate import sampling_params
@@ -146,7 +147,6 @@ def main():
     logits = torch.from_numpy(inp.logits).to(dev)
     gumbel = torch.from_numpy(inp.gumbel).to(dev)
     t, p, k = (torch.from_numpy(x).to(dev) for x in sampling_params(cfg))
-    flags = (pkv.PKV_SAMPLE_TOPK if cfg.top_k > 0 else 0) | (pkv.PKV_SAMPLE_TOPP if cfg.top_p < 1 else 0)
     max_len = int(n.max())
     split = pkv.decode_split_tokens(B, Hq, Hkv, max_len, args.split)
     ws = torch.empty(pkv.decode_workspace_bytes(B, Hq, Hkv, D, max_len, split), dtype=torch.uint8,
@@ -187,25 +187,23 @@ def main():
             pkv.decode_attention_reduce(out, nd, Hkv, tables.shape[1], bs, max_len, ws,
                                         split_tokens=split)
 
+    # the step itself: one fixed sequence of library calls shared with the
+    # step tests (paged_kv_decode_store_amd.step.decode_step)
+    layer_args = [[(q[l], kp[c][l], vp[c][l], kn[l], vn[l]) for l in range(L)] for c in range(R)]
+    samp = SamplerArgs(logits, gumbel, t, p, k, ids, sws)
+    mode = "cascade" if cascade else "fused" if fused else "unfused"
+    casc = CascadeArgs(prefix, cws) if cascade else None
+
     def step(ev=None, c=0):
-        if not fused:
-            pkv.slot_mapping(td, nd, bs, out=slots)
-        for layer in range(L):
-            if not fused:
-                pkv.kv_store(kp[c][layer], vp[c][layer], kn[layer], vn[layer], slots)
-            if ev is not None:
-                ev["p0"][layer].record()
-            partial(layer, c)
-            if ev is not None:
-                ev["p1"][layer].record()
-            reduce()
-            if ev is not None:
-                ev["r1"][layer].record()
+        mark = None
         if ev is not None:
-            ev["s0"].record()
-        pkv.sample_next_token(logits, gumbel, t, p, k, flags=flags, out=ids, workspace=sws)
-        if ev is not None:
-            ev["s1"].record()
+            def mark(point, layer):
+                {"partial": lambda: ev["p0"][layer], "reduce": lambda: ev["p1"][layer],
+                 "done": lambda: ev["r1"][layer], "sampler": lambda: ev["s0"],
+                 "end": lambda: ev["s1"]}[point]().record()
+        decode_step(layer_args[c], td, nd, bs, max_len, out=out, workspace=ws,
+                    split_tokens=args.split if cascade else split, sampler=samp, mode=mode,
+                    slots=slots, cascade=casc, mark=mark)
 
     for i in range(args.warmup):
         step(c=i % R)
@@ -288,7 +286,7 @@ def main():
         samp_copies = int(min(64, max(1, -(-(1 << 30) // (logits.numel() * 4)))))
         lcopies = [logits] + [logits.clone() for _ in range(samp_copies - 1)]
         graph_samp_us = 1e3 * graph_time_ms(
-            lambda c: pkv.sample_next_token(lcopies[c], gumbel, t, p, k, flags=flags, out=ids,
+            lambda c: pkv.sample_next_token(lcopies[c], gumbel, t, p, k, out=ids,
                                             workspace=sws), ncalls=samp_copies)
         del lcopies
         log(f"[bench] sampler graph replay: {graph_samp_us:.2f} us per draw "

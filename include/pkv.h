@@ -51,6 +51,41 @@ const char *pkv_status_string(int status);
 /* Text of the last failure on the calling host thread ("" if none). */
 const char *pkv_last_error(void);
 
+/* ---- device error word ----------------------------------------------------
+ * Kernels cannot return a status, and device-side contents are only checked
+ * on the device.  Rather than degrade silently (the "xAI native runtime"
+ * article, section 4.2, asks for an explicit out-of-KV-slots error), the
+ * kernels OR the bits below into a caller-owned device word when they meet
+ * contents that break the contract stated with each entry point.  They keep
+ * their in-bounds behaviour (skip the slot, read block 0, truncate the row),
+ * so a set bit means the affected outputs are unspecified, never that memory
+ * outside the buffers was touched.
+ *
+ * pkv_set_error_word(word): word is a device pointer to one uint32_t (4-byte
+ * aligned), or NULL to stop reporting (the default).  The setting belongs to
+ * the calling host thread and applies to the calls it makes afterwards
+ * (kernels captured into a graph keep the word they were captured with).
+ * The library never clears the word: the caller zeroes it (e.g. with a fill
+ * kernel on the same stream) and reads it back when it wants the result. */
+#define PKV_DEVERR_SLOT 0x1u        /* store: slot >= num_blocks * block_size */
+#define PKV_DEVERR_BLOCK_ID 0x2u    /* a block id a row needs is < 0 or >= num_blocks */
+#define PKV_DEVERR_CONTEXT_LEN 0x4u /* context length < 0, > max_context_len (or
+                                       max_seqlen_k), or past the block table */
+#define PKV_DEVERR_SEQLENS 0x8u     /* varlen: q_len < 0, k_len < q_len, or
+                                       q_len > max_seqlen_q */
+#define PKV_DEVERR_WAIT 0x10u       /* an in-kernel bounded wait gave up; the
+                                       outputs of that launch are unreliable */
+
+int pkv_set_error_word(uint32_t *word);
+uint32_t *pkv_get_error_word(void);
+
+/* Test hook: the iteration cap of the in-kernel bounded waits (varlen
+ * attention's per-group step synchronisation), for the calling host thread.
+ * 0 restores the default (2^22 polls, never reached in a correct run).  A
+ * small cap makes the wait give up, which sets PKV_DEVERR_WAIT; addresses
+ * never depend on the wait, so the launch still stays inside its buffers. */
+int pkv_set_wait_limit(uint32_t polls);
+
 /* ---- slot mapping ---------------------------------------------------------
  * Decode-step slot of each row's new token (nano-vllm "Model Runner" page,
  * sections "allocated kv cache" and "prefill and decode"): a row whose

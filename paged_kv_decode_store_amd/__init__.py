@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import PKV_SAMPLE_TOPK, PKV_SAMPLE_TOPP, PkvError, check, lib
+from ._lib import (PKV_DEVERR_BLOCK_ID, PKV_DEVERR_CONTEXT_LEN, PKV_DEVERR_SEQLENS,
+                   PKV_DEVERR_SLOT, PKV_DEVERR_WAIT, PKV_SAMPLE_TOPK, PKV_SAMPLE_TOPP, PkvError,
+                   check, lib)
 
 __all__ = [
     "slot_mapping", "kv_store", "paged_decode_attention", "decode_attention_partial",
@@ -25,7 +27,27 @@ __all__ = [
     "sample_next_token", "sample_next_token_ex", "sampler_workspace_bytes", "PkvError",
     "varlen_split_tokens", "varlen_workspace_bytes",
     "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
+    "set_error_word", "set_wait_limit", "PKV_DEVERR_SLOT", "PKV_DEVERR_BLOCK_ID",
+    "PKV_DEVERR_CONTEXT_LEN", "PKV_DEVERR_SEQLENS", "PKV_DEVERR_WAIT",
 ]
+
+
+def set_error_word(word: Optional[torch.Tensor]) -> None:
+    """Report device-side contract violations (PKV_DEVERR_* bits) into
+    `word`, a one-element int32 GPU tensor the caller zeroes and reads; None
+    stops reporting.  Applies to later calls from this host thread."""
+    if word is None:
+        check(lib().pkv_set_error_word(None), "pkv_set_error_word")
+        return
+    if word.numel() < 1:
+        raise ValueError("word must hold at least one element")
+    check(lib().pkv_set_error_word(_dev(word, "word", torch.int32)), "pkv_set_error_word")
+
+
+def set_wait_limit(polls: int) -> None:
+    """Poll cap of the kernels' bounded waits for this host thread (0 = the
+    default); a test hook that makes the waits give up and report."""
+    check(lib().pkv_set_wait_limit(int(polls)), "pkv_set_wait_limit")
 
 
 def _stream():

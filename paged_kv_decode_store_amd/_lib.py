@@ -17,6 +17,12 @@ PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
 PKV_SAMPLE_TOPK = 1
 PKV_SAMPLE_TOPP = 2
+# device error word bits (include/pkv.h)
+PKV_DEVERR_SLOT = 0x1
+PKV_DEVERR_BLOCK_ID = 0x2
+PKV_DEVERR_CONTEXT_LEN = 0x4
+PKV_DEVERR_SEQLENS = 0x8
+PKV_DEVERR_WAIT = 0x10
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -29,6 +35,9 @@ _F = ctypes.c_float
 PROTOTYPES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_set_error_word": (ctypes.c_int, [_P]),
+    "pkv_get_error_word": (_P, []),
+    "pkv_set_wait_limit": (ctypes.c_int, [_U32]),
     "pkv_slot_mapping": (ctypes.c_int, [_P, _P, _I32, _P, _I32, _I32, _P]),
     "pkv_kv_store": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I64, _P]),
     "pkv_decode_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32]),

@@ -12,6 +12,12 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+// device error word and bounded-wait cap of the calling host thread
+thread_local uint32_t *g_err_word = nullptr;
+thread_local uint32_t g_wait_limit = 0;
+constexpr uint32_t kDefaultWaitLimit = 1u << 22;
+
+uint32_t wait_limit() { return g_wait_limit ? g_wait_limit : kDefaultWaitLimit; }
 
 int fail(int status, const char *fmt, ...)
 {
@@ -157,6 +163,21 @@ const char *pkv_status_string(int status)
 
 const char *pkv_last_error(void) { return g_last_error; }
 
+int pkv_set_error_word(uint32_t *word)
+{
+    REQUIRE(aligned(word, 4), PKV_ERR_INVALID_ARG, "error word must be 4-byte aligned");
+    g_err_word = word;
+    return PKV_OK;
+}
+
+uint32_t *pkv_get_error_word(void) { return g_err_word; }
+
+int pkv_set_wait_limit(uint32_t polls)
+{
+    g_wait_limit = polls;
+    return PKV_OK;
+}
+
 int pkv_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
                      int32_t block_table_stride, const int32_t *context_lens, int32_t batch,
                      int32_t block_size, hipStream_t stream)
@@ -170,7 +191,8 @@ int pkv_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
     REQUIRE(pow2(block_size) && block_size <= (1 << 20), PKV_ERR_UNSUPPORTED,
             "block_size %d must be a power of two", block_size);
     return hip_status(pkv::launch_slot_mapping(slot_mapping, block_tables, block_table_stride,
-                                               context_lens, batch, block_size, stream),
+                                               context_lens, batch, block_size, g_err_word,
+                                               stream),
                       "slot_mapping launch");
 }
 
@@ -203,7 +225,7 @@ int pkv_kv_store(void *k_cache, void *v_cache, const void *k_new, const void *v_
                                            static_cast<const uint16_t *>(k_new),
                                            static_cast<const uint16_t *>(v_new), slot_mapping,
                                            num_tokens, num_kv_heads, head_dim, stride,
-                                           num_blocks * block_size, stream),
+                                           num_blocks * block_size, g_err_word, stream),
                       "kv_store launch");
 }
 
@@ -243,6 +265,8 @@ int setup_partial(pkv::PartialArgs &a, const void *q, int64_t q_stride, const vo
     // every field not set below is zero: in particular `out` stays null, so
     // the partial kernels write partials, not the direct output
     memset(&a, 0, sizeof a);
+    a.err = g_err_word;
+    a.wait_limit = wait_limit();
     int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
                                    block_table_stride, max_context_len);
     if (rc) return rc;
@@ -580,6 +604,8 @@ int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q, int
     }
     pkv::PartialArgs a;
     memset(&a, 0, sizeof a);
+    a.err = g_err_word;
+    a.wait_limit = wait_limit();
     a.q = static_cast<const uint16_t *>(q);
     a.q_stride = qs;
     a.k_cache = static_cast<const uint16_t *>(k_cache);

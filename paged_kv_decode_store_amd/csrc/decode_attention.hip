@@ -63,6 +63,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     const int n = min(max(n_row, 0), a.max_len);
     const int t_begin = a.pos_base + s * a.split_tokens;
     const int h0 = kvh * a.group + hc * G;
+    // one workgroup per row reports a length outside [0, max_len]
+    if (threadIdx.x == 0 && s == 0 && kv_slot == 0 && hc == 0 && n != n_row)
+        report_error(a.err, PKV_DEVERR_CONTEXT_LEN);
     if (t_begin >= n) {
         // direct output (one split per row): an empty row's output is zero
         if (a.out && s == 0)
@@ -97,10 +100,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     const int32_t *table = a.block_tables + (int64_t)b * a.table_stride;
 
     // Issue the K/V loads of the chunk starting at t0 (one block, U positions
-    // per lane group, one 16-byte piece per lane and position).
+    // per lane group, one 16-byte piece per lane and position).  A bad block
+    // id is only noted here (a scalar flag, no branch in the loop) and
+    // reported once after it.
+    bool bad_block = false;
     auto load_chunk = [&](int t0, uint4 (&kr)[U], uint4 (&vr)[U]) {
         const int raw = load_block_id(table, uniform(t0 >> a.bs_log2));
         const bool blk_ok = raw >= 0 && raw < a.num_blocks;
+        bad_block |= !blk_ok;
         const int blk = blk_ok ? raw : 0;
         const int64_t base =
             (((int64_t)blk << a.bs_log2) + (t0 & bs_mask)) * tok_stride + lane_off;
@@ -199,6 +206,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
         load_chunk(t0, ka, va);
         compute_chunk(t0, ka, va);
     }
+    if (bad_block && lane == 0) report_error(a.err, PKV_DEVERR_BLOCK_ID);
 
     // merge the lane groups of this wave
 #pragma unroll

@@ -127,6 +127,9 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
         const int n_row = a.context_lens[b];
         n = min(max(n_row, 0), a.max_len);
         t_begin = a.pos_base + s * a.split_tokens;
+        // one workgroup per row reports a length outside [0, max_len]
+        if (threadIdx.x == 0 && s == 0 && hc == 0 && kvh == 0 && n != n_row)
+            report_error(a.err, PKV_DEVERR_CONTEXT_LEN);
         if (t_begin >= n) {
             // direct output (one split per row): an empty row's output is zero
             if (a.out && s == 0) {
@@ -201,9 +204,12 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
         }
     }
 
+    // a bad block id is noted in a scalar flag and reported after the loop
+    bool bad_block = false;
     for (int t0 = t_begin + wave * kMChunk; t0 < t_end; t0 += kMRound) {
         const int raw = load_block_id(table, uniform(t0 >> a.bs_log2));
         const bool blk_ok = raw >= 0 && raw < a.num_blocks;
+        bad_block |= !blk_ok;
         const int64_t base = (((int64_t)(blk_ok ? raw : 0) << a.bs_log2) + (t0 & bs_mask)) *
                                  tok_stride + (int64_t)kvh * D;
         // K: position t0 + ln, pieces 4*w + kb.  V: positions t0 + 4*kb + j,
@@ -290,6 +296,8 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
             o[j] = mfma16(pr, vb, o[j]);
         }
     }
+
+    if (bad_block && lane == 0) report_error(a.err, PKV_DEVERR_BLOCK_ID);
 
     // merge the waves through LDS: o rows are queries 4*kb + i, columns dims
     lsum += __shfl_xor(lsum, 16);

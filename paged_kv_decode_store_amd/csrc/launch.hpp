@@ -8,14 +8,16 @@
 
 namespace pkv {
 
+// `err`: the device error word of the calling thread (null: no reporting).
 hipError_t launch_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
                                int32_t table_stride, const int32_t *context_lens,
-                               int32_t batch, int32_t block_size, hipStream_t stream);
+                               int32_t batch, int32_t block_size, uint32_t *err,
+                               hipStream_t stream);
 
 hipError_t launch_kv_store(uint16_t *k_cache, uint16_t *v_cache, const uint16_t *k_new,
                            const uint16_t *v_new, const int32_t *slots, int32_t num_tokens,
                            int32_t num_kv_heads, int32_t head_dim, int64_t new_stride,
-                           int64_t total_slots, hipStream_t stream);
+                           int64_t total_slots, uint32_t *err, hipStream_t stream);
 
 // Split-KV geometry shared by the partial and reduce steps.
 struct SplitGeometry {
@@ -82,6 +84,11 @@ struct PartialArgs {
     int64_t out_stride;
     int32_t qchunks;        // chunks per sequence (from the longest one)
     int32_t total_q;        // rows of q / out (the merge step's grid)
+    int32_t max_q;          // varlen: tokens past this in a sequence are not computed
+    // device error word (PKV_DEVERR_* bits) or null, and the poll cap of
+    // in-kernel bounded waits
+    uint32_t *err;
+    uint32_t wait_limit;
 };
 
 struct ReduceArgs {

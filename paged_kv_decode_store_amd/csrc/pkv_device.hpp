@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -77,6 +79,14 @@ __device__ __forceinline__ float wave_sum(float v)
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Records contract violations (PKV_DEVERR_* bits) in the caller's device
+// error word, if one is set.  A vector-memory atomic OR; callers keep it off
+// their hot paths (it runs only when a bad value was actually seen).
+__device__ __forceinline__ void report_error(uint32_t *err, uint32_t bits)
+{
+    if (err) __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Block id j of a block table, as a scalar load.  The table is read-only in
 // every kernel, but where the same kernel also stores to the KV pools the

@@ -163,6 +163,11 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     const int q0 = a.cu_q[b];
     const int q_len = a.cu_q[b + 1] - q0;
     const int k_len = a.cu_k[b + 1] - a.cu_k[b];
+    // one workgroup per sequence reports lengths that break the contract
+    if (threadIdx.x == 0 && kvh == 0 && rest == 0) {
+        if (q_len < 0 || k_len < q_len || q_len > a.max_q) report_error(a.err, PKV_DEVERR_SEQLENS);
+        if (k_len > a.max_len) report_error(a.err, PKV_DEVERR_CONTEXT_LEN);
+    }
     if (q_len <= 0 || k_len < q_len) return;
     const int cached = k_len - q_len;
     const int row0 = tile * kVRows;
@@ -209,7 +214,13 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
         koff[i] = (uint32_t)(((kq + i * KSTEP) * tok_stride + piece * 8) * 2);
         voff[i] = (uint32_t)(((4 * kq + i) * tok_stride + piece * 8) * 2);
     }
-    auto valid_block = [&](int raw) { return (raw >= 0 && raw < a.num_blocks) ? raw : 0; };
+    // a bad id reads block 0 and is noted (no branch) for one report at the end
+    bool bad_block = false;
+    auto valid_block = [&](int raw) {
+        const bool ok = raw >= 0 && raw < a.num_blocks;
+        bad_block |= !ok;
+        return ok ? raw : 0;
+    };
 
     // Block ids, read ahead and checked only where used (a range check at
     // the read would become a branch whose wait also drains the tile loads
@@ -313,21 +324,30 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
     // each SIMD are not held in lock-step by a workgroup-wide barrier.  An
     // arrival counter per group in LDS: each wave adds one and waits for
     // four arrivals per step so far.  The wait is bounded (every wave of a
-    // group runs the same number of steps, so all arrive; the cap only
-    // guards against a defect turning into a hang).
+    // group runs the same number of steps, so all arrive; the cap, 2^22
+    // polls unless the caller set another, only guards against a defect
+    // turning into a hang).  A wait that gives up is reported in the device
+    // error word; no address depends on it.
     __shared__ uint32_t s_gbar[kVGroups];
     if (threadIdx.x < kVGroups) s_gbar[threadIdx.x] = 0;
     uint32_t gen = 0;
+    bool gave_up = false;
+    const uint32_t polls = a.wait_limit;
     auto group_sync = [&]() {
         ++gen;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         if (lane == 0) __hip_atomic_fetch_add(&s_gbar[wgroup], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         const uint32_t target = gen * kVRowWaves;
-        for (uint32_t spin = 0; spin < (1u << 22); ++spin) {
+        bool met = false;
+        for (uint32_t spin = 0; spin < polls; ++spin) {
             const uint32_t seen = __hip_atomic_load(&s_gbar[wgroup], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (__builtin_amdgcn_readfirstlane(seen) >= target) break;
+            if (__builtin_amdgcn_readfirstlane(seen) >= target) {
+                met = true;
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
         }
+        gave_up |= !met;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     };
 
@@ -445,6 +465,11 @@ __global__ __launch_bounds__(kVThreads) void varlen_attention_kernel(const Parti
 
         if (more && t0 + TSTRIDE < t_end) store_tile(slot((it & 1) ^ 1), t0 + TSTRIDE, kr, vr);
         group_sync();
+    }
+    const bool any_bad = __any(bad_block);   // the whole wave votes, then one lane reports
+    if (lane == 0) {
+        if (any_bad) report_error(a.err, PKV_DEVERR_BLOCK_ID);
+        if (gave_up) report_error(a.err, PKV_DEVERR_WAIT);
     }
     __syncthreads();   // both groups are done with their slots, which the merge reuses
 
@@ -587,6 +612,7 @@ hipError_t launch_varlen_attention(const PartialArgs &a, int32_t head_dim, int32
     if (a.batch == 0 || max_seqlen_q <= 0) return hipSuccess;
     PartialArgs m = a;
     m.qchunks = (int32_t)(((int64_t)max_seqlen_q * a.group + kVRows - 1) / kVRows);
+    m.max_q = max_seqlen_q;
     if (head_dim == 128) return launch_varlen_d<128>(m, stream);
     if (head_dim == 64) return launch_varlen_d<64>(m, stream);
     return hipErrorInvalidValue;

@@ -58,3 +58,31 @@ def compare_ids(gpu_ids, ref_ids, infos):
             continue
         bad.append((b, int(g), int(r), info.kept, info.margin))
     return bad, amb
+
+
+def oracle_head_jobs(jobs, k_pool, v_pool, scale, threads=16):
+    """Oracle outputs of single (query, context) jobs, each (key, q_head
+    [D] uint16, block-table row, context length, KV head), on up to
+    `threads` host threads (the C oracle runs outside the interpreter lock).
+    Returns {key: fp64 [D]}."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    kc = np.ascontiguousarray(k_pool)
+    vc = np.ascontiguousarray(v_pool)
+
+    def one(job):
+        key, qh, row, n, kvh = job
+        return key, oracle.decode_attention_head(qh, kc, vc, row, n, kvh, scale)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return dict(ex.map(one, jobs))
+
+
+def oracle_heads(q, k_pool, v_pool, tables, lens, pairs, group, scale=None, threads=16):
+    """Decode-attention oracle outputs of the given (row, query head) pairs,
+    threaded; returns {(b, h): fp64 [D]}."""
+    sc = scale if scale is not None else 1.0 / np.sqrt(q.shape[-1])
+    jobs = [((b, h), q[b, h], tables[b], int(lens[b]), h // group) for b, h in pairs]
+    return oracle_head_jobs(jobs, k_pool, v_pool, sc, threads)

@@ -26,10 +26,30 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.PROTOTYPES)
+
+
+def test_error_word_setting_is_per_thread_and_checked():
+    """Host side of the device error word: a misaligned word is refused,
+    a set word is returned by the getter, NULL stops reporting, and another
+    host thread keeps its own setting.  (No kernel runs here.)"""
+    import threading
+    L = _lib.lib()
+    assert L.pkv_set_error_word(FAKE + 2) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_set_error_word(FAKE) == _lib.PKV_OK
+    assert L.pkv_get_error_word() == FAKE
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(L.pkv_get_error_word()))
+    th.start()
+    th.join()
+    assert seen == [None]
+    assert L.pkv_set_error_word(None) == _lib.PKV_OK
+    assert L.pkv_get_error_word() is None
+    assert L.pkv_set_wait_limit(5) == _lib.PKV_OK
+    assert L.pkv_set_wait_limit(0) == _lib.PKV_OK
 
 
 def test_status_strings():

@@ -16,7 +16,7 @@ from workloads.device import device_pool
 from workloads.generate import block_tables, bf16_bits_from_f32, context_lengths, sampling_params
 
 from gpu_util import (ATTN_TOL, bf16_out_to_f64, compare_ids, dev_f32, dev_i32, dev_u16,
-                      host_u16, say)
+                      host_u16, oracle_heads, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -220,9 +220,11 @@ def test_decode_step_qwen3_full_layers():
 
 
 def test_decode_step_long_sampled_heads():
-    """Long-context split-KV workload at full size; the oracle checks three
-    query heads (first, middle, last) of every row, which covers all
-    splits of every row."""
+    """Long-context split-KV workload at full size (matrix-core kernel, KV
+    head rotated by split index); the threaded oracle checks two query
+    heads of every KV head of every row (the first and last of its group on
+    even rows, two middle ones on odd rows), which covers every split of
+    every (row, KV head)."""
     cfg = config_by_name("long")
     inp = host_inputs(cfg, layers=(0,), pools=False, sampler=False)
     n, t = inp.context_lens, inp.block_tables
@@ -236,13 +238,13 @@ def test_decode_step_long_sampled_heads():
     got = bf16_out_to_f64(out)
     kh, vh = host_u16(kc), host_u16(vc)
     g = cfg.group
-    scale = 1.0 / np.sqrt(cfg.head_dim)
-    worst = 0.0
+    pairs = []
     for b in range(cfg.batch):
-        for h in (0, cfg.num_q_heads // 2 + 1, cfg.num_q_heads - 1):
-            ref = oracle.decode_attention_head(inp.q[0][b, h], kh, vh, t[b], n[b], h // g, scale)
-            worst = max(worst, float(np.abs(got[b, h] - ref).max()))
-    say(f"  max abs err {worst:.3e}")
+        inner = (0, g - 1) if b % 2 == 0 else (g // 2 - 1, g // 2)
+        pairs += [(b, kvh * g + i) for kvh in range(cfg.num_kv_heads) for i in inner]
+    ref = oracle_heads(inp.q[0], kh, vh, t, n, pairs, g)
+    worst = max(float(np.abs(got[b, h] - ref[(b, h)]).max()) for b, h in pairs)
+    say(f"  max abs err {worst:.3e} over {len(pairs)} (row, head) pairs")
     assert worst <= ATTN_TOL
 
 
