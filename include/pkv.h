@@ -227,6 +227,38 @@ int pkv_paged_decode_attention_store(void *out, int64_t out_stride,
                                      int32_t split_tokens, void *workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 
+/* The fused store + attention without a workspace argument, for callers
+ * that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The split-KV partials
+ * go to a fixed device array inside the library, PKV_STATIC_SCRATCH_BYTES
+ * long, of which each GPU holds its own copy for the life of the process;
+ * no call allocates or frees anything.  The result equals
+ * pkv_paged_decode_attention_store with the same arguments.
+ * Limits: the partials must fit, i.e. pkv_decode_workspace_bytes(batch,
+ * num_q_heads, num_kv_heads, head_dim, max_context_len, split_tokens) <=
+ * PKV_STATIC_SCRATCH_BYTES, else PKV_ERR_WORKSPACE before any HIP call
+ * (e.g. 64 rows x 16 heads at 4096 positions use about 4.3 MB).
+ * Concurrency: every call on one GPU uses that GPU's single array, so calls
+ * that overlap in time on one GPU (different streams, or other host
+ * threads) race and give unspecified results; serialise them on one
+ * stream.  Calls in order on one stream are safe (nothing in the array
+ * needs clearing: each call fully writes what it reads). */
+#define PKV_STATIC_SCRATCH_BYTES (32u << 20)
+
+int pkv_paged_decode_attention_store_noalloc(void *out, int64_t out_stride,
+                                             const void *q, int64_t q_stride,
+                                             void *k_cache, void *v_cache,
+                                             const void *k_new, const void *v_new,
+                                             int64_t new_token_stride,
+                                             const int32_t *block_tables,
+                                             int32_t block_table_stride,
+                                             const int32_t *context_lens,
+                                             int32_t batch, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int64_t num_blocks,
+                                             int32_t max_context_len, float scale,
+                                             int32_t split_tokens, hipStream_t stream);
+
 /* Partial step of the fused path only (store + partials); finish with
  * pkv_decode_attention_reduce. */
 int pkv_decode_attention_partial_store(const void *q, int64_t q_stride,

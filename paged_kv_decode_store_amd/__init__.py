@@ -27,7 +27,7 @@ __all__ = [
     "sample_next_token", "sample_next_token_ex", "sampler_workspace_bytes", "PkvError",
     "varlen_split_tokens", "varlen_workspace_bytes",
     "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
-    "set_error_word", "set_wait_limit", "PKV_DEVERR_SLOT", "PKV_DEVERR_BLOCK_ID",
+    "set_error_word", "set_wait_limit", "paged_decode_attention_store_noalloc", "PKV_DEVERR_SLOT", "PKV_DEVERR_BLOCK_ID",
     "PKV_DEVERR_CONTEXT_LEN", "PKV_DEVERR_SEQLENS", "PKV_DEVERR_WAIT",
 ]
 
@@ -268,6 +268,28 @@ def paged_decode_attention_store(q: torch.Tensor, k_cache: torch.Tensor, v_cache
         _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs, nb, max_context_len,
         scale, split_tokens, ws.data_ptr(), ws.numel(), _stream()),
         "pkv_paged_decode_attention_store")
+    return out
+
+
+def paged_decode_attention_store_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                                         v_cache: torch.Tensor, k_new: torch.Tensor,
+                                         v_new: torch.Tensor, block_tables: torch.Tensor,
+                                         context_lens: torch.Tensor, max_context_len: int,
+                                         out: torch.Tensor, scale: float = 0.0,
+                                         split_tokens: int = 0) -> torch.Tensor:
+    """paged_decode_attention_store without a workspace: the partials live
+    in the library's fixed device array (PKV_STATIC_SCRATCH_BYTES), so the
+    call allocates nothing (the caller passes `out`).  Calls overlapping in
+    time on one GPU race on that array."""
+    B, Hq, D, nb, bs, hkv = _attn_shapes(q, k_cache, block_tables)
+    ns = _new_rows(k_new, v_new, hkv, D)
+    check(lib().pkv_paged_decode_attention_store_noalloc(
+        _dev(out, "out", torch.bfloat16), out.stride(0), _dev(q, "q", torch.bfloat16), q.stride(0),
+        _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16), ns,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), B, Hq, hkv, D, bs, nb, max_context_len,
+        scale, split_tokens, _stream()), "pkv_paged_decode_attention_store_noalloc")
     return out
 
 

@@ -23,6 +23,7 @@ PKV_DEVERR_BLOCK_ID = 0x2
 PKV_DEVERR_CONTEXT_LEN = 0x4
 PKV_DEVERR_SEQLENS = 0x8
 PKV_DEVERR_WAIT = 0x10
+PKV_STATIC_SCRATCH_BYTES = 32 << 20   # fixed device array of the no-allocation entry point
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -54,6 +55,10 @@ PROTOTYPES = {
                                                         _P, _I32, _P, _I32, _I32, _I32, _I32,
                                                         _I32, _I64, _I32, _F, _I32, _P, _SZ,
                                                         _P]),
+    "pkv_paged_decode_attention_store_noalloc": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _P,
+                                                                _P, _I64, _P, _I32, _P, _I32,
+                                                                _I32, _I32, _I32, _I32, _I64,
+                                                                _I32, _F, _I32, _P]),
     "pkv_decode_attention_partial_store": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _P,
                                                           _I32, _P, _I32, _I32, _I32, _I32, _I32,
                                                           _I64, _I32, _F, _I32, _P, _SZ, _P]),

@@ -404,7 +404,7 @@ int decode_attention_combined(void *out, int64_t out_stride, const void *q, int6
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               int64_t num_blocks, int32_t max_context_len, float scale,
                               int32_t split_tokens, void *workspace, size_t workspace_bytes,
-                              bool fused, hipStream_t stream)
+                              bool fused, hipStream_t stream, bool validate_only = false)
 {
     const int64_t os = out_stride ? out_stride : (int64_t)num_q_heads * head_dim;
     if (batch > 0) {
@@ -418,7 +418,7 @@ int decode_attention_combined(void *out, int64_t out_stride, const void *q, int6
                            block_tables, block_table_stride, context_lens, batch, num_q_heads,
                            num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale,
                            split_tokens, workspace, workspace_bytes, fused);
-    if (rc || batch == 0) return rc;
+    if (rc || batch == 0 || validate_only) return rc;
     if (a.num_splits == 1) {
         a.out = static_cast<uint16_t *>(out);
         a.out_stride = os;
@@ -747,6 +747,51 @@ int pkv_paged_decode_attention_store(void *out, int64_t out_stride, const void *
                                      context_lens, batch, num_q_heads, num_kv_heads, head_dim,
                                      block_size, num_blocks, max_context_len, scale, split_tokens,
                                      workspace, workspace_bytes, true, stream);
+}
+
+int pkv_paged_decode_attention_store_noalloc(void *out, int64_t out_stride, const void *q,
+                                             int64_t q_stride, void *k_cache, void *v_cache,
+                                             const void *k_new, const void *v_new,
+                                             int64_t new_token_stride,
+                                             const int32_t *block_tables,
+                                             int32_t block_table_stride,
+                                             const int32_t *context_lens, int32_t batch,
+                                             int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t block_size,
+                                             int64_t num_blocks, int32_t max_context_len,
+                                             float scale, int32_t split_tokens,
+                                             hipStream_t stream)
+{
+    // the size of the partials, checked before any HIP call
+    int rc = check_attention_shape(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   block_table_stride, max_context_len);
+    if (rc) return rc;
+    if ((rc = check_split(split_tokens))) return rc;
+    const int32_t split =
+        effective_split(batch, num_q_heads, num_kv_heads, max_context_len, split_tokens);
+    const size_t need =
+        pkv::split_geometry(batch, num_q_heads, head_dim, max_context_len, split).total_bytes;
+    REQUIRE(need <= PKV_STATIC_SCRATCH_BYTES, PKV_ERR_WORKSPACE,
+            "partials need %zu bytes, more than the library's fixed %u-byte device array; "
+            "use pkv_paged_decode_attention_store with a workspace",
+            need, (unsigned)PKV_STATIC_SCRATCH_BYTES);
+    // every other argument, checked before the first HIP call (the 256-byte
+    // stand-in only passes the workspace checks; nothing is launched)
+    rc = decode_attention_combined(out, out_stride, q, q_stride, k_cache, v_cache, k_new, v_new,
+                                   new_token_stride, block_tables, block_table_stride,
+                                   context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                   block_size, num_blocks, max_context_len, scale, split_tokens,
+                                   reinterpret_cast<void *>(256), PKV_STATIC_SCRATCH_BYTES, true,
+                                   stream, true);
+    if (rc || batch == 0) return rc;
+    void *scratch = nullptr;
+    rc = hip_status(pkv::static_scratch(&scratch), "static scratch address");
+    if (rc) return rc;
+    return decode_attention_combined(out, out_stride, q, q_stride, k_cache, v_cache, k_new, v_new,
+                                     new_token_stride, block_tables, block_table_stride,
+                                     context_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                     block_size, num_blocks, max_context_len, scale, split_tokens,
+                                     scratch, PKV_STATIC_SCRATCH_BYTES, true, stream);
 }
 
 size_t pkv_sampler_workspace_bytes(int32_t batch, int32_t vocab)

@@ -125,6 +125,10 @@ hipError_t launch_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *bloc
 // kernel is ALU-bound beyond group 2 on MI355X).
 constexpr int32_t kMfmaMinGroup = 3;
 
+// The library's fixed device scratch array (PKV_STATIC_SCRATCH_BYTES) on
+// the current device: its device address, resolved on first use per device.
+hipError_t static_scratch(void **out);
+
 // Sampler
 size_t sampler_workspace_bytes(int32_t batch, int32_t vocab);
 hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_stride,

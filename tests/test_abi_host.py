@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.PROTOTYPES)
@@ -188,6 +188,27 @@ def test_fused_attention_validation():
     assert call(ns=8 * 128 - 8) == _lib.PKV_ERR_INVALID_ARG
     assert call(out=None) == _lib.PKV_ERR_INVALID_ARG
     assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
+
+
+def test_noalloc_attention_validation():
+    """The no-allocation entry point checks everything on the host before
+    its first HIP call: partials larger than the fixed device array are
+    refused with PKV_ERR_WORKSPACE, other argument errors as usual."""
+    L = _lib.lib()
+
+    def call(B=64, Hq=16, Hkv=8, max_len=4096, out=FAKE, kn=FAKE, split=0):
+        return L.pkv_paged_decode_attention_store_noalloc(out, 0, FAKE, 0, FAKE, FAKE, kn, FAKE, 0,
+                                                          FAKE, 16, FAKE, B, Hq, Hkv, 128, 256,
+                                                          600, max_len, 0.0, split, None)
+
+    big = L.pkv_decode_workspace_bytes(64, 64, 8, 128, 131072, 0)
+    assert big > _lib.PKV_STATIC_SCRATCH_BYTES
+    assert call(Hq=64, max_len=131072) == _lib.PKV_ERR_WORKSPACE
+    assert b"fixed" in L.pkv_last_error()
+    assert call(out=None) == _lib.PKV_ERR_INVALID_ARG
+    assert call(kn=FAKE + 2) == _lib.PKV_ERR_INVALID_ARG
+    assert call(split=100) == _lib.PKV_ERR_INVALID_ARG
+    assert call(B=0) == _lib.PKV_OK     # nothing to do, no HIP call
 
 
 def test_cascade_validation():
