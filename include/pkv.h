@@ -388,41 +388,40 @@ int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q,
 
 /* ---- sampler --------------------------------------------------------------
  * Next token per row (Grok-1 runners chapter, section 8.3 and 8.3.1;
- * nanochat engine page, section 3; nano-vllm page, "run model"):
+ * nanochat engine page, section 3; nano-vllm page, "run model").  Each row's
+ * own settings decide what runs for it:
  *   temperature <= 0 (or NaN): greedy, the lowest index of max logits.
  *   otherwise, in this order:
  *     s_i = logits_i / T                      (IEEE fp32 division)
  *     top-k  if 0 < k < vocab: keep the k largest s, ties to lower index
+ *            (k <= 0 or k >= vocab: off)
  *     top-p  if p < 1: over the kept set, keep every s_i >= tau where tau is
  *            the smallest value whose strictly-greater mass is <= p of the
  *            kept mass (the ascending-cumsum rule of the page, exact
- *            arithmetic); p <= 0 keeps only the maxima
+ *            arithmetic); p <= 0 keeps only the maxima (p >= 1: off)
  *     id = argmax over kept i of fl32(s_i + gumbel_i), ties to lower index
  * The Gumbel noise is an input (standard Gumbel, fp32), so the draw is
- * reproducible.  Only the ids are written.
+ * reproducible.  Only the ids are written.  Two launches: one pass over the
+ * logits (per-chunk maxima and candidate lists), then one workgroup per row
+ * that selects the cut exactly from the candidates, or, when they cannot be
+ * shown to hold the cut (e.g. k larger than the candidate lists, or many
+ * tokens tied at the cut), from the whole row read again (exact, slower).
  * out_ids      int32 [batch]
  * logits       fp32 [batch][vocab], row b at b*logits_stride (elements)
  * gumbel       fp32 [batch][vocab], row b at b*gumbel_stride; only read
  *              where a token is eligible (unused for greedy rows)
  * temperature, top_p  fp32 [batch];  top_k  int32 [batch]
- * flags        which filters ANY row may use: PKV_SAMPLE_TOPK and/or
- *              PKV_SAMPLE_TOPP.  A filter whose flag is clear is off for
- *              every row whatever its per-row value (its passes are not
- *              launched).
- * vocab        1 .. 2^24
- * workspace    >= pkv_sampler_workspace_bytes(batch, vocab), 256-B aligned */
-#define PKV_SAMPLE_TOPK 1u
-#define PKV_SAMPLE_TOPP 2u
-
+ * vocab        1 .. 2^24;  batch <= 65535
+ * workspace    >= pkv_sampler_workspace_bytes(batch, vocab), 256-B aligned;
+ *              about 3 bytes per logit; contents on entry are ignored */
 size_t pkv_sampler_workspace_bytes(int32_t batch, int32_t vocab);
 
 int pkv_sample_next_token(int32_t *out_ids, const float *logits,
                           int64_t logits_stride, const float *gumbel,
                           int64_t gumbel_stride, const float *temperature,
                           const float *top_p, const int32_t *top_k,
-                          int32_t batch, int32_t vocab, uint32_t flags,
-                          void *workspace, size_t workspace_bytes,
-                          hipStream_t stream);
+                          int32_t batch, int32_t vocab, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /* The sampler with the runner's vocabulary mask and extra outputs (Grok-1
  * runners chapter, section 8.3: sample_token scales by 1/T, replaces the
@@ -447,7 +446,7 @@ int pkv_sample_next_token_ex(int32_t *out_ids, const float *logits,
                              int64_t gumbel_stride, const uint8_t *vocab_mask,
                              int64_t mask_stride, const float *temperature,
                              const float *top_p, const int32_t *top_k,
-                             int32_t batch, int32_t vocab, uint32_t flags,
+                             int32_t batch, int32_t vocab,
                              float *out_prob, int32_t *out_top_ids,
                              float *out_top_probs, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);

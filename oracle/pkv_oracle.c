@@ -430,8 +430,10 @@ int32_t oracle_sample_row_ex(const float *logits, const float *gumbel,
         float tau;
         double margin = 0.0;
         if (!(top_p > 0.0f)) {
-            /* p <= 0: only the maxima stay eligible */
+            /* p <= 0: only the maxima stay eligible; no mass is compared,
+             * so no rounding can move the cut */
             tau = asc[n - 1];
+            margin = INFINITY;
         } else {
             double mx = asc[n - 1];
             double z = 0.0;

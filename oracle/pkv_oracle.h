@@ -118,7 +118,8 @@ typedef struct {
     float kth;           /* k-th largest scaled logit (if top-k applied) */
     double margin;       /* distance of 1-p from the nearest cumulative-mass
                             boundary around tau (normalised mass units);
-                            0 when the cut had no crossing */
+                            0 when the cut had no crossing; +inf for
+                            p <= 0 (the maxima: no mass is compared) */
 } oracle_sample_info;
 
 /* Next-token sampler for one row, in the Grok-1 runner's order

@@ -15,7 +15,7 @@ import torch
 
 from . import _lib
 from ._lib import (PKV_DEVERR_BLOCK_ID, PKV_DEVERR_CONTEXT_LEN, PKV_DEVERR_SEQLENS,
-                   PKV_DEVERR_SLOT, PKV_DEVERR_WAIT, PKV_SAMPLE_TOPK, PKV_SAMPLE_TOPP, PkvError,
+                   PKV_DEVERR_SLOT, PKV_DEVERR_WAIT, PkvError,
                    check, lib)
 
 __all__ = [
@@ -26,7 +26,6 @@ __all__ = [
     "varlen_slot_mapping", "varlen_paged_attention",
     "sample_next_token", "sample_next_token_ex", "sampler_workspace_bytes", "PkvError",
     "varlen_split_tokens", "varlen_workspace_bytes",
-    "PKV_SAMPLE_TOPK", "PKV_SAMPLE_TOPP",
     "set_error_word", "set_wait_limit", "paged_decode_attention_store_noalloc", "PKV_DEVERR_SLOT", "PKV_DEVERR_BLOCK_ID",
     "PKV_DEVERR_CONTEXT_LEN", "PKV_DEVERR_SEQLENS", "PKV_DEVERR_WAIT",
 ]
@@ -298,16 +297,14 @@ def sampler_workspace_bytes(batch: int, vocab: int) -> int:
 
 
 def sample_next_token(logits: torch.Tensor, gumbel: torch.Tensor, temperature: torch.Tensor,
-                      top_p: torch.Tensor, top_k: torch.Tensor, flags: Optional[int] = None,
+                      top_p: torch.Tensor, top_k: torch.Tensor,
                       out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """int32 [B] next-token ids.  flags: which filters any row may use
-    (PKV_SAMPLE_TOPK | PKV_SAMPLE_TOPP); None enables both."""
+    """int32 [B] next-token ids; each row's own temperature, top_p and top_k
+    decide its filters."""
     B, V = logits.shape
     if logits.stride(1) != 1 or gumbel.stride(1) != 1 or gumbel.shape != logits.shape:
         raise ValueError("logits/gumbel must be [B, V] with unit element stride")
-    if flags is None:
-        flags = PKV_SAMPLE_TOPK | PKV_SAMPLE_TOPP
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=logits.device)
     ws = _workspace(sampler_workspace_bytes(B, V), logits.device, workspace)
@@ -315,14 +312,14 @@ def sample_next_token(logits: torch.Tensor, gumbel: torch.Tensor, temperature: t
         _dev(out, "out", torch.int32), _dev(logits, "logits", torch.float32), logits.stride(0),
         _dev(gumbel, "gumbel", torch.float32), gumbel.stride(0),
         _dev(temperature, "temperature", torch.float32), _dev(top_p, "top_p", torch.float32),
-        _dev(top_k, "top_k", torch.int32), B, V, flags, ws.data_ptr(), ws.numel(), _stream()),
+        _dev(top_k, "top_k", torch.int32), B, V, ws.data_ptr(), ws.numel(), _stream()),
         "pkv_sample_next_token")
     return out
 
 
 def sample_next_token_ex(logits: torch.Tensor, gumbel: torch.Tensor, temperature: torch.Tensor,
                          top_p: torch.Tensor, top_k: torch.Tensor,
-                         mask: Optional[torch.Tensor] = None, flags: Optional[int] = None,
+                         mask: Optional[torch.Tensor] = None,
                          extras: bool = True, out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None):
     """Next-token ids with the vocabulary mask (uint8/bool [B, V], nonzero =
@@ -332,8 +329,6 @@ def sample_next_token_ex(logits: torch.Tensor, gumbel: torch.Tensor, temperature
     B, V = logits.shape
     if logits.stride(1) != 1 or gumbel.stride(1) != 1 or gumbel.shape != logits.shape:
         raise ValueError("logits/gumbel must be [B, V] with unit element stride")
-    if flags is None:
-        flags = PKV_SAMPLE_TOPK | PKV_SAMPLE_TOPP
     mptr, mstride = None, 0
     if mask is not None:
         if mask.dtype == torch.bool:
@@ -353,7 +348,7 @@ def sample_next_token_ex(logits: torch.Tensor, gumbel: torch.Tensor, temperature
         _dev(out, "out", torch.int32), _dev(logits, "logits", torch.float32), logits.stride(0),
         _dev(gumbel, "gumbel", torch.float32), gumbel.stride(0), mptr, mstride,
         _dev(temperature, "temperature", torch.float32), _dev(top_p, "top_p", torch.float32),
-        _dev(top_k, "top_k", torch.int32), B, V, flags,
+        _dev(top_k, "top_k", torch.int32), B, V,
         None if prob is None else prob.data_ptr(), None if top_ids is None else top_ids.data_ptr(),
         None if top_probs is None else top_probs.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
         "pkv_sample_next_token_ex")

@@ -15,8 +15,6 @@ PKV_ERR_INVALID_ARG = -1
 PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
-PKV_SAMPLE_TOPK = 1
-PKV_SAMPLE_TOPP = 2
 # device error word bits (include/pkv.h)
 PKV_DEVERR_SLOT = 0x1
 PKV_DEVERR_BLOCK_ID = 0x2
@@ -73,10 +71,10 @@ PROTOTYPES = {
                                                   _I32, _I32, _I32, _I32, _I32, _I32, _I64, _I32,
                                                   _I32, _F, _I32, _P, _SZ, _P]),
     "pkv_sampler_workspace_bytes": (_SZ, [_I32, _I32]),
-    "pkv_sample_next_token": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _U32,
-                                             _P, _SZ, _P]),
+    "pkv_sample_next_token": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _P, _P, _I32, _I32, _P,
+                                             _SZ, _P]),
     "pkv_sample_next_token_ex": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _I32,
-                                                _I32, _U32, _P, _P, _P, _P, _SZ, _P]),
+                                                _I32, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None

@@ -803,15 +803,13 @@ size_t pkv_sampler_workspace_bytes(int32_t batch, int32_t vocab)
 int pkv_sample_next_token_ex(int32_t *out_ids, const float *logits, int64_t logits_stride,
                              const float *gumbel, int64_t gumbel_stride, const uint8_t *vocab_mask,
                              int64_t mask_stride, const float *temperature, const float *top_p,
-                             const int32_t *top_k, int32_t batch, int32_t vocab, uint32_t flags,
+                             const int32_t *top_k, int32_t batch, int32_t vocab,
                              float *out_prob, int32_t *out_top_ids, float *out_top_probs,
                              void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     REQUIRE(batch >= 0 && batch <= 65535, PKV_ERR_INVALID_ARG, "batch must be in [0, 65535]");
     REQUIRE(vocab > 0 && vocab <= (1 << 24), PKV_ERR_UNSUPPORTED,
             "vocab %d unsupported (1 .. 2^24)", vocab);
-    REQUIRE((flags & ~(PKV_SAMPLE_TOPK | PKV_SAMPLE_TOPP)) == 0, PKV_ERR_INVALID_ARG,
-            "unknown flag bits 0x%x", flags);
     const int64_t ls = logits_stride ? logits_stride : vocab;
     const int64_t gs = gumbel_stride ? gumbel_stride : vocab;
     const int64_t ms = mask_stride ? mask_stride : vocab;
@@ -832,20 +830,19 @@ int pkv_sample_next_token_ex(int32_t *out_ids, const float *logits, int64_t logi
     REQUIRE(workspace_bytes >= need, PKV_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes",
             workspace_bytes, need);
     return hip_status(pkv::launch_sampler(out_ids, logits, ls, gumbel, gs, vocab_mask, ms,
-                                          temperature, top_p, top_k, batch, vocab, flags,
-                                          out_prob, out_top_ids, out_top_probs, workspace, stream),
+                                          temperature, top_p, top_k, batch, vocab, out_prob,
+                                          out_top_ids, out_top_probs, workspace, stream),
                       "sampler launch");
 }
 
 int pkv_sample_next_token(int32_t *out_ids, const float *logits, int64_t logits_stride,
                           const float *gumbel, int64_t gumbel_stride, const float *temperature,
                           const float *top_p, const int32_t *top_k, int32_t batch, int32_t vocab,
-                          uint32_t flags, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream)
+                          void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     return pkv_sample_next_token_ex(out_ids, logits, logits_stride, gumbel, gumbel_stride,
-                                    nullptr, 0, temperature, top_p, top_k, batch, vocab, flags,
-                                    nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+                                    nullptr, 0, temperature, top_p, top_k, batch, vocab, nullptr,
+                                    nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

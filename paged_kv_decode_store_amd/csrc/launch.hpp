@@ -134,8 +134,8 @@ size_t sampler_workspace_bytes(int32_t batch, int32_t vocab);
 hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_stride,
                           const float *gumbel, int64_t gumbel_stride, const uint8_t *mask,
                           int64_t mask_stride, const float *temperature, const float *top_p,
-                          const int32_t *top_k, int32_t batch, int32_t vocab, uint32_t flags,
-                          float *out_prob, int32_t *out_top_ids, float *out_top_probs,
-                          void *workspace, hipStream_t stream);
+                          const int32_t *top_k, int32_t batch, int32_t vocab, float *out_prob,
+                          int32_t *out_top_ids, float *out_top_probs, void *workspace,
+                          hipStream_t stream);
 
 }  // namespace pkv

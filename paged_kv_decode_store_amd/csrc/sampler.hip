@@ -1,42 +1,38 @@
 // Next-token sampler: temperature, top-k, nucleus (top-p) and a Gumbel-max
-// draw, on fp32 logits [B][V].
+// draw, on fp32 logits [B][V], in two launches.
 //
-// Row-parallel passes split each row into chunks of `chunk` logits, one
-// 256-thread workgroup per (chunk, row).  Each thread first loads its whole
-// share of the chunk into registers (float4 when rows are 16-byte aligned).
-// The scaled logit is s = z / T, an IEEE fp32 division; since that division
-// is monotone in z for T > 0, only the bins pass divides every logit.
+// scan   (one 256-thread workgroup per (chunk, row); the one pass over the
+//        logits).  Greedy and unfiltered rows reduce their chunk to a best
+//        packed key (the unfiltered ones read the noise too: every token is
+//        eligible).  Filtered rows compute s = z / T, the chunk max M_c and
+//        a histogram of 2048 value bins of width 1/32 below M_c, and from
+//        it a candidate list: the tokens of the top bins, as many bins as
+//        fit in the list (nucleus rows), or just enough to hold k (top-k)
+//        or the maxima (p <= 0).  Every token of a listed bin is larger
+//        than every unlisted one, so the chunk also records the largest
+//        value it left out and, for nucleus rows, the mass of what it left
+//        out (relative to M_c).
+// finish (one 1024-thread workgroup per row).  With T* the largest value
+//        left out by any chunk, the lists hold every token of the row with
+//        s > T*.  Their exact masses exp(s - M) (fp64, then 2^-38 fixed
+//        point: sums are order independent and bit-reproducible) plus the
+//        left-out masses give Z.  The top-k cut is a radix select on (s,
+//        then index) among the tokens above T*; the nucleus cut a radix
+//        select by mass on s (the smallest value whose strictly-greater
+//        mass is within p of the kept mass); both are exact.  They are
+//        valid when the cut lies above T* (checked: at least k tokens above
+//        T*, or more than p of the mass above T*); otherwise the same
+//        selections run over the whole row, read again from memory, which
+//        is slow but exact.  The Gumbel argmax over the kept tokens reads
+//        their noise only.
 //
-// Rows with a top-k or nucleus filter take three passes over their logits:
-//   max     the row max M of s, as (max allowed z) / T
-//   bins    a histogram over 2048 value bins of width 1/32 below M
-//           (bin = floor(fl(M - s) * 32), the last bin catching everything
-//           >= 64 below M), with counts and the mass exp(s - M) in 2^-40
-//           fixed point: exact, order independent and identical from run
-//           to run
-//   collect every logit in a bin above the threshold bin is eligible: its
-//           Gumbel key fl32(s + g) joins a max of the packed 64-bit
-//           (key, ~index) (ties to the lowest index); the logits of the
-//           threshold bin itself are appended to a per-row candidate list.
-//           Both classes are upper sets of z, so a logit is classified by
-//           two thresholds on z that `select` finds by bisection, and s is
-//           computed only for the logits that join the list.
-// and two per-row kernels: `select` finds the threshold bin from the
-// histogram, `resolve` ranks the candidates (by counting when there are at
-// most 512, else by a bitonic sort in LDS) and fixes the exact cut inside
-// that bin (by rank for top-k, by strictly-greater mass for the nucleus),
-// then writes the id.  Top-k followed by the nucleus may need one more
-// collect/resolve round when the nucleus cut lies above the top-k bin.  If a
-// threshold bin holds more candidates than the list, `resolve` finds the cut
-// exactly by scanning the row itself (radix select on the key).
-//
-// Greedy rows (T <= 0) and rows without a filter need only the collect pass.
-// Passes communicate only through kernel boundaries: no workgroup waits for
-// or fences against another one inside a kernel.  Per-chunk results (row
-// max, best Gumbel key) go to per-chunk slots that the next kernel reduces,
-// so no pass needs memory cleared beforehand except the histograms, which
-// the max pass clears.
+// Workgroups communicate only through the kernel boundary: no workgroup
+// waits for or fences against another one, and no workspace memory needs
+// clearing (every per-chunk record and list is fully written by its scan
+// workgroup; the finish workgroup builds its row's buffers itself).
 #include <math.h>
+
+#include <type_traits>
 
 #include "launch.hpp"
 #include "pkv_device.hpp"
@@ -45,19 +41,21 @@ namespace pkv {
 
 namespace {
 
-constexpr int kThreads = 256;           // row-parallel passes
-constexpr int kRThreads = 512;          // per-row select / resolve
-constexpr int kBins = 2048;             // value bins below the row max
+constexpr int kThreads = 256;           // scan kernel
+constexpr int kFThreads = 1024;         // finish kernel: one workgroup per row
+constexpr int kRThreads = 512;          // extra outputs: one workgroup per row
+constexpr int kBins = 2048;             // value bins below the chunk max
 constexpr float kBinsPerUnit = 32.f;    // bin width: 1/32 of a logit unit
-constexpr int kCap = 4096;              // threshold-bin candidates kept per row
-constexpr int kMaxPer = 32;             // logits per thread per chunk (bit masks: <= 32)
-constexpr int kDigits = 2048;           // radix digits of the exact in-row fallback
-constexpr int kMinGroups = 256;         // row-parallel workgroups wanted (one per CU)
-constexpr int kList = 1024;             // compacted noise reads per collect workgroup
-constexpr uint32_t kCandBit = 0x80000000u;
-constexpr uint32_t kKeptBit = 0x40000000u;
-constexpr uint32_t kIndexMask = 0x3fffffffu;  // vocab < 2^30
-constexpr uint32_t kSlotMasked = 0x80000000u; // list entry of a forbidden logit
+constexpr int kMaxPer = 16;             // logits per thread per chunk (more: register spills)
+constexpr int kMinGroups = 256;         // scan workgroups wanted (one per CU)
+constexpr int kListDiv = 8;             // list capacity per chunk: chunk / kListDiv
+constexpr int kMaxChunks = 4096;        // vocab <= 2^24 in chunks of 4096
+constexpr int kDigits = 4096;           // radix digits per level (<= 12 bits)
+constexpr int kHBins = 1024;            // finish-side value bins (the last one takes the rest)
+constexpr int kGroups = 8;              // histogram workgroups per row (at most)
+constexpr int kGroupChunks = kMaxChunks / kGroups;   // chunks of one group (at most)
+constexpr int kHBatch = 16;             // list slots per thread whose loads are issued together
+constexpr double kMassUnit = 0x1p38;    // fixed-point masses: 2^-38 of the row max's
 
 enum : uint32_t {
     MODE_GREEDY = 1,     // T <= 0: lowest index of the max raw logit
@@ -65,28 +63,59 @@ enum : uint32_t {
     MODE_TOPK = 4,
     MODE_TOPP = 8,
     MODE_TOPP_MAX = 16,  // p <= 0: only the maxima are eligible
-    MODE_DONE = 32,      // id written
 };
 
-struct alignas(64) SampCtl {
-    unsigned long long Z;     // eligible mass, 2^-40 units
-    unsigned long long A;     // mass of the bins above the threshold bin
-    uint32_t max_key;         // key of max s
-    uint32_t mode;
-    uint32_t k;               // top-k
-    uint32_t jstar;           // threshold bin
-    uint32_t rank;            // top-k: logits of the threshold bin to keep
-    uint32_t ncand;           // logits of the threshold bin appended
-    uint32_t round2;          // 1 while a second collect round is pending
-    uint32_t tau;             // final cut: kept logits have key(s) >= tau (0: none)
-    unsigned long long kpack; // top-k cut: kept have (key, ~index) >= kpack (0: none)
+// One scan workgroup's result for its chunk.
+struct alignas(32) ChunkRec {
+    uint32_t mkey;             // key of the chunk max of s (filtered rows)
+    uint32_t outkey;           // key of the largest s left out of the list (0: none)
+    uint32_t n;                // tokens listed
+    uint32_t pad;
+    double zx;                 // mass of the tokens left out, exp(s - M_c) summed
+    unsigned long long best;   // greedy / unfiltered rows: best packed key of the chunk
 };
-static_assert(sizeof(SampCtl) == 64, "control block");
+static_assert(sizeof(ChunkRec) == 32, "chunk record");
+
+// The final cut of a row, for the extra outputs: kept tokens have
+// key(s) >= tau and, for top-k, (key, ~index) >= kpack.
+struct alignas(16) RowCut {
+    uint32_t mode;
+    uint32_t tau;
+    unsigned long long kpack;
+};
+
+// Totals of one histogram workgroup's share of a row (integer sums: the
+// row's totals do not depend on the order they are added in).
+struct alignas(32) RowTot {
+    unsigned long long Z;    // mass of its tokens (2^-38 units of the row max's)
+    unsigned long long mu;   // mass of its listed tokens above T*
+    uint32_t nu;             // its listed tokens above T*
+    uint32_t pad[3];
+};
+static_assert(sizeof(RowTot) == 32, "row totals");
+
+// One histogram group's share of a finish-side value bin.
+struct alignas(8) BinRec {
+    uint32_t cnt;              // the group's listed tokens above T* in the bin
+    uint32_t off;              // ... in the bins before it (where the bin starts
+                               // in the group's bin-sorted tokens)
+    unsigned long long mass;   // mass of the bin's tokens (nucleus rows)
+    unsigned long long above;  // best Gumbel key of the group's tokens in the
+                               // bins before it (0: none)
+};
+static_assert(sizeof(BinRec) == 24, "bin record");
+
+// A listed token above T* with its noise, in a group's bin-sorted array.
+struct alignas(16) SortedTok {
+    unsigned long long packed;
+    float g;
+    uint32_t pad;
+};
 
 struct SampLayout {
-    int32_t chunk;
-    int32_t nchunks;
-    size_t ctl_off, cnt_off, mass_off, cand_off, kap_off, pmax_off, pbest_off, total;
+    int32_t chunk, nchunks, cap, groups;
+    int32_t gslots;   // bin-sorted tokens per group (at most)
+    size_t rec_off, list_off, bins_off, sorted_off, tot_off, cut_off, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -94,26 +123,29 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 SampLayout sampler_layout(int32_t batch, int32_t vocab)
 {
     SampLayout L;
-    // the largest chunk that still gives kMinGroups workgroups per pass
+    // the largest chunk that still gives kMinGroups scan workgroups
     int32_t chunk = kMaxPer * kThreads;
     while (chunk > 4 * kThreads && (int64_t)batch * ((vocab + chunk - 1) / chunk) < kMinGroups) chunk >>= 1;
     L.chunk = chunk;
     L.nchunks = (vocab + chunk - 1) / chunk;
+    L.cap = chunk / kListDiv;
+    L.groups = L.nchunks < kGroups ? L.nchunks : kGroups;
+    const size_t slots = (size_t)batch * L.nchunks * L.cap;
     size_t off = 0;
-    L.ctl_off = off;
-    off = align256(off + (size_t)batch * sizeof(SampCtl));
-    L.cnt_off = off;
-    off = align256(off + (size_t)batch * kBins * sizeof(uint32_t));
-    L.mass_off = off;
-    off = align256(off + (size_t)batch * kBins * sizeof(unsigned long long));
-    L.cand_off = off;
-    off = align256(off + (size_t)batch * kCap * sizeof(unsigned long long));
-    L.kap_off = off;
-    off = align256(off + (size_t)batch * kCap * sizeof(uint32_t));
-    L.pmax_off = off;
-    off = align256(off + (size_t)batch * L.nchunks * sizeof(uint32_t));
-    L.pbest_off = off;
-    off = align256(off + (size_t)batch * L.nchunks * sizeof(unsigned long long));
+    L.rec_off = off;
+    off = align256(off + (size_t)batch * L.nchunks * sizeof(ChunkRec));
+    L.list_off = off;
+    off = align256(off + slots * sizeof(unsigned long long));
+    // per row and histogram group: value bins, bin-sorted tokens, totals
+    L.gslots = (L.nchunks + L.groups - 1) / L.groups * L.cap;
+    L.bins_off = off;
+    off = align256(off + (size_t)batch * L.groups * kHBins * sizeof(BinRec));
+    L.sorted_off = off;
+    off = align256(off + (size_t)batch * L.groups * L.gslots * sizeof(SortedTok));
+    L.tot_off = off;
+    off = align256(off + (size_t)batch * L.groups * sizeof(RowTot));
+    L.cut_off = off;
+    off = align256(off + (size_t)batch * sizeof(RowCut));
     L.total = off;
     return L;
 }
@@ -127,15 +159,13 @@ struct SampArgs {
     const float *temperature;
     const float *top_p;
     const int32_t *top_k;
-    int32_t batch, vocab, chunk, nchunks;
-    uint32_t flags;
-    SampCtl *ctl;
-    uint32_t *cnt;                 // [B][kBins]
-    unsigned long long *mass;      // [B][kBins]
-    unsigned long long *cand;      // [B][kCap]  (key << 32) | ~index
-    uint32_t *kap;                 // [B][kCap]  key of fl32(s + g)
-    uint32_t *part_max;            // [B][nchunks] key of the chunk max of s
-    unsigned long long *part_best; // [B][nchunks] best packed Gumbel key of the chunk
+    int32_t batch, vocab, chunk, nchunks, cap, groups, gslots;
+    ChunkRec *rec;                 // [B][nchunks]
+    unsigned long long *list;      // [B][nchunks][cap]  (key << 32) | ~index
+    BinRec *bins;                  // [B][groups][kHBins]
+    SortedTok *sorted;             // [B][groups][gslots]
+    RowTot *tot;                   // [B][groups]
+    RowCut *cut;                   // [B]
     const uint8_t *mask;           // [B][V] (row b at b*mstride), 0 = forbidden; or null
     int64_t mstride;
     float *out_prob;               // [B] probability of the drawn id, or null
@@ -176,96 +206,127 @@ __device__ __forceinline__ uint32_t unpack_index(unsigned long long v)
     return 0xffffffffu - (uint32_t)(v & 0xffffffffull);
 }
 
-// exp(s - M) in 2^-40 fixed point, by the hardware base-2 exponential.  The
-// rounding errors of d = s - M (TwoSum) and of d * log2(e) (FMA residual)
-// are recovered exactly and folded in to first order.  The fixed-point value
-// is assembled from two 20-bit halves (w < 2, so w * 2^40 < 2^41).
-__device__ __forceinline__ unsigned long long mass_fixed(float s, float M)
-{
-    constexpr float kLog2e = 1.44269504088896341f;
-    constexpr float kLn2 = 0.693147180559945309f;
-    const float d = s - M;
-    const float bb = d - s;
-    const float e = (s - (d - bb)) + (-M - bb);
-    const float x = d * kLog2e;
-    const float xe = fmaf(d, kLog2e, -x);
-    float w = __builtin_amdgcn_exp2f(x);
-    w = fmaf(w, fmaf(xe, kLn2, e), w);
-    const float hi = floorf(w * 1048576.0f);             // w * 2^20, integer part
-    const float lo = (w * 1048576.0f - hi) * 1048576.0f; // exact remainder, * 2^20
-    return ((unsigned long long)(uint32_t)hi << 20) + (uint32_t)lo;
-}
-
-// Value bin below the row max M: monotone non-increasing in s (rounding of
-// M - s is monotone, the scale is a power of two).
+// Value bin below the chunk max M: monotone non-increasing in s (rounding of
+// M - s is monotone, the scale is a power of two); NaN lands in the last bin.
 __device__ __forceinline__ int bin_of(float s, float M)
 {
     const float d = (M - s) * kBinsPerUnit;
     return d < (float)(kBins - 1) ? (int)d : kBins - 1;
 }
 
-// One wave: the smallest z, in key order over the non-NaN floats, at which a
-// monotone predicate (false below some z, true from there up) holds; -inf if
-// it holds everywhere, NaN if nowhere.  64 probes per step narrow the key
-// interval (lo, hi] about 64-fold, so a 32-bit key takes six steps.
-template <typename Pred>
-__device__ float wave_first_z(Pred pred)
+// The finish-side bin: as bin_of, with everything from kHBins - 1 bins down
+// in the last one.
+__device__ __forceinline__ int hbin_of(float s, float M)
 {
-    const float inf = __builtin_huge_valf();
-    if (pred(-inf)) return -inf;
-    if (!pred(inf)) return __builtin_nanf("");
-    uint32_t lo = float_key(-inf), hi = float_key(inf);  // pred(lo) false, pred(hi) true
-    const int lane = (int)threadIdx.x & 63;
-    while (hi - lo > 1u) {
-        const uint32_t probe = lo + (uint32_t)(((unsigned long long)(hi - lo) * (unsigned)(lane + 1)) >> 6);
-        const unsigned long long t = __ballot(pred(key_float(probe)));  // lane 63 probes hi: true
-        const int f = __builtin_ctzll(t);
-        const uint32_t nlo = (uint32_t)__shfl((int)probe, f > 0 ? f - 1 : 0);
-        hi = (uint32_t)__shfl((int)probe, f);
-        if (f > 0) lo = nlo;
-    }
-    return key_float(hi);
+    const float d = (M - s) * kBinsPerUnit;
+    return d < (float)(kHBins - 1) ? (int)d : kHBins - 1;
 }
 
-// Thresholds on the raw logit z equivalent to "bin of z / T below j"
-// (out[0]) and "bin of z / T at most j" (out[1]): division by T > 0 is
-// monotone and bin_of is monotone in s, so each class is an upper set of z.
-// (-0 and +0 fall in the same bin, so a float comparison with the threshold
-// decides as the bin does.)  Wave 0 finds the first, wave 1 the second.
-__device__ void z_thresholds(float T, float M, int j, float *out)
+// exp(s - M) for s <= M, good to ~2e-7 relative however far s lies below M:
+// s - M is exact in double, its base-2 exponent is split into an integer
+// and a fraction in [0, 1) (both exact), and only the fraction goes through
+// the fp32 exponential.  0 below 2^-200 (and for NaN).
+__device__ __forceinline__ float mass_approx(float s, double M)
 {
-    const int w = (int)threadIdx.x >> 6;
-    if (w > 1) return;
-    const int lim = w == 0 ? j : j + 1;
-    const float z0 = wave_first_z([=](float z) { return bin_of(z / T, M) < lim; });
-    if ((threadIdx.x & 63) == 0) out[w] = z0;
+    const double x = ((double)s - M) * 1.4426950408889634;
+    if (!(x > -200.0)) return 0.f;
+    const double fl = floor(x);
+    return ldexpf(__builtin_amdgcn_exp2f((float)(x - fl)), (int)fl);
+}
+
+// exp(s - M) for s <= M in fp64, to ~1e-14 relative: s - M is exact in
+// double; with x = (s - M) log2(e) = e + j/64 + r (integers e, j in [0, 64),
+// |r| <= 1/128), 2^x = 2^e * 2^(j/64) * exp(r ln 2), the middle factor from
+// a 64-entry table of 2^(j/64) and the last from its Taylor series to the
+// 6th power (remainder below 1e-19).  0 below 2^-1000 (and for NaN).
+__device__ __forceinline__ double exp_below(double d, const double *tab)
+{
+    const double x = d * 1.4426950408889634;
+    if (!(x > -1000.0)) return 0.0;
+    const double k = rint(x * 64.0);
+    const int ki = (int)k;
+    const double y = (x - k * 0.015625) * 0.69314718055994531;
+    double p = 1.0 + y * (1.0 / 6.0);
+    p = 1.0 + y * (1.0 / 5.0) * p;
+    p = 1.0 + y * (1.0 / 4.0) * p;
+    p = 1.0 + y * (1.0 / 3.0) * p;
+    p = 1.0 + y * (1.0 / 2.0) * p;
+    p = 1.0 + y * p;
+    return ldexp(tab[ki & 63] * p, ki >> 6);
+}
+
+// exp(s - M) in 2^-38 fixed point (round to nearest): each term within
+// 2^-39 of exact, sums order independent.
+__device__ __forceinline__ float value_of(unsigned long long packed)
+{
+    return key_float((uint32_t)(packed >> 32));
+}
+
+__device__ __forceinline__ unsigned long long mass_fixed(float s, double M, const double *tab)
+{
+    return (unsigned long long)(exp_below((double)s - M, tab) * kMassUnit + 0.5);
 }
 
 // Block-wide reductions and scans: within each wave by lane shuffles, then
 // one exchange of the per-wave results through `scratch` (>= NT / 64
 // entries).  Every thread gets the result; `scratch` is free again on return.
+// Wave-wide sum and max: four DPP steps within each row of 16 lanes (quad
+// permutations 1032 and 2301, half-row mirror, row mirror), then the four
+// row results read as scalars.  Every lane of the wave must be active (all
+// callers are in wave-uniform control flow); every lane gets the result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_t(T v)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit lanes");
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+    } else {
+        const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+        const unsigned long long lo = dpp_u32<CTRL>((uint32_t)u);
+        const unsigned long long hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+        return __builtin_bit_cast(T, (hi << 32) | lo);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T readlane_t(T v, int lane)
+{
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+    } else {
+        const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+        const unsigned long long lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+        const unsigned long long hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+        return __builtin_bit_cast(T, (hi << 32) | lo);
+    }
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce_t(T v, Op op)
+{
+    v = op(v, dpp_t<0xB1>(v));    // quad_perm 1,0,3,2
+    v = op(v, dpp_t<0x4E>(v));    // quad_perm 2,3,0,1
+    v = op(v, dpp_t<0x141>(v));   // row_half_mirror
+    v = op(v, dpp_t<0x140>(v));   // row_mirror
+    return op(op(readlane_t(v, 0), readlane_t(v, 16)), op(readlane_t(v, 32), readlane_t(v, 48)));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum_t(T v)
 {
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m);
-    return v;
+    return wave_reduce_t(v, [](T x, T y) { return x + y; });
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_max_t(T v)
 {
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1) v = max(v, __shfl_xor(v, m));
-    return v;
-}
-
-// Sum over aligned groups of q consecutive lanes (q a power of two <= 64).
-template <typename T>
-__device__ __forceinline__ T group_sum_lanes(T v, int q)
-{
-    for (int m = 1; m < q; m <<= 1) v += __shfl_xor(v, m);
-    return v;
+    return wave_reduce_t(v, [](T x, T y) { return max(x, y); });
 }
 
 template <typename T, int NT>
@@ -296,14 +357,38 @@ __device__ T block_max(T v, T *scratch)
     return r;
 }
 
-// Inclusive scan over the threads in ascending order.
-template <typename T, int NT>
+// Inclusive scan over the threads in ascending order (REV: descending, i.e.
+// thread t gets the sum over threads t .. NT-1).
+// Two block-wide maxima of 32-bit values with one exchange.
+template <int NT>
+__device__ __forceinline__ void block_max2(uint32_t x, uint32_t y, unsigned long long *scratch,
+                                           uint32_t &mx, uint32_t &my)
+{
+    x = wave_max_t(x);
+    y = wave_max_t(y);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = ((unsigned long long)x << 32) | y;
+    __syncthreads();
+    mx = 0;
+    my = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const unsigned long long s = scratch[w];
+        mx = max(mx, (uint32_t)(s >> 32));
+        my = max(my, (uint32_t)s);
+    }
+    __syncthreads();
+}
+
+template <typename T, int NT, bool REV = false>
 __device__ T block_scan_inclusive(T v, T *scratch)
 {
-    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+    const int tid = REV ? NT - 1 - (int)threadIdx.x : (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    // lanes of a wave in scan order: REV reverses the lane order too
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const T u = __shfl_up(v, (unsigned)off);
+        const T u = REV ? __shfl_down(v, (unsigned)off) : __shfl_up(v, (unsigned)off);
         if (lane >= off) v += u;
     }
     __syncthreads();
@@ -408,22 +493,20 @@ struct Tile {
     }
 };
 
-// Calls f(j) for each element j of this thread's share of the chunk
-// [i0, i1): without per-element range checks for a full chunk.
-template <bool VEC4, typename F>
-__device__ __forceinline__ void for_each_elem(int i0, int i1, int per, F f)
+// Bit j set when element j of this thread's share lies in the chunk [i0, i1).
+template <bool VEC4>
+__device__ __forceinline__ uint32_t in_chunk_bits(int i0, int i1, int per)
 {
-    if (Tile<VEC4>::full(i0, i1, per)) {
+    if (Tile<VEC4>::full(i0, i1, per)) return 0xffffffffu;
+    uint32_t bits = 0;
 #pragma unroll
-        for (int j = 0; j < kMaxPer; ++j) f(j);
-    } else {
-#pragma unroll
-        for (int j = 0; j < kMaxPer; ++j)
-            if (j < per && Tile<VEC4>::index(i0, j) < i1) f(j);
-    }
+    for (int j = 0; j < kMaxPer; ++j)
+        bits |= ((j < per && Tile<VEC4>::index(i0, j) < i1) ? 1u : 0u) << j;
+    return bits;
 }
 
-// What a row needs, from its own settings and the enabled filters.
+// What a row needs, from its own settings: 0 < k < V turns top-k on, p < 1
+// the nucleus (p <= 0: the maxima only), T <= 0 (or NaN) means greedy.
 __device__ __forceinline__ uint32_t row_mode(const SampArgs &a, int b)
 {
     const float T = a.temperature[b];
@@ -431,862 +514,1086 @@ __device__ __forceinline__ uint32_t row_mode(const SampArgs &a, int b)
     const int32_t k = a.top_k[b];
     const float p = a.top_p[b];
     uint32_t mode = 0;
-    if ((a.flags & 1u) && k > 0 && k < a.vocab) mode |= MODE_TOPK;
-    if ((a.flags & 2u) && p < 1.f) {
-        if (!(p > 0.f)) return MODE_TOPP_MAX;  // the maxima are always in the top k
-        mode |= MODE_TOPP;
-    }
+    if (k > 0 && k < a.vocab) mode |= MODE_TOPK;
+    if (p < 1.f) mode |= (p > 0.f) ? MODE_TOPP : MODE_TOPP_MAX;
     return mode ? mode : MODE_PLAIN;
 }
 
-// First pass of filtered sampling: per-chunk max of s.  Chunk 0 of each row
-// also sets up the row's control block, and the chunks of a filtered row
-// clear its histogram between them.
-template <bool VEC4, bool MASK>
-__global__ __launch_bounds__(kThreads) void samp_max_kernel(const SampArgs a)
+// ---- scan ------------------------------------------------------------------
+
+// Element j of this thread's share of a chunk starting at i0 (PER per
+// thread; VEC4: float4 groups).
+template <bool VEC4>
+__device__ __forceinline__ int elem_index(int i0, int j)
 {
-    const int b = blockIdx.y;
-    const int i0 = blockIdx.x * a.chunk;
-    const int i1 = min(a.vocab, i0 + a.chunk);
-    const int per = a.chunk / kThreads;
-    // issued before the row's settings are known, so that the two overlap
-    Tile<VEC4> t;
-    t.template load<true>(a.logits + (int64_t)b * a.lstride, i0, i1, per);
-    t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
-    const uint32_t mode = row_mode(a, b);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        SampCtl c = {};
-        c.mode = mode;
-        c.k = (uint32_t)a.top_k[b];
-        c.jstar = kBins;
-        a.ctl[b] = c;
-    }
-    if (!(mode & (MODE_TOPK | MODE_TOPP | MODE_TOPP_MAX))) return;
-    if (mode & (MODE_TOPK | MODE_TOPP)) {
-        for (int d = (int)(blockIdx.x * kThreads + threadIdx.x); d < kBins; d += (int)(gridDim.x * kThreads)) {
-            a.cnt[(int64_t)b * kBins + d] = 0;
-            a.mass[(int64_t)b * kBins + d] = 0;
-        }
-    }
-    __shared__ uint32_t s_red[kThreads / 64];
-    const float T = a.temperature[b];
-    // Division by T > 0 is monotone, so the largest s = z / T is the largest
-    // allowed z divided by T: one division per thread instead of per logit.
-    // Forbidden logits count as kMasked.
-    // The running max is a float select (a NaN z never wins it); float_key
-    // maps -0 and +0 to one key, so this equals the max over keys of s for
-    // every NaN-free row.
-    float zmax = -__builtin_huge_valf();
-    uint32_t seen = 0;  // bit j: element j is in the chunk
-    for_each_elem<VEC4>(i0, i1, per, [&](int j) {
-        const float z = ((t.ok >> j) & 1u) ? t.v[j] : -__builtin_huge_valf();
-        zmax = z > zmax ? z : zmax;
-        seen |= 1u << j;
-    });
-    uint32_t kmax = float_key(zmax / T);
-    if (~t.ok & seen) kmax = max(kmax, float_key(kMasked));
-    kmax = block_max<uint32_t, kThreads>(kmax, s_red);
-    if (threadIdx.x == 0) a.part_max[(int64_t)b * a.nchunks + blockIdx.x] = kmax;
+    return Tile<VEC4>::index(i0, j);
 }
 
-// Key of the row max of s, from the per-chunk maxima.
-template <int NT>
-__device__ uint32_t row_max_key(const SampArgs &a, int b, uint32_t *scratch)
+// One scan workgroup's work on its chunk, PER logits per thread.  FULL: the
+// chunk lies inside the row (no per-element range checks).
+template <bool VEC4, bool MASK, int PER, bool FULL>
+__device__ __forceinline__ void scan_chunk(const SampArgs &a, Tile<VEC4> &t, int b, int c, int i0,
+                                           int i1, uint32_t mode)
 {
-    const uint32_t *pm = a.part_max + (int64_t)b * a.nchunks;
-    uint32_t k = 0;
-    for (int c = threadIdx.x; c < a.nchunks; c += NT) k = max(k, pm[c]);
-    return block_max<uint32_t, NT>(k, scratch);
-}
-
-// Counts (and, for the nucleus, masses) per value bin below the row max.
-template <bool VEC4, bool MASK>
-__global__ __launch_bounds__(kThreads) void samp_bins_kernel(const SampArgs a)
-{
-    const int b = blockIdx.y;
-    SampCtl *ctl = a.ctl + b;
-    const int i0 = blockIdx.x * a.chunk;
-    const int i1 = min(a.vocab, i0 + a.chunk);
-    const int per = a.chunk / kThreads;
-    // The chunk maxima are requested before the tile: loads complete in
-    // order, so waiting for them then does not wait for the tile, whose
-    // elements are used as they arrive.  (Clamped, not range-checked: a
-    // repeated maximum changes no max.)
-    const uint32_t *pm = a.part_max + (int64_t)b * a.nchunks;
-    uint32_t kpm = pm[min((int)threadIdx.x, a.nchunks - 1)];
-    Tile<VEC4> t;
-    t.load(a.logits + (int64_t)b * a.lstride, i0, i1, per);
-    t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
-    const uint32_t mode = ctl->mode;
-    if (!(mode & (MODE_TOPK | MODE_TOPP))) return;
+    __shared__ unsigned long long s_red[kThreads / 64];
     __shared__ uint32_t s_cnt[kBins];
-    __shared__ unsigned long long s_mass[kBins];
-    __shared__ unsigned long long s_red[kThreads / 64];
-    const float T = a.temperature[b];
-    const Scaler sc(T);
-    for (int d = threadIdx.x; d < kBins; d += kThreads) {
-        s_cnt[d] = 0;
-        s_mass[d] = 0;
-    }
-    for (int c = threadIdx.x + kThreads; c < a.nchunks; c += kThreads) kpm = max(kpm, pm[c]);
-    const float M = key_float(block_max<uint32_t, kThreads>(kpm, reinterpret_cast<uint32_t *>(s_red)));
-    const bool want_mass = (mode & MODE_TOPP) != 0;
-    const bool want_cnt = (mode & MODE_TOPK) != 0;  // nucleus-only rows need masses alone
-    unsigned long long zloc = 0;
-    uint32_t tail = 0;
-    for_each_elem<VEC4>(i0, i1, per, [&](int j) {
-        const float s = t.scaled(j, sc);
-        const int bin = bin_of(s, M);
-        // >= 64 below the max (the last bin): counted per thread, its mass
-        // exp(-64) is below the fixed-point unit
-        const bool last = bin == kBins - 1;
-        tail += last ? 1u : 0u;
-        if (!last) {
-            if (want_cnt) atomicAdd(&s_cnt[bin], 1u);
-            if (want_mass) {
-                const unsigned long long w = mass_fixed(s, M);
-                atomicAdd(&s_mass[bin], w);
-                zloc += w;
-            }
-        }
-    });
-    __syncthreads();
-    for (int d = threadIdx.x; d < kBins - 1; d += kThreads) {
-        if (s_cnt[d]) atomicAdd(&a.cnt[(int64_t)b * kBins + d], s_cnt[d]);
-        if (s_mass[d]) atomicAdd(&a.mass[(int64_t)b * kBins + d], s_mass[d]);
-    }
-    const unsigned long long tails = block_sum<unsigned long long, kThreads>(tail, s_red);
-    if (threadIdx.x == 0 && tails)
-        atomicAdd(&a.cnt[(int64_t)b * kBins + kBins - 1], (uint32_t)tails);
-    if (want_mass) {
-        const unsigned long long zs = block_sum<unsigned long long, kThreads>(zloc, s_red);
-        if (threadIdx.x == 0 && zs) atomicAdd(&ctl->Z, zs);
-    }
-}
-
-// One workgroup per row: the row max, and the threshold bin.  Top-k: the
-// bin holding the k-th largest s, with the rank inside it.  Nucleus: the
-// lowest non-empty bin whose strictly-greater mass is within p of the total;
-// every bin above it is eligible in full.
-__global__ __launch_bounds__(kRThreads) void samp_select_kernel(const SampArgs a)
-{
-    constexpr int BPT = kBins / kRThreads;
-    const int b = blockIdx.x;
-    SampCtl *ctl = a.ctl + b;
-    const uint32_t mode = ctl->mode;
-    if (!(mode & (MODE_TOPK | MODE_TOPP | MODE_TOPP_MAX))) return;
-    __shared__ unsigned long long s_red[kRThreads / 64];
-    // The histogram is requested before the row max is reduced, so that the
-    // two round trips overlap; both arrays are read unconditionally (a
-    // branch at a load makes the compiler wait for it), the counts are used
-    // by top-k rows only and neither by p <= 0 rows.
-    const int d0 = (int)threadIdx.x * BPT;
-    const bool topk = (mode & MODE_TOPK) != 0;
-    uint32_t cnt[BPT];
-    unsigned long long mass[BPT];
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        cnt[j] = a.cnt[(int64_t)b * kBins + d0 + j];
-        mass[j] = a.mass[(int64_t)b * kBins + d0 + j];
-    }
-    const uint32_t max_key = row_max_key<kRThreads>(a, b, reinterpret_cast<uint32_t *>(s_red));
-    if (threadIdx.x == 0) ctl->max_key = max_key;
-    if (mode & MODE_TOPP_MAX) return;
-    unsigned long long own_c = 0, own_m = 0;
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        if (!topk) cnt[j] = 0;
-        own_c += cnt[j];
-        own_m += mass[j];
-    }
-    unsigned long long above_m = block_scan_inclusive<unsigned long long, kRThreads>(own_m, s_red) - own_m;
-    if (topk) {
-        unsigned long long above_c = block_scan_inclusive<unsigned long long, kRThreads>(own_c, s_red) - own_c;
-        const unsigned long long k = ctl->k;
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-            if (above_c < k && k <= above_c + cnt[j]) {
-                ctl->jstar = (uint32_t)(d0 + j);
-                ctl->rank = (uint32_t)(k - above_c);
-                ctl->A = above_m;
-            }
-            above_c += cnt[j];
-            above_m += mass[j];
-        }
-    } else {
-        // Nucleus only (no counts kept): a bin whose logits all have mass 0
-        // (below 2^-40 of the max's) has the whole Z above it, which exceeds
-        // p Z for p < 1, so the non-empty bins that can qualify are exactly
-        // those with mass.
-        const double limit = (double)a.top_p[b] * (double)ctl->Z;
-        long long cand = -1;
-        unsigned long long cand_above = 0;
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-            if (mass[j] && (double)above_m <= limit) {
-                cand = d0 + j;
-                cand_above = above_m;
-            }
-            above_m += mass[j];
-        }
-        const long long best = block_max<long long, kRThreads>(cand, reinterpret_cast<long long *>(s_red));
-        if (cand >= 0 && cand == best) {
-            ctl->jstar = (uint32_t)cand;
-            ctl->A = cand_above;
-        }
-    }
-}
-
-// Eligible logits above the threshold bin join the Gumbel argmax; logits of
-// the threshold bin are appended to the candidate list.  The noise is read
-// only where it is needed: the (index, z) pairs that need it are compacted
-// in LDS and their noise fetched together, kList pairs per round.  ROUND2:
-// only rows waiting for a second round work.
-template <bool VEC4, bool MASK, bool ROUND2>
-__global__ __launch_bounds__(kThreads) void samp_collect_kernel(const SampArgs a)
-{
-    const int b = blockIdx.y;
-    SampCtl *ctl = a.ctl + b;
-    if (ROUND2 && !ctl->round2) return;
-    __shared__ unsigned long long s_red[kThreads / 64];
-    __shared__ uint32_t s_tot, s_base;
-    __shared__ uint32_t s_idx[kList];   // index | kCandBit
-    __shared__ float s_s[kList];
-    __shared__ uint32_t s_slot[kList];
-    const int i0 = blockIdx.x * a.chunk;
-    const int i1 = min(a.vocab, i0 + a.chunk);
-    const int per = a.chunk / kThreads;
-    const float *g = a.gumbel + (int64_t)b * a.gstride;
-    // the tile is requested before the row's settings are read, so that
-    // the two overlap
-    Tile<VEC4> t;
-    t.template load<true>(a.logits + (int64_t)b * a.lstride, i0, i1, per);
-    t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, per);
-    const uint32_t mode = a.flags ? ctl->mode : row_mode(a, b);
-    unsigned long long best = 0;
-    if (mode & MODE_GREEDY) {
-        for_each_elem<VEC4>(i0, i1, per, [&](int j) {
-            const uint32_t i = (uint32_t)Tile<VEC4>::index(i0, j);
-            best = max(best, pack_key_index(float_key(t.raw(j)), i));
-        });
-    } else if (mode & MODE_PLAIN) {
-        // every logit is eligible: stream the noise as a tile too, half a
-        // tile at a time (fewer registers live)
-        const float T = a.temperature[b];
-        const Scaler sc(T);
-        Tile<VEC4> gt;
-        auto first_half = [&](int j) {
-            if (j >= kMaxPer / 2) return;
-            const float kappa = t.scaled(j, sc) + gt.v[j];
-            best = max(best, pack_key_index(float_key(kappa), (uint32_t)Tile<VEC4>::index(i0, j)));
-        };
-        gt.template load_range<0, kMaxPer / 2>(g, i0, i1, per);
-        for_each_elem<VEC4>(i0, i1, per, first_half);
-        gt.template load_range<kMaxPer / 2, kMaxPer / 2>(g, i0, i1, per);
-        for_each_elem<VEC4>(i0, i1, per, [&](int j) {
-            if (j < kMaxPer / 2) return;
-            const float kappa = t.scaled(j, sc) + gt.v[j];
-            best = max(best, pack_key_index(float_key(kappa), (uint32_t)Tile<VEC4>::index(i0, j)));
-        });
-    } else {
-        const float T = a.temperature[b];
-        const Scaler sc(T);
-        const uint32_t max_key = ctl->max_key;
-        const float M = key_float(max_key);
-        const int jstar = (int)ctl->jstar;
-        const bool maxima = (mode & MODE_TOPP_MAX) != 0;
-        uint32_t kept = 0, incand = 0;
-        // The class bits are shifted in from the top element down, one
-        // dependent step each, so no element's bit waits in a register of
-        // its own.
-        const bool full = Tile<VEC4>::full(i0, i1, per);
-        if (maxima) {
-            // p <= 0: the logits whose s equals the row max (t.v becomes s)
-#pragma unroll
-            for (int j = kMaxPer - 1; j >= 0; --j) {
-                const bool in = full | ((j < per) & (Tile<VEC4>::index(i0, j) < i1));
-                const float s = t.scaled(j, sc);
-                t.v[j] = s;
-                kept = (kept << 1) | ((in & (float_key(s) == max_key)) ? 1u : 0u);
-            }
-        } else {
-            // The class of an allowed logit follows from z itself, so z / T
-            // is computed only for the logits that go to the list (t.v stays
-            // z).  The two thresholds are found while the tile loads are in
-            // flight.  Forbidden logits (s = kMasked) and NaN ones (bin
-            // kBins - 1) take their bin's class.
-            __shared__ float s_zt[2];
-            z_thresholds(T, M, jstar, s_zt);
-            __syncthreads();
-            const float z_elig = s_zt[0], z_cand = s_zt[1];
-            const int bm = bin_of(kMasked, M);
-            const bool ok_m = bm < jstar, c_m = bm == jstar;
-            const bool ok_n = kBins - 1 < jstar, c_n = kBins - 1 == jstar;
-#pragma unroll
-            for (int j = kMaxPer - 1; j >= 0; --j) {
-                const bool in = full | ((j < per) & (Tile<VEC4>::index(i0, j) < i1));
-                const float z = t.v[j];
-                const bool allowed = (t.ok >> j) & 1u;
-                const bool nan = !(z == z);
-                const bool ge_elig = z >= z_elig, ge_cand = z >= z_cand;
-                const bool ok = !allowed ? ok_m : (nan ? ok_n : ge_elig);
-                const bool c = !allowed ? c_m : (nan ? c_n : (!ge_elig & ge_cand));
-                kept = (kept << 1) | ((in & ok) ? 1u : 0u);
-                incand = (incand << 1) | ((in & c) ? 1u : 0u);
-            }
-        }
-        const uint32_t need = kept | incand;
-        const uint32_t nc = __popc(incand), nn = __popc(need);
-        // candidates (high half) and noise reads (low half) before this thread;
-        // both totals stay below 2^16
-        const uint32_t incl = block_scan_inclusive<uint32_t, kThreads>((nc << 16) | nn,
-                                                                       reinterpret_cast<uint32_t *>(s_red));
-        // The last thread claims the workgroup's candidate slots; the claim's
-        // result is needed only when the candidates are written, so its
-        // latency overlaps the list building and the noise reads.
-        uint32_t claimed = 0;
-        if (threadIdx.x == kThreads - 1) {
-            s_tot = incl;
-            if (incl >> 16) claimed = atomicAdd(&ctl->ncand, incl >> 16);
-        }
-        __syncthreads();
-        const uint32_t tot_n = s_tot & 0xffffu;
-        unsigned long long *cand = a.cand + (int64_t)b * kCap;
-        uint32_t *kap = a.kap + (int64_t)b * kCap;
-        // s of a listed logit: z / T, or kMasked (the maxima rows hold s)
-        auto scaled_entry = [&](float v, bool masked) {
-            return maxima ? v : (masked ? kMasked : v / T);
-        };
-        // candidate `lc` of this workgroup: its key and Gumbel key go to slot cbase + lc
-        auto put_cand = [&](uint32_t cs, float sv, uint32_t kk, uint32_t i) {
-            if (cs < (uint32_t)kCap) {
-                cand[cs] = pack_key_index(float_key(sv), i);
-                kap[cs] = kk;
-            }
-        };
-        uint32_t lc = (incl >> 16) - nc;  // this thread's first candidate, within the workgroup
-        if (tot_n <= (uint32_t)kList) {
-            // one list: this thread's entries take positions [pos0, pos0 + nn)
-            uint32_t pos = (incl & 0xffffu) - nn;
-#pragma unroll
-            for (int j = 0; j < kMaxPer; ++j) {
-                if (!((need >> j) & 1u)) continue;
-                const bool c = (incand >> j) & 1u;
-                const uint32_t i = (uint32_t)Tile<VEC4>::index(i0, j);
-                s_idx[pos] = i | (c ? kCandBit : 0u) | (((kept >> j) & 1u) ? kKeptBit : 0u);
-                s_s[pos] = t.v[j];
-                s_slot[pos] = lc | (((t.ok >> j) & 1u) ? 0u : kSlotMasked);
-                ++pos;
-                lc += c ? 1u : 0u;
-            }
-            __syncthreads();
-            constexpr int R = kList / kThreads;
-            float gv[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t q = (uint32_t)(r * kThreads) + threadIdx.x;
-                gv[r] = q < tot_n ? g[s_idx[q] & kIndexMask] : 0.f;
-            }
-            if (threadIdx.x == kThreads - 1) s_base = claimed;
-            __syncthreads();
-            const uint32_t cbase = s_base;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t q = (uint32_t)(r * kThreads) + threadIdx.x;
-                if (q >= tot_n) continue;
-                const uint32_t e = s_idx[q];
-                const uint32_t i = e & kIndexMask;
-                const uint32_t sq = s_slot[q];
-                const float sv = scaled_entry(s_s[q], (sq & kSlotMasked) != 0);
-                const uint32_t kk = float_key(sv + gv[r]);
-                if (e & kKeptBit) best = max(best, pack_key_index(kk, i));
-                if (e & kCandBit) put_cand(cbase + (sq & ~kSlotMasked), sv, kk, i);
-            }
-        } else {
-            // more entries than the list holds: each thread reads the noise
-            // of its own entries
-            if (threadIdx.x == kThreads - 1) s_base = claimed;
-            __syncthreads();
-            const uint32_t cbase = s_base;
-#pragma unroll
-            for (int j = 0; j < kMaxPer; ++j) {
-                if (!((need >> j) & 1u)) continue;
-                const uint32_t i = (uint32_t)Tile<VEC4>::index(i0, j);
-                const float sv = scaled_entry(t.v[j], !((t.ok >> j) & 1u));
-                const uint32_t kk = float_key(sv + g[i]);
-                if ((kept >> j) & 1u) best = max(best, pack_key_index(kk, i));
-                if ((incand >> j) & 1u) put_cand(cbase + lc++, sv, kk, i);
-            }
-        }
-    }
-    best = block_max<unsigned long long, kThreads>(best, s_red);
-    if (threadIdx.x == 0) a.part_best[(int64_t)b * a.nchunks + blockIdx.x] = best;
-}
-
-// ---- per-row resolution ---------------------------------------------------
-
-struct ResolveShared {
-    union {
-        struct {
-            unsigned long long key[kCap];  // candidates (sorted, descending, above kRThreads)
-            uint32_t kap[kCap];
-            unsigned long long w[kRThreads];  // masses of the kept few
-        };
-        struct {                           // exact in-row fallback
-            uint32_t hcnt[kDigits];
-            unsigned long long hmass[kDigits];
-        };
-    };
-    unsigned long long scan[kRThreads];
-};
-
-// Descending bitonic sort of n (a power of two) packed keys with payload.
-__device__ void bitonic_sort_desc(unsigned long long *key, uint32_t *pay, int n)
-{
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n; i += kRThreads) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const unsigned long long x = key[i], y = key[ixj];
-                    const bool first = (i & k) == 0;
-                    if (first ? (x < y) : (x > y)) {
-                        key[i] = y;
-                        key[ixj] = x;
-                        const uint32_t p = pay[i];
-                        pay[i] = pay[ixj];
-                        pay[ixj] = p;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// In-row exact machinery (used when the threshold bin overflows the
-// candidate list).  The row is rescanned from memory; `sel` picks the logits
-// that take part (in the threshold bin, maybe kept by top-k).
-struct RowScan {
-    const float *z;
-    const uint8_t *m;   // mask row or null
-    float T, M;
-    int V;
-    int jstar;
-};
-
-__device__ __forceinline__ bool in_bin(const RowScan &r, int i, float &s, uint32_t &key)
-{
-    s = (r.m && !r.m[i]) ? kMasked : r.z[i] / r.T;
-    key = float_key(s);
-    return bin_of(s, r.M) == r.jstar;
-}
-
-// Radix select, three levels of 11/11/10 key bits, over the logits of the
-// threshold bin that pass `kept_k` (top-k cut: key > kkey or key == kkey and
-// index <= kcut; kkey == 0 means no cut).  BY_MASS: the lowest digit whose
-// strictly-greater mass stays within `limit` given mass `above` of keys
-// above the bin; else: the digit holding the rank-th largest key.  Returns
-// the exact key; for ranks, `rank_left` is how many of its ties to keep.
-template <bool BY_MASS>
-__device__ uint32_t radix_in_bin(const RowScan &r, ResolveShared &sh, uint32_t kkey, uint32_t kcut,
-                                 unsigned long long above, double limit, uint32_t rank,
-                                 uint32_t *rank_left)
-{
-    uint32_t prefix = 0;
-    constexpr int DPT = kDigits / kRThreads;
-    __shared__ int s_d;
-    __shared__ unsigned long long s_above;
-    __shared__ uint32_t s_rank;
-    if (threadIdx.x == 0) {
-        s_above = above;
-        s_rank = rank;
-    }
-    __syncthreads();
-    for (int level = 0; level < 3; ++level) {
-        const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-        const int width = level == 2 ? 10 : 11;
-        const int hi = shift + width;
-        const unsigned long long rk = s_rank;   // read before any thread can update it
-        const unsigned long long A = s_above;
-        for (int d = threadIdx.x; d < kDigits; d += kRThreads) {
-            sh.hcnt[d] = 0;
-            sh.hmass[d] = 0;
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < r.V; i += kRThreads) {
-            float s;
-            uint32_t key;
-            if (!in_bin(r, i, s, key)) continue;
-            if (kkey && !(key > kkey || (key == kkey && (uint32_t)i <= kcut))) continue;
-            if (hi < 32 && (key >> hi) != (prefix >> hi)) continue;
-            const uint32_t d = (key >> shift) & ((1u << width) - 1u);
-            atomicAdd(&sh.hcnt[d], 1u);
-            if (BY_MASS) atomicAdd(&sh.hmass[d], mass_fixed(s, r.M));
-        }
-        __syncthreads();
-        // thread t owns digits [DPT t, DPT t + DPT); scan from the top digit down
-        const int d_hi = (int)threadIdx.x * DPT + DPT - 1;
-        unsigned long long own = 0;
-        for (int j = 0; j < DPT; ++j) own += BY_MASS ? sh.hmass[d_hi - j] : sh.hcnt[d_hi - j];
-        // exclusive sum over the digits above this thread's range
-        __syncthreads();
-        sh.scan[kRThreads - 1 - threadIdx.x] = own;
-        __syncthreads();
-        for (int off = 1; off < kRThreads; off <<= 1) {
-            const int tt = kRThreads - 1 - (int)threadIdx.x;
-            const unsigned long long add = tt >= off ? sh.scan[tt - off] : 0ull;
-            __syncthreads();
-            sh.scan[tt] += add;
-            __syncthreads();
-        }
-        unsigned long long up = sh.scan[kRThreads - 1 - threadIdx.x] - own;
-        if (threadIdx.x == 0) s_d = kDigits;
-        __syncthreads();
-        if (BY_MASS) {
-            int cand = -1;
-            unsigned long long cand_up = 0;
-            for (int j = 0; j < DPT; ++j) {
-                const int d = d_hi - j;
-                if ((double)(A + up) > limit) break;
-                if (sh.hcnt[d]) {
-                    cand = d;
-                    cand_up = up;
-                }
-                up += sh.hmass[d];
-            }
-            // the lowest qualifying digit
-            if (cand >= 0) atomicMin(&s_d, cand);
-            __syncthreads();
-            if (cand >= 0 && cand == s_d) s_above = A + cand_up;
-            __syncthreads();
-            prefix |= (uint32_t)s_d << shift;
-        } else {
-            for (int j = 0; j < DPT; ++j) {
-                const int d = d_hi - j;
-                const unsigned long long c = sh.hcnt[d];
-                if (up < rk && rk <= up + c) {
-                    s_d = d;
-                    s_rank = (uint32_t)(rk - up);
-                }
-                up += c;
-            }
-            __syncthreads();
-            prefix |= (uint32_t)s_d << shift;
-        }
-        __syncthreads();
-    }
-    if (rank_left) *rank_left = s_rank;
-    return prefix;
-}
-
-// Index of the `need`-th (1-based) logit of the threshold bin, in index
-// order, whose key equals `key`.
-__device__ uint32_t nth_tie_index(const RowScan &r, ResolveShared &sh, uint32_t key, uint32_t need)
-{
-    __shared__ uint32_t s_wave[kRThreads / 64];
-    __shared__ uint32_t s_found;
-    __shared__ uint32_t s_seen;
-    if (threadIdx.x == 0) {
-        s_found = 0xffffffffu;
-        s_seen = 0;
-    }
-    __syncthreads();
+    __shared__ uint32_t s_wkey[kThreads / 64];
+    __shared__ float s_wzx[kThreads / 64];
+    __shared__ uint32_t s_nlist;
+    __shared__ uint32_t s_wtot[kThreads / 64];
+    __shared__ int s_wfit[kThreads / 64], s_wneed[kThreads / 64];
+    ChunkRec *rec = a.rec + (int64_t)b * a.nchunks + c;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int base = 0; base < r.V; base += kRThreads) {
-        const int i = base + (int)threadIdx.x;
-        bool hit = false;
-        if (i < r.V) {
-            float s;
-            uint32_t k2;
-            hit = in_bin(r, i, s, k2) && k2 == key;
+    auto in = [&](int j) { return FULL || elem_index<VEC4>(i0, j) < i1; };
+
+    if (mode & (MODE_GREEDY | MODE_PLAIN)) {
+        unsigned long long best = 0;
+        if (mode & MODE_GREEDY) {
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                if (in(j)) best = max(best, pack_key_index(float_key(t.raw(j)), (uint32_t)elem_index<VEC4>(i0, j)));
+        } else {
+            // every token is eligible: stream the noise too
+            const Scaler sc(a.temperature[b]);
+            Tile<VEC4> gt;
+            gt.template load_range<0, PER>(a.gumbel + (int64_t)b * a.gstride, i0, i1, PER);
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                if (in(j))
+                    best = max(best, pack_key_index(float_key(t.scaled(j, sc) + gt.v[j]),
+                                                    (uint32_t)elem_index<VEC4>(i0, j)));
         }
-        const unsigned long long m = __ballot(hit);
-        if (lane == 0) s_wave[wave] = __popcll(m);
-        __syncthreads();
-        uint32_t before = s_seen;
-        for (int w = 0; w < wave; ++w) before += s_wave[w];
-        const uint32_t below = __popcll(m & ((1ull << lane) - 1ull));
-        if (hit && before + below + 1 == need) s_found = (uint32_t)i;
-        __syncthreads();
+        best = block_max<unsigned long long, kThreads>(best, s_red);
         if (threadIdx.x == 0) {
-            uint32_t tot = 0;
-            for (int w = 0; w < kRThreads / 64; ++w) tot += s_wave[w];
-            s_seen += tot;
-        }
-        __syncthreads();
-        if (s_found != 0xffffffffu) break;
-    }
-    return s_found;
-}
-
-// Gumbel argmax over the threshold bin's logits that pass the final cut.
-__device__ unsigned long long best_in_bin(const RowScan &r, const float *g, ResolveShared &sh,
-                                          uint32_t kkey, uint32_t kcut, uint32_t tau)
-{
-    unsigned long long best = 0;
-    for (int i = threadIdx.x; i < r.V; i += kRThreads) {
-        float s;
-        uint32_t key;
-        if (!in_bin(r, i, s, key)) continue;
-        if (kkey && !(key > kkey || (key == kkey && (uint32_t)i <= kcut))) continue;
-        if (key < tau) continue;
-        best = max(best, pack_key_index(float_key(s + g[i]), (uint32_t)i));
-    }
-    return block_max<unsigned long long, kRThreads>(best, sh.scan);
-}
-
-// Mass of the threshold bin's logits kept by the top-k cut.
-__device__ unsigned long long kept_mass_in_bin(const RowScan &r, ResolveShared &sh, uint32_t kkey,
-                                               uint32_t kcut)
-{
-    unsigned long long m = 0;
-    for (int i = threadIdx.x; i < r.V; i += kRThreads) {
-        float s;
-        uint32_t key;
-        if (!in_bin(r, i, s, key)) continue;
-        if (!(key > kkey || (key == kkey && (uint32_t)i <= kcut))) continue;
-        m += mass_fixed(s, r.M);
-    }
-    return block_sum<unsigned long long, kRThreads>(m, sh.scan);
-}
-
-// Second collect/resolve pass, set-up: the nucleus cut of a top-k row lies
-// above its top-k bin.
-// Every logit in bins above `jk` is in the top-k set, so the nucleus over
-// that set is found like a plain nucleus with total mass Zk.
-__device__ void setup_round2(const SampArgs &a, SampCtl *ctl, ResolveShared &sh, int b, int jk,
-                             unsigned long long Zk)
-{
-    constexpr int BPT = kBins / kRThreads;
-    const double limit = (double)a.top_p[b] * (double)Zk;
-    const int d0 = (int)threadIdx.x * BPT;
-    unsigned long long own = 0;
-    for (int j = 0; j < BPT; ++j) own += a.mass[(int64_t)b * kBins + d0 + j];
-    unsigned long long above = block_scan_inclusive<unsigned long long, kRThreads>(own, sh.scan) - own;
-    long long cand = -1;
-    unsigned long long cand_above = 0;
-    for (int j = 0; j < BPT; ++j) {
-        const int d = d0 + j;
-        if (d < jk && a.cnt[(int64_t)b * kBins + d] && (double)above <= limit) {
-            cand = d;
-            cand_above = above;
-        }
-        above += a.mass[(int64_t)b * kBins + d];
-    }
-    const long long best = block_max<long long, kRThreads>(cand, reinterpret_cast<long long *>(sh.scan));
-    if (cand >= 0 && cand == best) {
-        ctl->jstar = (uint32_t)cand;
-        ctl->A = cand_above;
-        ctl->Z = Zk;
-        ctl->mode = MODE_TOPP;
-        ctl->ncand = 0;
-        ctl->round2 = 1;
-    }
-}
-
-template <bool ROUND2>
-__global__ __launch_bounds__(kRThreads) void samp_resolve_kernel(const SampArgs a)
-{
-    __shared__ ResolveShared sh;
-    const int b = blockIdx.x;
-    SampCtl *ctl = a.ctl + b;
-    // Everything the row may need is requested up front, so that the loads
-    // overlap: the chunks' best keys, the first kRThreads list entries (in
-    // bounds whatever the count; entries past it are ignored) and the
-    // control block.
-    const int i = (int)threadIdx.x;
-    unsigned long long best = 0;
-    {
-        const unsigned long long *pb = a.part_best + (int64_t)b * a.nchunks;
-        for (int c = i; c < a.nchunks; c += kRThreads) best = max(best, pb[c]);
-    }
-    const unsigned long long cand0 = a.cand[(int64_t)b * kCap + i];
-    const uint32_t kap0 = a.kap[(int64_t)b * kCap + i];
-    const double p = (double)a.top_p[b];
-    SampCtl c = {};
-    if (a.flags) c = *ctl;
-    if (ROUND2 && !c.round2) return;
-    const uint32_t mode = a.flags ? c.mode : row_mode(a, b);
-    if (mode & MODE_DONE) return;
-    // best eligible logit outside the threshold bin, over the chunks
-    best = block_max<unsigned long long, kRThreads>(best, sh.scan);
-    if (mode & (MODE_GREEDY | MODE_PLAIN | MODE_TOPP_MAX)) {
-        if (threadIdx.x == 0) {
-            a.out_ids[b] = (int32_t)unpack_index(best);
-            if (a.flags) {
-                ctl->mode = mode | MODE_DONE;
-                ctl->tau = (mode & MODE_TOPP_MAX) ? c.max_key : 0u;
-                ctl->kpack = 0;
-            }
+            ChunkRec r = {};
+            r.best = best;
+            *rec = r;
         }
         return;
     }
-    // the final cut, kept for the extra outputs: key >= cut_tau and, for
-    // top-k, (key, ~index) >= cut_k
-    uint32_t cut_tau = 0;
-    unsigned long long cut_k = 0;
-    const bool topk = (mode & MODE_TOPK) != 0;
-    const bool topp = (mode & MODE_TOPP) != 0;
-    const uint32_t n = c.ncand;
-    const float M = key_float(c.max_key);
-    const unsigned long long A = c.A;
-    const int jstar = (int)c.jstar;
 
-    if (n <= (uint32_t)kRThreads) {
-        // ---- few candidates: ranks and masses above by direct counting ----
-        // q lanes (consecutive, q <= 64) share candidate e = i / q and split
-        // the comparisons against all n candidates between them.
-        int np = 1;
-        while (np < (int)n) np <<= 1;
-        const int q = min(64, kRThreads / np);
-        const int e = i / q, part = i % q;
-        sh.key[i] = i < (int)n ? cand0 : 0ull;
-        sh.kap[i] = kap0;
-        __syncthreads();
-        const bool real = e < (int)n;
-        const unsigned long long ke = real ? sh.key[e] : 0ull;
-        const uint32_t se = (uint32_t)(ke >> 32);
-        // top-k keeps the r largest (s, then lowest index); the nucleus runs
-        // over what top-k keeps
-        bool kept = real;
-        if (topk) {
-            uint32_t larger = 0;
-            for (int j = part; j < (int)n; j += q) larger += sh.key[j] > ke ? 1u : 0u;
-            larger = group_sum_lanes(larger, q);
-            kept = real && larger < c.rank;
-        }
-        uint32_t tau = 0;
-        if (topp) {
-            __shared__ unsigned long long s_tot;
-            const unsigned long long w = kept ? mass_fixed(key_float(se), M) : 0ull;
-            if (part == 0 && real) sh.w[e] = w;
-            const unsigned long long tot = block_sum<unsigned long long, kRThreads>(part == 0 ? w : 0ull, sh.scan);
-            unsigned long long Zrow = c.Z;
-            if (topk) {
-                // the nucleus over the top-k set: total mass above the bin + kept candidates
-                Zrow = A + tot;
-                if ((double)A > p * (double)Zrow) {
-                    setup_round2(a, ctl, sh, b, jstar, Zrow);
-                    return;
-                }
-            }
-            const double limit = p * (double)Zrow;
-            // mass of kept candidates with a strictly larger s
-            unsigned long long above = 0;
-            for (int j = part; j < (int)n; j += q) above += (uint32_t)(sh.key[j] >> 32) > se ? sh.w[j] : 0ull;
-            above = group_sum_lanes(above, q);
-            // the smallest s whose strictly-larger mass fits the limit
-            const uint32_t fit = (kept && (double)(A + above) <= limit) ? se : 0xffffffffu;
-            tau = ~block_max<uint32_t, kRThreads>(~fit, reinterpret_cast<uint32_t *>(sh.scan));
-        }
-        if (part == 0 && kept && se >= tau) best = max(best, pack_key_index(sh.kap[e], unpack_index(ke)));
-        best = block_max<unsigned long long, kRThreads>(best, sh.scan);
-        cut_tau = tau;
-        if (topk)  // the smallest packed key top-k keeps
-            cut_k = ~block_max<unsigned long long, kRThreads>((part == 0 && kept) ? ~ke : 0ull, sh.scan);
-    } else if (n <= (uint32_t)kCap) {
-        // ---- sort the candidates of the threshold bin ----
-        int np = 1;
-        while (np < (int)n) np <<= 1;
-        for (int i = threadIdx.x; i < np; i += kRThreads) {
-            sh.key[i] = i < (int)n ? a.cand[(int64_t)b * kCap + i] : 0ull;
-            sh.kap[i] = i < (int)n ? a.kap[(int64_t)b * kCap + i] : 0u;
-        }
-        __syncthreads();
-        bitonic_sort_desc(sh.key, sh.kap, np);
-        // thread t owns sorted positions [PT t, PT t + PT)
-        constexpr int PT = kCap / kRThreads;
-        const int i0 = (int)threadIdx.x * PT;
-        // top-k keeps the first r; the nucleus runs over what top-k keeps
-        const int r = topk ? (int)c.rank : (int)n;
-        unsigned long long w[PT];
-        unsigned long long own = 0;
-        for (int j = 0; j < PT; ++j) {
-            const int i = i0 + j;
-            w[j] = (topp && i < r) ? mass_fixed(key_float((uint32_t)(sh.key[i] >> 32)), M) : 0ull;
-            own += w[j];
-        }
-        const unsigned long long incl = block_scan_inclusive<unsigned long long, kRThreads>(own, sh.scan);
-        const unsigned long long excl0 = incl - own;
-        uint32_t tau = 0;
-        if (topp) {
-            unsigned long long Zrow = c.Z;
-            if (topk) {
-                // the nucleus over the top-k set: total mass above the bin + kept candidates
-                __shared__ unsigned long long s_tot;
-                if (threadIdx.x == kRThreads - 1) s_tot = incl;
-                __syncthreads();
-                Zrow = A + s_tot;
-                if ((double)A > p * (double)Zrow) {
-                    setup_round2(a, ctl, sh, b, jstar, Zrow);
-                    return;
-                }
-            }
-            const double limit = p * (double)Zrow;
-            // the lowest group head whose strictly-greater mass fits the limit
-            long long last = -1;
-            unsigned long long run = excl0;
-            for (int j = 0; j < PT; ++j) {
-                const int i = i0 + j;
-                if (i < r) {
-                    const uint32_t k1 = (uint32_t)(sh.key[i] >> 32);
-                    const bool head = i == 0 || (uint32_t)(sh.key[i - 1] >> 32) != k1;
-                    if (head && (double)(A + run) <= limit) last = i;
-                }
-                run += w[j];
-            }
-            const long long lh = block_max<long long, kRThreads>(last, reinterpret_cast<long long *>(sh.scan));
-            tau = lh >= 0 ? (uint32_t)(sh.key[lh] >> 32) : 0u;
-        }
-        // best Gumbel key over the kept candidates
-        for (int j = 0; j < PT; ++j) {
-            const int i = i0 + j;
-            if (i < r && (uint32_t)(sh.key[i] >> 32) >= tau)
-                best = max(best, pack_key_index(sh.kap[i], unpack_index(sh.key[i])));
-        }
-        best = block_max<unsigned long long, kRThreads>(best, sh.scan);
-        cut_tau = tau;
-        if (topk) cut_k = sh.key[r - 1];
+    // ---- filtered rows: s, the chunk max and the value histogram ----
+    // Reductions run inside each wave and meet through small LDS arrays,
+    // and list slots are claimed per wave (the list's order carries no
+    // meaning).
+    for (int d = threadIdx.x; d < kBins; d += kThreads) s_cnt[d] = 0;
+    if (threadIdx.x == 0) s_nlist = 0;
+    const float T = a.temperature[b];
+    const Scaler sc(T);
+    // s = z / T by the double product for every element; a wave that holds
+    // a logit small enough for a subnormal tie redoes those by division
+    unsigned long long tiny = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) tiny |= __ballot(fabsf(t.v[j]) < sc.tiny);
+    if (__builtin_expect(tiny != 0, 0)) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) t.v[j] = sc(t.v[j]);
     } else {
-        // ---- the threshold bin overflowed the list: exact cut from the row ----
-        RowScan rs;
-        rs.z = a.logits + (int64_t)b * a.lstride;
-        rs.m = a.mask ? a.mask + (int64_t)b * a.mstride : nullptr;
-        rs.T = a.temperature[b];
-        rs.M = M;
-        rs.V = a.vocab;
-        rs.jstar = jstar;
-        const float *g = a.gumbel + (int64_t)b * a.gstride;
-        uint32_t kkey = 0, kcut = 0xffffffffu, tau = 0;
-        if (topk) {
-            uint32_t left = 0;
-            kkey = radix_in_bin<false>(rs, sh, 0, 0, 0, 0.0, c.rank, &left);
-            // keep only the `left` lowest-index logits equal to the k-th key
-            kcut = nth_tie_index(rs, sh, kkey, left);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) t.v[j] = (float)((double)t.v[j] * sc.inv);
+    }
+    float smax = -__builtin_huge_valf();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if (MASK && !((t.ok >> j) & 1u)) t.v[j] = kMasked;
+        // (fmaxf: NaN never wins)
+        if (in(j)) smax = fmaxf(smax, t.v[j]);
+    }
+    {
+        const uint32_t wk = wave_max_t(float_key(smax));
+        if (lane == 0) s_wkey[wave] = wk;
+    }
+    __syncthreads();                                       // (1) also orders the clearing
+    uint32_t kmax = s_wkey[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) kmax = max(kmax, s_wkey[w]);
+    const float Mc = key_float(kmax);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (in(j)) atomicAdd(&s_cnt[bin_of(t.v[j], Mc)], 1u);
+    __syncthreads();                                       // (2)
+
+    // Cut bin jc: the list holds the tokens of bins [0, jc).  cum(j) =
+    // tokens in bins below j (non-decreasing, cum(kBins) = all).  j_fit: the
+    // most bins whose tokens fit in the list; j_need: the fewest holding
+    // `need` (top-k: k; p <= 0: the maxima, i.e. bin 0).  Thread t owns bins
+    // [8t, 8t + 8); one exchange of wave totals, then each thread tests its
+    // own bins and the results meet in LDS.
+    int jc;
+    {
+        constexpr int BPT = kBins / kThreads;
+        const int d0 = (int)threadIdx.x * BPT;
+        uint32_t cnt[BPT];
+        uint32_t own = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            cnt[j] = s_cnt[d0 + j];
+            own += cnt[j];
         }
-        if (topp) {
-            unsigned long long Zrow = c.Z;
-            if (topk) {
-                Zrow = A + kept_mass_in_bin(rs, sh, kkey, kcut);
-                if ((double)A > p * (double)Zrow) {
-                    setup_round2(a, ctl, sh, b, jstar, Zrow);
-                    return;
-                }
+        uint32_t incl = own;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t u = __shfl_up(incl, (unsigned)off);
+            if (lane >= off) incl += u;
+        }
+        if (lane == 63) s_wtot[wave] = incl;
+        __syncthreads();                                   // (3a)
+        uint32_t cum = incl - own;
+        for (int w = 0; w < wave; ++w) cum += s_wtot[w];
+        const uint32_t cap = (uint32_t)a.cap;
+        uint32_t need = cap;                               // nucleus: as many as fit
+        if (mode & MODE_TOPK) need = min((uint32_t)a.top_k[b], cap);
+        else if (mode & MODE_TOPP_MAX) need = 1;
+        int fit = 0, nd = kBins;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            if (cum <= cap) fit = d0 + j;
+            if (cum >= need) nd = min(nd, d0 + j);
+            cum += cnt[j];
+        }
+        if (threadIdx.x == kThreads - 1) {                 // j = kBins: every token
+            if (cum <= cap) fit = kBins;
+            if (cum >= need) nd = min(nd, kBins);
+        }
+        const int wfit = wave_max_t(fit), wneed = -wave_max_t(-nd);
+        if (lane == 0) {
+            s_wfit[wave] = wfit;
+            s_wneed[wave] = wneed;
+        }
+        __syncthreads();                                   // (3b)
+        int j_fit = s_wfit[0], j_need = s_wneed[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) {
+            j_fit = max(j_fit, s_wfit[w]);
+            j_need = min(j_need, s_wneed[w]);
+        }
+        jc = (mode & (MODE_TOPK | MODE_TOPP_MAX)) ? min(j_fit, j_need) : j_fit;
+    }
+
+    // ---- classify: listed tokens, the largest left out, the left-out mass ----
+    // Branch-free per element: a listed token enters the max and the mass
+    // as -inf (mass exactly 0); the mass is computed only for nucleus rows
+    // (a wave-uniform choice made once).
+    uint32_t listed = 0;
+    float omax = -__builtin_huge_valf();
+    float zx = 0.f;
+    bool any_nan_out = false;
+    auto classify = [&](auto with_mass) {
+        const double Md = (double)Mc;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const float s = t.v[j];
+            const bool lj = in(j) && bin_of(s, Mc) < jc;
+            const bool oj = in(j) && !lj;
+            listed |= (lj ? 1u : 0u) << j;
+            const float so = oj ? s : -__builtin_huge_valf();
+            omax = fmaxf(omax, so);
+            any_nan_out |= oj && !(s == s);
+            if (decltype(with_mass)::value) zx += mass_approx(so, Md);
+        }
+    };
+    if ((mode & MODE_TOPP) && !(mode & MODE_TOPK))
+        classify(std::true_type{});
+    else
+        classify(std::false_type{});
+    {
+        const uint32_t nl = __popc(listed);
+        uint32_t incl = nl;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t u = __shfl_up(incl, (unsigned)off);
+            if (lane >= off) incl += u;
+        }
+        uint32_t base = 0;
+        if (lane == 63 && incl) base = atomicAdd(&s_nlist, incl);
+        base = __shfl(base, 63);
+        unsigned long long *lst = a.list + ((int64_t)b * a.nchunks + c) * a.cap;
+        uint32_t pos = base + incl - nl;
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            if ((listed >> j) & 1u)
+                lst[pos++] = pack_key_index(float_key(t.v[j]), (uint32_t)elem_index<VEC4>(i0, j));
+        // a left-out NaN counts as the largest key (nothing is known above it)
+        uint32_t ok_key = (omax == -__builtin_huge_valf()) ? 0u : float_key(omax);
+        if (any_nan_out) ok_key = 0xffffffffu;
+        const uint32_t wo = wave_max_t(ok_key);
+        const float wz = wave_sum_t(zx);
+        if (lane == 0) {
+            s_wkey[wave] = wo;
+            s_wzx[wave] = wz;
+        }
+    }
+    __syncthreads();                                       // (4)
+    if (threadIdx.x == 0) {
+        ChunkRec r;
+        r.mkey = kmax;
+        r.outkey = s_wkey[0];
+        double z = 0.0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            r.outkey = max(r.outkey, s_wkey[w]);
+            z += (double)s_wzx[w];
+        }
+        r.n = s_nlist;
+        r.pad = 0;
+        r.zx = z;
+        r.best = 0;
+        *rec = r;
+    }
+}
+
+template <bool VEC4, bool MASK, int PER>
+__global__ __launch_bounds__(kThreads) void samp_scan_kernel(const SampArgs a)
+{
+    const int b = blockIdx.y;
+    const int c = blockIdx.x;
+    const int i0 = c * PER * kThreads;
+    const int i1 = min(a.vocab, i0 + PER * kThreads);
+    // the tile is requested before the row's settings are read, so that
+    // the two overlap
+    Tile<VEC4> t;
+    t.template load_range<0, PER, true>(a.logits + (int64_t)b * a.lstride, i0, i1, PER);
+    t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, PER);
+    const uint32_t mode = row_mode(a, b);
+    if (i1 - i0 == PER * kThreads)
+        scan_chunk<VEC4, MASK, PER, true>(a, t, b, c, i0, i1, mode);
+    else
+        scan_chunk<VEC4, MASK, PER, false>(a, t, b, c, i0, i1, mode);
+}
+
+// ---- histogram -------------------------------------------------------------
+
+// Finish-side bins that can hold a token above T*: [0, nb).
+__device__ __forceinline__ int bins_above(uint32_t tout, float M)
+{
+    return tout == 0u ? kHBins : hbin_of(key_float(tout), M) + 1;
+}
+
+// One workgroup per (group of chunks, row) of the filtered rows.  The
+// group's listed tokens above T* get their noise and go into value bins
+// below the row max M: counts, masses (nucleus rows) and the best Gumbel
+// key per bin, from which each bin's count and best over the bins before it
+// follow by prefix scans; the tokens are then written in bin order with
+// their noise.  Every listed token's mass plus the chunks' left-out masses
+// brought to M make the group's share of Z.  Everything is written for the
+// group (no atomics across workgroups); the finish combines the groups.
+// The first kHBatch list slots of each thread are requested together with
+// the row's records, before anything is known of them (slots past a
+// chunk's count hold stale data and are dropped once the counts arrive).
+__global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
+{
+    const int b = blockIdx.y;
+    const int g = blockIdx.x;
+    const uint32_t mode = row_mode(a, b);
+    if (!(mode & (MODE_TOPK | MODE_TOPP))) return;   // greedy, plain, maxima: not needed
+    __shared__ unsigned long long s_red[kThreads / 64];
+    __shared__ double s_tab[64];
+    __shared__ uint32_t s_cnt[kHBins];
+    __shared__ unsigned long long s_mass[kHBins];
+    __shared__ unsigned long long s_best[kHBins];
+    __shared__ unsigned long long s_sum[3][kThreads / 64];
+    __shared__ uint32_t s_n[kGroupChunks], s_mk[kGroupChunks];
+    __shared__ double s_zx[kGroupChunks];
+    const int c0 = (int)((int64_t)g * a.nchunks / a.groups);
+    const int c1 = (int)((int64_t)(g + 1) * a.nchunks / a.groups);
+    const unsigned long long *lgrp = a.list + ((int64_t)b * a.nchunks + c0) * a.cap;
+    const int nslots = (c1 - c0) * a.cap;
+    const int lc = __ffs(a.cap) - 1;   // cap is a power of two
+    // ---- one round of loads: the first batch of slots and the records ----
+    unsigned long long v[kHBatch];
+#pragma unroll
+    for (int j = 0; j < kHBatch; ++j) {
+        const int f = (int)threadIdx.x + j * kThreads;
+        v[j] = lgrp[f < nslots ? f : 0];
+    }
+    const ChunkRec *rec = a.rec + (int64_t)b * a.nchunks;
+    uint32_t km = 0, to = 0;
+    for (int c = threadIdx.x; c < a.nchunks; c += kThreads) {
+        const ChunkRec r = rec[c];
+        km = max(km, r.mkey);
+        to = max(to, r.outkey);
+        if (c >= c0 && c < c1) {
+            s_n[c - c0] = r.n;
+            s_mk[c - c0] = r.mkey;
+            s_zx[c - c0] = r.zx;
+        }
+    }
+    if (threadIdx.x < 64) s_tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+    for (int d = threadIdx.x; d < kHBins; d += kThreads) {
+        s_cnt[d] = 0;
+        s_mass[d] = 0;
+        s_best[d] = 0;
+    }
+    uint32_t kmax, tout;
+    block_max2<kThreads>(km, to, s_red, kmax, tout);   // (its barrier orders the fills)
+    const float Mf = key_float(kmax);
+    const double M = (double)Mf;
+    const bool nucleus = (mode & MODE_TOPP) && !(mode & MODE_TOPK);
+    const float *gn = a.gumbel + (int64_t)b * a.gstride;
+    // slot f of the batch at f0, slot j: listed (live: and above T*)
+    auto listed = [&](int f) {
+        return f < nslots && (uint32_t)(f & (a.cap - 1)) < s_n[f < nslots ? f >> lc : 0];
+    };
+    auto live = [&](int f, unsigned long long p) { return listed(f) && (uint32_t)(p >> 32) > tout; };
+    unsigned long long zl = 0, mu = 0, nu = 0;
+    float gv[kHBatch];
+    for (int f0 = threadIdx.x; f0 < nslots; f0 += kHBatch * kThreads) {
+        if (f0 != (int)threadIdx.x) {   // later batches
+#pragma unroll
+            for (int j = 0; j < kHBatch; ++j) {
+                const int f = f0 + j * kThreads;
+                v[j] = lgrp[f < nslots ? f : 0];
             }
-            tau = radix_in_bin<true>(rs, sh, kkey, kcut, A, p * (double)Zrow, 0, nullptr);
         }
-        const unsigned long long bb = best_in_bin(rs, g, sh, kkey, kcut, tau);
-        best = max(best, bb);
-        cut_tau = tau;
-        if (topk) cut_k = pack_key_index(kkey, kcut);
+#pragma unroll
+        for (int j = 0; j < kHBatch; ++j)
+            gv[j] = gn[live(f0 + j * kThreads, v[j]) ? unpack_index(v[j]) : 0u];
+#pragma unroll
+        for (int j = 0; j < kHBatch; ++j) {
+            const int f = f0 + j * kThreads;
+            if (!listed(f)) continue;
+            const float s = value_of(v[j]);
+            const unsigned long long m = nucleus ? mass_fixed(s, M, s_tab) : 0ull;
+            zl += m;
+            if ((uint32_t)(v[j] >> 32) > tout) {
+                const int d = hbin_of(s, Mf);
+                const uint32_t i = unpack_index(v[j]);
+                atomicAdd(&s_cnt[d], 1u);
+                if (nucleus) atomicAdd(&s_mass[d], m);
+                atomicMax(&s_best[d], pack_key_index(float_key(s + gv[j]), i));
+                mu += m;
+                ++nu;
+            }
+        }
+    }
+    if (nucleus)   // the chunks' left-out masses, brought from M_c to M
+        for (int c = threadIdx.x; c < c1 - c0; c += kThreads)
+            if (s_zx[c] > 0.0)
+                zl += (unsigned long long)(s_zx[c] * exp_below((double)key_float(s_mk[c]) - M, s_tab) *
+                                           kMassUnit + 0.5);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    zl = wave_sum_t(zl);
+    mu = wave_sum_t(mu);
+    nu = wave_sum_t(nu);
+    if (lane == 0) {
+        s_sum[0][wave] = zl;
+        s_sum[1][wave] = mu;
+        s_sum[2][wave] = nu;
+    }
+    __syncthreads();   // the bins are complete
+
+    // Exclusive prefix count and prefix max over the bins: thread t owns
+    // bins [kPB t, kPB t + kPB).
+    constexpr int kPB = kHBins / kThreads;
+    const int d0 = kPB * (int)threadIdx.x;
+    uint32_t cnt[kPB];
+    unsigned long long bst[kPB];
+    uint32_t csum = 0;
+    unsigned long long cmax = 0;
+#pragma unroll
+    for (int j = 0; j < kPB; ++j) {
+        cnt[j] = s_cnt[d0 + j];
+        bst[j] = s_best[d0 + j];
+        csum += cnt[j];
+        cmax = max(cmax, bst[j]);
+    }
+    uint32_t isum = csum;
+    unsigned long long imax = cmax;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t us = (uint32_t)__shfl_up((int)isum, (unsigned)o);
+        const unsigned long long um = __shfl_up(imax, (unsigned)o);
+        if (lane >= o) {
+            isum += us;
+            imax = max(imax, um);
+        }
+    }
+    __shared__ unsigned long long s_wmax[kThreads / 64];
+    if (lane == 63) {   // (s_red is free: its last use was behind a barrier)
+        s_red[wave] = isum;
+        s_wmax[wave] = imax;
+    }
+    __syncthreads();
+    uint32_t run = isum - csum;
+    unsigned long long rmax = 0;
+    {   // this thread's inclusive-exclusive conversion, plus the waves before
+        const unsigned long long prev = __shfl_up(imax, 1u);
+        rmax = lane > 0 ? prev : 0ull;
+    }
+    for (int w = 0; w < wave; ++w) {
+        run += (uint32_t)s_red[w];
+        rmax = max(rmax, s_wmax[w]);
+    }
+    const int nb = bins_above(tout, Mf);
+    const int64_t part = (int64_t)b * a.groups + g;
+#pragma unroll
+    for (int j = 0; j < kPB; ++j) {
+        const int d = d0 + j;
+        if (d < nb) {
+            BinRec r;
+            r.cnt = cnt[j];
+            r.off = run;
+            r.mass = nucleus ? s_mass[d] : 0ull;
+            r.above = rmax;
+            a.bins[part * kHBins + d] = r;
+        }
+        s_cnt[d] = run;   // the bin's write cursor
+        run += cnt[j];
+        rmax = max(rmax, bst[j]);
+    }
+    __syncthreads();
+    // the tokens in bin order, with their noise
+    SortedTok *out = a.sorted + part * a.gslots;
+    for (int f0 = threadIdx.x; f0 < nslots; f0 += kHBatch * kThreads) {
+        if (nslots > kHBatch * kThreads) {   // several batches: read again
+#pragma unroll
+            for (int j = 0; j < kHBatch; ++j) {
+                const int f = f0 + j * kThreads;
+                v[j] = lgrp[f < nslots ? f : 0];
+            }
+#pragma unroll
+            for (int j = 0; j < kHBatch; ++j)
+                gv[j] = gn[live(f0 + j * kThreads, v[j]) ? unpack_index(v[j]) : 0u];
+        }
+#pragma unroll
+        for (int j = 0; j < kHBatch; ++j) {
+            if (!live(f0 + j * kThreads, v[j])) continue;
+            const uint32_t pos = atomicAdd(&s_cnt[hbin_of(value_of(v[j]), Mf)], 1u);
+            SortedTok st;
+            st.packed = v[j];
+            st.g = gv[j];
+            st.pad = 0;
+            out[pos] = st;
+        }
     }
     if (threadIdx.x == 0) {
+        RowTot r = {};
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            r.Z += s_sum[0][w];
+            r.mu += s_sum[1][w];
+            r.nu += (uint32_t)s_sum[2][w];
+        }
+        a.tot[part] = r;
+    }
+}
+
+// ---- finish ----------------------------------------------------------------
+
+constexpr int kCand = 1024;   // tokens of a threshold bin resolved in LDS
+// the counting cut gives each candidate q >= 1 lanes: at most one per thread
+static_assert(kCand <= kFThreads, "cand_rank / cand_cut need a lane per candidate");
+constexpr int kBatch = 8;     // list entries per thread whose loads are issued together
+
+struct FinishShared {
+    double tab[64];                       // 2^(j/64)
+    uint32_t nlist[kMaxChunks];           // list sizes of the chunks
+    uint32_t bcnt[kBins];                 // value bins below the row max (the first
+    unsigned long long bmass[kBins];      // kHBins): counts and masses (2^-38 units)
+    unsigned long long ckey[kCand];       // one bin's tokens: packed keys ...
+    unsigned long long cmass[kCand];      // ... masses
+    float cgum[kCand];                    // ... and noise (one-pass draw)
+    RowTot gtot[kGroups];                 // the histogram groups' totals
+    uint32_t goff[kGroups], gcnt[kGroups], gstart[kGroups + 1];   // the cut bin, per group
+    uint32_t hcnt[kDigits];               // radix digits (slow path)
+    unsigned long long red[kFThreads / 64];
+    uint32_t nc, sel;
+    unsigned long long up, pick;
+};
+
+// The row's listed tokens above T*, streamed from memory.  Thread t takes
+// slot t % cap of chunks t / cap, t / cap + per, ... (per = kFThreads / cap;
+// cap divides kFThreads), kBatch chunks' loads issued together.
+struct ListSource {
+    const unsigned long long *lrow;
+    const uint32_t *nlist;   // LDS
+    int cap, per, nch, slot, csub;
+    uint32_t tout;
+    double M;
+    const double *tab;
+
+    template <typename F>
+    __device__ __forceinline__ void each(F f) const
+    {
+        for (int c0 = csub; c0 < nch; c0 += kBatch * per) {
+            unsigned long long v[kBatch];
+            bool ok[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int c = c0 + j * per;
+                ok[j] = c < nch && slot < (int)nlist[c < nch ? c : 0];
+                v[j] = lrow[(int64_t)(ok[j] ? c : 0) * cap + (ok[j] ? slot : 0)];
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (ok[j] && (uint32_t)(v[j] >> 32) > tout) f(v[j]);
+        }
+    }
+    __device__ __forceinline__ unsigned long long mass(unsigned long long packed) const
+    {
+        return mass_fixed(value_of(packed), M, tab);
+    }
+};
+
+// The whole row, read again from memory (s recomputed).
+struct RowSource {
+    const float *z;
+    const uint8_t *m;
+    Scaler sc;
+    double M;
+    int V;
+    const double *tab;
+    template <typename F>
+    __device__ __forceinline__ void each(F f) const
+    {
+        for (int i = threadIdx.x; i < V; i += kFThreads) {
+            const float s = (m && !m[i]) ? kMasked : sc(z[i]);
+            f(pack_key_index(float_key(s), (uint32_t)i));
+        }
+    }
+    __device__ __forceinline__ unsigned long long mass(unsigned long long packed) const
+    {
+        return mass_fixed(value_of(packed), M, tab);
+    }
+};
+
+// The 56 significant bits of a packed key: the value key and the low 24 bits
+// of ~index (vocab <= 2^24, so the top 8 bits of ~index are all ones).
+__device__ __forceinline__ unsigned long long v56(unsigned long long packed)
+{
+    return ((packed >> 32) << 24) | (packed & 0xffffffull);
+}
+
+__device__ __forceinline__ unsigned long long packed_of_v56(unsigned long long v)
+{
+    return ((v >> 24) << 32) | 0xff000000ull | (v & 0xffffffull);
+}
+
+// Value-bin histogram (counts, and masses if MASS; bins below the row max
+// M) of the tokens for which keep(packed) holds; returns their total mass.
+template <bool MASS, typename Src, typename Keep>
+__device__ __forceinline__ unsigned long long bin_hist(const Src &src, FinishShared &sh, float M, Keep keep)
+{
+    for (int d = threadIdx.x; d < kHBins; d += kFThreads) {
+        sh.bcnt[d] = 0;
+        sh.bmass[d] = 0;
+    }
+    __syncthreads();
+    unsigned long long tot = 0;
+    src.each([&](unsigned long long packed) {
+        if (!keep(packed)) return;
+        const int d = hbin_of(value_of(packed), M);
+        atomicAdd(&sh.bcnt[d], 1u);
+        if (MASS) {
+            const unsigned long long m = src.mass(packed);
+            atomicAdd(&sh.bmass[d], m);
+            tot += m;
+        }
+    });
+    return block_sum<unsigned long long, kFThreads>(tot, sh.red);
+}
+
+// Thread t owns bins [kFBins t, kFBins t + kFBins) (bin 0: largest values).
+constexpr int kFBins = kHBins / kFThreads;
+static_assert(kFBins >= 1 && kHBins % kFThreads == 0, "finish bins per thread");
+
+// The bin holding the rank-th largest token, and the rank inside it.
+__device__ __forceinline__ void bin_by_count(FinishShared &sh, uint32_t rank, int &bin, uint32_t &rank_in)
+{
+    const int d0 = kFBins * (int)threadIdx.x;
+    uint32_t own = 0;
+#pragma unroll
+    for (int j = 0; j < kFBins; ++j) own += sh.bcnt[d0 + j];
+    uint32_t above = (uint32_t)block_scan_inclusive<unsigned long long, kFThreads>(own, sh.red) - own;
+#pragma unroll
+    for (int j = 0; j < kFBins; ++j) {
+        const uint32_t c = sh.bcnt[d0 + j];
+        if (above < rank && rank <= above + c) {
+            sh.sel = (uint32_t)(d0 + j);
+            sh.up = above;
+        }
+        above += c;
+    }
+    __syncthreads();
+    bin = (int)sh.sel;
+    rank_in = rank - (uint32_t)sh.up;
+    __syncthreads();
+}
+
+// The deepest non-empty bin whose strictly-greater mass is <= limit (the
+// bin of the nucleus cut), and that mass.
+__device__ __forceinline__ void bin_by_mass(FinishShared &sh, double limit, int &bin, unsigned long long &A)
+{
+    const int d0 = kFBins * (int)threadIdx.x;
+    unsigned long long own = 0;
+#pragma unroll
+    for (int j = 0; j < kFBins; ++j) own += sh.bmass[d0 + j];
+    unsigned long long above = block_scan_inclusive<unsigned long long, kFThreads>(own, sh.red) - own;
+    int cand = -1;
+    unsigned long long cand_a = 0;
+#pragma unroll
+    for (int j = 0; j < kFBins; ++j) {
+        if (sh.bcnt[d0 + j] && (double)above <= limit) {
+            cand = d0 + j;
+            cand_a = above;
+        }
+        above += sh.bmass[d0 + j];
+    }
+    const int best =
+        (int)block_max<unsigned long long, kFThreads>((unsigned long long)(cand + 1), sh.red) - 1;
+    if (cand >= 0 && cand == best) sh.up = cand_a;
+    __syncthreads();
+    bin = best;
+    A = sh.up;
+    __syncthreads();
+}
+
+// Copies the tokens of bin `bin` passing keep, with their masses, into
+// sh.ckey / sh.cmass; returns their number (only the first kCand stored).
+template <typename Src, typename Keep>
+__device__ __forceinline__ uint32_t compact_bin(const Src &src, FinishShared &sh, float M, int bin, Keep keep)
+{
+    if (threadIdx.x == 0) sh.nc = 0;
+    __syncthreads();
+    src.each([&](unsigned long long packed) {
+        if (!keep(packed) || hbin_of(value_of(packed), M) != bin) return;
+        const uint32_t slot = atomicAdd(&sh.nc, 1u);
+        if (slot < (uint32_t)kCand) {
+            sh.ckey[slot] = packed;
+            sh.cmass[slot] = src.mass(packed);
+        }
+    });
+    __syncthreads();
+    const uint32_t n = sh.nc;
+    __syncthreads();
+    return n;
+}
+
+// Exact cut among n <= kCand candidates in LDS by counting: q consecutive
+// lanes (q a power of two) share one candidate and split the comparisons.
+// Top-k: the packed key of rank `rank` (1 = largest, by value then index).
+__device__ __forceinline__ unsigned long long cand_rank(FinishShared &sh, uint32_t n, uint32_t rank)
+{
+    uint32_t np = 1;
+    while (np < n) np <<= 1;
+    const uint32_t q = min(64u, (uint32_t)kFThreads / np);
+    const uint32_t e = threadIdx.x / q, part = threadIdx.x % q;
+    const bool real = e < n;
+    const unsigned long long ke = real ? sh.ckey[e] : 0ull;
+    uint32_t larger = 0;
+    uint32_t j = part;
+    for (; j + 7 * q < n; j += 8 * q) {   // eight LDS reads in flight
+#pragma unroll
+        for (int u = 0; u < 8; ++u) larger += sh.ckey[j + u * q] > ke ? 1u : 0u;
+    }
+    for (; j < n; j += q) larger += sh.ckey[j] > ke ? 1u : 0u;
+    for (uint32_t m = 1; m < q; m <<= 1) larger += __shfl_xor(larger, (int)m);
+    if (real && part == 0 && larger + 1 == rank) sh.pick = ke;
+    __syncthreads();
+    const unsigned long long r = sh.pick;
+    __syncthreads();
+    return r;
+}
+
+// Nucleus: the smallest candidate value whose strictly-greater mass (A from
+// the bins above plus the candidates above) is <= limit.
+__device__ __forceinline__ uint32_t cand_cut(FinishShared &sh, uint32_t n, unsigned long long A, double limit)
+{
+    uint32_t np = 1;
+    while (np < n) np <<= 1;
+    const uint32_t q = min(64u, (uint32_t)kFThreads / np);
+    const uint32_t e = threadIdx.x / q, part = threadIdx.x % q;
+    const bool real = e < n;
+    const uint32_t ke = real ? (uint32_t)(sh.ckey[e] >> 32) : 0u;
+    unsigned long long above = 0;
+    uint32_t j = part;
+    for (; j + 7 * q < n; j += 8 * q) {   // eight LDS reads in flight
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            above += (uint32_t)(sh.ckey[j + u * q] >> 32) > ke ? sh.cmass[j + u * q] : 0ull;
+    }
+    for (; j < n; j += q) above += (uint32_t)(sh.ckey[j] >> 32) > ke ? sh.cmass[j] : 0ull;
+    for (uint32_t m = 1; m < q; m <<= 1) above += __shfl_xor(above, (int)m);
+    const bool fits = real && (double)(A + above) <= limit;
+    // the smallest qualifying key: a max over complemented keys
+    const uint32_t t =
+        (uint32_t)block_max<unsigned long long, kFThreads>(fits ? (unsigned long long)(~ke) : 0ull, sh.red);
+    return ~t;
+}
+
+// Slow path of a bin with more than kCand tokens: radix select over the
+// source restricted to that bin.  By count: the rank-th largest 56-bit value
+// (11/11/10/12/12-bit levels).
+template <typename Src, typename Keep>
+__device__ __forceinline__ unsigned long long radix_rank(const Src &src, FinishShared &sh, uint32_t rank, Keep keep)
+{
+    constexpr int kShift[5] = {45, 34, 24, 12, 0};
+    constexpr int kWidth[5] = {11, 11, 10, 12, 12};
+    unsigned long long prefix = 0;
+    for (int level = 0; level < 5; ++level) {
+        const int shift = kShift[level], width = kWidth[level];
+        const int hi = shift + width;
+        const int nd = 1 << width;
+        for (int d = threadIdx.x; d < nd; d += kFThreads) sh.hcnt[d] = 0;
+        __syncthreads();
+        src.each([&](unsigned long long packed) {
+            if (!keep(packed)) return;
+            const unsigned long long v = v56(packed);
+            if (hi < 56 && (v >> hi) != (prefix >> hi)) return;
+            atomicAdd(&sh.hcnt[(uint32_t)(v >> shift) & (uint32_t)(nd - 1)], 1u);
+        });
+        __syncthreads();
+        const int dpt = nd / kFThreads;
+        const int dlo = (int)threadIdx.x * dpt;
+        unsigned long long own = 0;
+        for (int j = 0; j < dpt; ++j) own += sh.hcnt[dlo + j];
+        unsigned long long up =
+            block_scan_inclusive<unsigned long long, kFThreads, true>(own, sh.red) - own;
+        for (int j = dpt - 1; j >= 0; --j) {
+            const unsigned long long cnt = sh.hcnt[dlo + j];
+            if (up < rank && rank <= up + cnt) {
+                sh.sel = (uint32_t)(dlo + j);
+                sh.up = up;
+            }
+            up += cnt;
+        }
+        __syncthreads();
+        prefix |= (unsigned long long)sh.sel << shift;
+        rank -= (uint32_t)sh.up;
+        __syncthreads();
+    }
+    return packed_of_v56(prefix);
+}
+
+// By mass on the value key (11/11/10-bit levels), above-mass starting at A:
+// the smallest key whose strictly-greater mass is <= limit.
+template <typename Src, typename Keep>
+__device__ __forceinline__ uint32_t radix_cut(const Src &src, FinishShared &sh, unsigned long long A, double limit,
+                              Keep keep)
+{
+    constexpr int kShift[3] = {21, 10, 0};
+    constexpr int kWidth[3] = {11, 11, 10};
+    uint32_t prefix = 0;
+    for (int level = 0; level < 3; ++level) {
+        const int shift = kShift[level], width = kWidth[level];
+        const int hi = shift + width;
+        const int nd = 1 << width;
+        for (int d = threadIdx.x; d < nd; d += kFThreads) {
+            sh.bcnt[d] = 0;
+            sh.bmass[d] = 0;
+        }
+        if (threadIdx.x == 0) sh.sel = 0xffffffffu;
+        __syncthreads();
+        src.each([&](unsigned long long packed) {
+            if (!keep(packed)) return;
+            const uint32_t key = (uint32_t)(packed >> 32);
+            if (hi < 32 && (key >> hi) != (prefix >> hi)) return;
+            const uint32_t d = (key >> shift) & (uint32_t)(nd - 1);
+            atomicAdd(&sh.bcnt[d], 1u);
+            atomicAdd(&sh.bmass[d], src.mass(packed));
+        });
+        __syncthreads();
+        const int dpt = (nd + kFThreads - 1) / kFThreads;
+        const int dlo = (int)threadIdx.x * dpt;
+        unsigned long long own = 0;
+        for (int j = 0; j < dpt; ++j)
+            if (dlo + j < nd) own += sh.bmass[dlo + j];
+        unsigned long long up =
+            A + block_scan_inclusive<unsigned long long, kFThreads, true>(own, sh.red) - own;
+        uint32_t cand = 0xffffffffu;
+        unsigned long long cand_up = 0;
+        for (int j = dpt - 1; j >= 0; --j) {
+            const int d = dlo + j;
+            if (d >= nd) continue;
+            if ((double)up > limit) break;
+            if (sh.bcnt[d]) {
+                cand = (uint32_t)d;
+                cand_up = up;
+            }
+            up += sh.bmass[d];
+        }
+        if (cand != 0xffffffffu) atomicMin(&sh.sel, cand);
+        __syncthreads();
+        if (cand != 0xffffffffu && cand == sh.sel) sh.up = cand_up;
+        __syncthreads();
+        prefix |= sh.sel << shift;
+        A = sh.up;
+        __syncthreads();
+    }
+    return prefix;
+}
+
+// Gumbel argmax over the kept tokens (packed >= kpack, key >= tau): per
+// batch of list entries, the noise of the kept ones is requested together
+// (a rejected entry reads element 0 and is ignored), so the gathers overlap.
+__device__ __forceinline__ unsigned long long gumbel_best(const ListSource &src, FinishShared &sh, const float *g,
+                                          unsigned long long kpack, uint32_t tau)
+{
+    unsigned long long best = 0;
+    for (int c0 = src.csub; c0 < src.nch; c0 += kBatch * src.per) {
+        unsigned long long v[kBatch];
+        bool keep[kBatch];
+        float gv[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const int c = c0 + j * src.per;
+            const bool ok = c < src.nch && src.slot < (int)src.nlist[c < src.nch ? c : 0];
+            v[j] = src.lrow[(int64_t)(ok ? c : 0) * src.cap + (ok ? src.slot : 0)];
+            const uint32_t key = (uint32_t)(v[j] >> 32);
+            keep[j] = ok && key > src.tout && v[j] >= kpack && key >= tau;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) gv[j] = g[keep[j] ? unpack_index(v[j]) : 0u];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const unsigned long long cand =
+                pack_key_index(float_key(value_of(v[j]) + gv[j]), unpack_index(v[j]));
+            best = keep[j] ? max(best, cand) : best;
+        }
+    }
+    return block_max<unsigned long long, kFThreads>(best, sh.red);
+}
+
+__device__ __forceinline__ unsigned long long gumbel_best(const RowSource &src, FinishShared &sh, const float *g,
+                                          unsigned long long kpack, uint32_t tau)
+{
+    unsigned long long best = 0;
+    src.each([&](unsigned long long packed) {
+        const uint32_t key = (uint32_t)(packed >> 32);
+        if (packed < kpack || key < tau) return;
+        const uint32_t i = unpack_index(packed);
+        best = max(best, pack_key_index(float_key(key_float(key) + g[i]), i));
+    });
+    return block_max<unsigned long long, kFThreads>(best, sh.red);
+}
+
+// Top-k, nucleus and the Gumbel argmax over one source; writes the id and
+// the cut.  hist: sh.bcnt (and, for nucleus-only rows, sh.bmass) already
+// hold the source's value bins.
+template <typename Src>
+__device__ __forceinline__ void select_and_draw(const SampArgs &a, FinishShared &sh, const Src &src, int b,
+                                uint32_t mode, uint32_t kmax, unsigned long long Z, bool hist)
+{
+    const float M = key_float(kmax);
+    const bool topk = (mode & MODE_TOPK) != 0;
+    auto all = [](unsigned long long) { return true; };
+    unsigned long long kpack = 0;
+    if (topk) {
+        const uint32_t k = (uint32_t)a.top_k[b];
+        if (!hist) bin_hist<false>(src, sh, M, all);
+        int jk;
+        uint32_t r;
+        bin_by_count(sh, k, jk, r);
+        const uint32_t n = compact_bin(src, sh, M, jk, all);
+        if (n <= (uint32_t)kCand)
+            kpack = cand_rank(sh, n, r);
+        else
+            kpack = radix_rank(src, sh, r, [&](unsigned long long p) { return hbin_of(value_of(p), M) == jk; });
+    }
+    auto in_k = [=](unsigned long long packed) { return packed >= kpack; };
+    uint32_t tau = 0;
+    if (mode & MODE_TOPP_MAX) {
+        tau = kmax;   // the maxima (top-k keeps the maximum too)
+    } else if (mode & MODE_TOPP) {
+        unsigned long long Zn = Z;
+        // top-k then nucleus: the bins and total of the top-k set; over the
+        // whole row the exact total replaces the lists' estimate
+        if (topk || !hist) Zn = bin_hist<true>(src, sh, M, in_k);
+        const double limit = (double)a.top_p[b] * (double)Zn;
+        int js;
+        unsigned long long A;
+        bin_by_mass(sh, limit, js, A);
+        const uint32_t n = compact_bin(src, sh, M, js, in_k);
+        if (n <= (uint32_t)kCand)
+            tau = cand_cut(sh, n, A, limit);
+        else
+            tau = radix_cut(src, sh, A, limit, [&](unsigned long long p) {
+                return p >= kpack && hbin_of(value_of(p), M) == js;
+            });
+    }
+    const unsigned long long best = gumbel_best(src, sh, a.gumbel + (int64_t)b * a.gstride, kpack, tau);
+    if (threadIdx.x == 0) {
         a.out_ids[b] = (int32_t)unpack_index(best);
-        ctl->mode = mode | MODE_DONE;
-        ctl->round2 = 0;
-        ctl->tau = cut_tau;
-        ctl->kpack = cut_k;
+        RowCut cut;
+        cut.mode = mode;
+        cut.tau = tau;
+        cut.kpack = kpack;
+        a.cut[b] = cut;
+    }
+}
+
+// Top-k alone or nucleus alone, from the groups' bins of the tokens above
+// T* (added up in sh.bcnt, sh.bmass; this thread's bin's group records in
+// grp): the cut bin jc follows from the bins; every token in the bins
+// before it is kept, and their best Gumbel key is the groups' prefix best at
+// jc; only bin jc's tokens are read (from the groups' bin-sorted arrays,
+// with their noise) and resolved in LDS.  Returns false, having written
+// nothing, when bin jc holds more than kCand tokens.
+__device__ __forceinline__ bool one_pass_draw(const SampArgs &a, FinishShared &sh, const BinRec (&grp)[kGroups],
+                                              int b, uint32_t mode, uint32_t kmax, unsigned long long Z)
+{
+    const float M = key_float(kmax);
+    const bool topk = (mode & MODE_TOPK) != 0;
+    if (threadIdx.x == 0) sh.gstart[kGroups] = 0u;   // (no cut bin found: nothing to resolve)
+    int jc;
+    uint32_t r = 0;
+    unsigned long long A = 0;
+    double limit = 0.0;
+    if (topk) {
+        bin_by_count(sh, (uint32_t)a.top_k[b], jc, r);
+    } else {
+        limit = (double)a.top_p[b] * (double)Z;
+        bin_by_mass(sh, limit, jc, A);
+    }
+    if ((int)threadIdx.x == jc) {
+        unsigned long long up = 0;
+        uint32_t start = 0;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            const bool in = g < a.groups;
+            sh.goff[g] = in ? grp[g].off : 0u;
+            sh.gcnt[g] = in ? grp[g].cnt : 0u;
+            sh.gstart[g] = start;
+            start += in ? grp[g].cnt : 0u;
+            up = in ? max(up, grp[g].above) : up;
+        }
+        sh.gstart[kGroups] = start;
+        sh.up = up;
+    }
+    __syncthreads();
+    const uint32_t n = sh.gstart[kGroups];
+    if (n == 0u || n > (uint32_t)kCand) return false;   // (uniform)
+    // bin jc's tokens: thread t < n takes the t-th, group by group
+    if (threadIdx.x < n) {
+        int g = 0;
+#pragma unroll
+        for (int h = 1; h < kGroups; ++h) g = threadIdx.x >= sh.gstart[h] ? h : g;
+        const SortedTok st = a.sorted[((int64_t)b * a.groups + g) * a.gslots + sh.goff[g] +
+                                      (threadIdx.x - sh.gstart[g])];
+        sh.ckey[threadIdx.x] = st.packed;
+        sh.cgum[threadIdx.x] = st.g;
+        sh.cmass[threadIdx.x] = topk ? 0ull : mass_fixed(value_of(st.packed), (double)M, sh.tab);
+    }
+    __syncthreads();
+    unsigned long long kpack = 0;
+    uint32_t tau = 0;
+    if (topk)
+        kpack = cand_rank(sh, n, r);
+    else
+        tau = cand_cut(sh, n, A, limit);
+    // the best of the bins before jc and of bin jc's kept tokens
+    unsigned long long best = threadIdx.x == 0 ? sh.up : 0ull;
+    if (threadIdx.x < n) {
+        const unsigned long long v = sh.ckey[threadIdx.x];
+        const bool keep = topk ? v >= kpack : (uint32_t)(v >> 32) >= tau;
+        if (keep) best = max(best, pack_key_index(float_key(value_of(v) + sh.cgum[threadIdx.x]),
+                                                  unpack_index(v)));
+    }
+    best = block_max<unsigned long long, kFThreads>(best, sh.red);
+    if (threadIdx.x == 0) {
+        a.out_ids[b] = (int32_t)unpack_index(best);
+        RowCut cut;
+        cut.mode = mode;
+        cut.tau = tau;
+        cut.kpack = kpack;
+        a.cut[b] = cut;
+    }
+    return true;
+}
+
+__global__ __launch_bounds__(kFThreads) void samp_finish_kernel(const SampArgs a)
+{
+    __shared__ FinishShared sh;
+    const int b = blockIdx.x;
+    const uint32_t mode = row_mode(a, b);
+    const ChunkRec *rec = a.rec + (int64_t)b * a.nchunks;
+    const int nch = a.nchunks;
+    if (mode & (MODE_GREEDY | MODE_PLAIN)) {
+        unsigned long long best = 0;
+        for (int c = threadIdx.x; c < nch; c += kFThreads) best = max(best, rec[c].best);
+        best = block_max<unsigned long long, kFThreads>(best, sh.red);
+        if (threadIdx.x == 0) {
+            a.out_ids[b] = (int32_t)unpack_index(best);
+            RowCut cut = {mode, 0u, 0ull};
+            a.cut[b] = cut;
+        }
+        return;
+    }
+    const bool use_hist = (mode & (MODE_TOPK | MODE_TOPP)) != 0;
+    const bool single = (mode == MODE_TOPK) || (mode == MODE_TOPP);
+
+    // ---- one round of loads: the groups' records of this thread's bin
+    // (requested blind: bins past the last one written hold stale data,
+    // dropped once T* is known), the groups' totals, the chunk records.
+    static_assert(kHBins == kFThreads, "one finish bin per thread");
+    BinRec grp[kGroups];
+    if (use_hist) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)   // (a missing group reads group 0, dropped below)
+            grp[g] = a.bins[((int64_t)b * a.groups + (g < a.groups ? g : 0)) * kHBins + threadIdx.x];
+        if (threadIdx.x < (unsigned)a.groups) sh.gtot[threadIdx.x] = a.tot[(int64_t)b * a.groups + threadIdx.x];
+    }
+    uint32_t km = 0, to = 0;
+    for (int c = threadIdx.x; c < nch; c += kFThreads) {
+        const ChunkRec r = rec[c];
+        km = max(km, r.mkey);
+        to = max(to, r.outkey);
+        sh.nlist[c] = r.n;
+    }
+    if (threadIdx.x < 64) sh.tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+    uint32_t kmax, tout;
+    block_max2<kFThreads>(km, to, sh.red, kmax, tout);   // (its barrier orders the LDS fills)
+    const float Mf = key_float(kmax);
+    const double M = (double)Mf;
+    RowTot tot = {};
+    if (use_hist) {   // the groups' bins and totals added up
+        const bool in = (int)threadIdx.x < bins_above(tout, Mf);
+        uint32_t cnt = 0;
+        unsigned long long mass = 0;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            if (!in || g >= a.groups) {
+                grp[g].cnt = 0;
+                grp[g].off = 0;
+                grp[g].mass = 0;
+                grp[g].above = 0;
+            }
+            cnt += grp[g].cnt;
+            mass += grp[g].mass;
+        }
+        sh.bcnt[threadIdx.x] = cnt;
+        sh.bmass[threadIdx.x] = mass;
+        for (int g = 0; g < a.groups; ++g) {
+            tot.Z += sh.gtot[g].Z;
+            tot.mu += sh.gtot[g].mu;
+            tot.nu += sh.gtot[g].nu;
+        }
+        __syncthreads();
+    }
+    // The lists hold every token above T*; the cut must lie above T*.
+    bool ok;
+    if (mode & MODE_TOPK) ok = tot.nu >= (uint32_t)a.top_k[b];
+    else if (mode & MODE_TOPP) ok = (double)tot.mu > (double)a.top_p[b] * (double)tot.Z;
+    else ok = tout < kmax;   // p <= 0: every maximum must be above T*
+    if (ok && single && one_pass_draw(a, sh, grp, b, mode, kmax, tot.Z)) return;
+    if (ok) {
+        ListSource src;
+        src.lrow = a.list + (int64_t)b * nch * a.cap;
+        src.nlist = sh.nlist;
+        src.cap = a.cap;
+        src.per = kFThreads / a.cap;
+        src.nch = nch;
+        src.slot = (int)threadIdx.x % a.cap;
+        src.csub = (int)threadIdx.x / a.cap;
+        src.tout = tout;
+        src.M = M;
+        src.tab = sh.tab;
+        select_and_draw(a, sh, src, b, mode, kmax, tot.Z, use_hist);
+    } else {
+        RowSource rs{a.logits + (int64_t)b * a.lstride,
+                     a.mask ? a.mask + (int64_t)b * a.mstride : nullptr,
+                     Scaler(a.temperature[b]), M, a.vocab, sh.tab};
+        select_and_draw(a, sh, rs, b, mode, kmax, tot.Z, false);
     }
 }
 
@@ -1303,10 +1610,11 @@ __global__ __launch_bounds__(kRThreads) void samp_resolve_kernel(const SampArgs 
 __global__ __launch_bounds__(kRThreads) void samp_extras_kernel(const SampArgs a)
 {
     const int b = blockIdx.x;
-    const uint32_t mode = a.flags ? (a.ctl[b].mode & ~MODE_DONE) : row_mode(a, b);
+    const RowCut cut = a.cut[b];
+    const uint32_t mode = cut.mode;
     const bool greedy = (mode & MODE_GREEDY) != 0;
-    const uint32_t tau = (a.flags && !greedy) ? a.ctl[b].tau : 0u;
-    const unsigned long long kpack = (a.flags && !greedy) ? a.ctl[b].kpack : 0ull;
+    const uint32_t tau = greedy ? 0u : cut.tau;
+    const unsigned long long kpack = greedy ? 0ull : cut.kpack;
     const float T = a.temperature[b];
     const float *z = a.logits + (int64_t)b * a.lstride;
     const uint8_t *mk = a.mask ? a.mask + (int64_t)b * a.mstride : nullptr;
@@ -1443,28 +1751,23 @@ __global__ __launch_bounds__(kRThreads) void samp_extras_kernel(const SampArgs a
         if (a.out_top_probs) a.out_top_probs[(int64_t)b * 8 + r] = pr;
     }
     if (threadIdx.x == 0 && a.out_prob) {
-        const float v = value(id);
+        const float v = (id >= 0 && id < V) ? value(id) : __builtin_nanf("");
         a.out_prob[b] = (float)(exp((double)v - (double)M) / Z);
     }
 }
 
-// MASK: a vocabulary mask is given (without one, the row-parallel passes
-// are compiled with every logit allowed).
+// MASK: a vocabulary mask is given (without one, the scan is compiled with
+// every logit allowed).
 template <bool VEC4, bool MASK>
-void launch_passes(const SampArgs &a, const dim3 grid, uint32_t flags, hipStream_t stream)
+void launch_passes(const SampArgs &a, const dim3 grid, hipStream_t stream)
 {
-    if (flags) {
-        samp_max_kernel<VEC4, MASK><<<grid, kThreads, 0, stream>>>(a);
-        samp_bins_kernel<VEC4, MASK><<<grid, kThreads, 0, stream>>>(a);
-        samp_select_kernel<<<a.batch, kRThreads, 0, stream>>>(a);
+    switch (a.chunk / kThreads) {
+    case 16: samp_scan_kernel<VEC4, MASK, 16><<<grid, kThreads, 0, stream>>>(a); break;
+    case 8: samp_scan_kernel<VEC4, MASK, 8><<<grid, kThreads, 0, stream>>>(a); break;
+    default: samp_scan_kernel<VEC4, MASK, 4><<<grid, kThreads, 0, stream>>>(a); break;
     }
-    samp_collect_kernel<VEC4, MASK, false><<<grid, kThreads, 0, stream>>>(a);
-    samp_resolve_kernel<false><<<a.batch, kRThreads, 0, stream>>>(a);
-    if ((flags & 3u) == 3u) {
-        // top-k then nucleus: rows whose nucleus cut lies above their top-k bin
-        samp_collect_kernel<VEC4, MASK, true><<<grid, kThreads, 0, stream>>>(a);
-        samp_resolve_kernel<true><<<a.batch, kRThreads, 0, stream>>>(a);
-    }
+    samp_hist_kernel<<<dim3(a.groups, a.batch), kThreads, 0, stream>>>(a);
+    samp_finish_kernel<<<a.batch, kFThreads, 0, stream>>>(a);
     if (a.out_prob || a.out_top_ids || a.out_top_probs)
         samp_extras_kernel<<<a.batch, kRThreads, 0, stream>>>(a);
 }
@@ -1479,9 +1782,9 @@ size_t sampler_workspace_bytes(int32_t batch, int32_t vocab)
 hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_stride,
                           const float *gumbel, int64_t gumbel_stride, const uint8_t *mask,
                           int64_t mask_stride, const float *temperature, const float *top_p,
-                          const int32_t *top_k, int32_t batch, int32_t vocab, uint32_t flags,
-                          float *out_prob, int32_t *out_top_ids, float *out_top_probs,
-                          void *workspace, hipStream_t stream)
+                          const int32_t *top_k, int32_t batch, int32_t vocab, float *out_prob,
+                          int32_t *out_top_ids, float *out_top_probs, void *workspace,
+                          hipStream_t stream)
 {
     if (batch == 0) return hipSuccess;
     const SampLayout L = sampler_layout(batch, vocab);
@@ -1499,14 +1802,15 @@ hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_
     a.vocab = vocab;
     a.chunk = L.chunk;
     a.nchunks = L.nchunks;
-    a.flags = flags;
-    a.ctl = reinterpret_cast<SampCtl *>(ws + L.ctl_off);
-    a.cnt = reinterpret_cast<uint32_t *>(ws + L.cnt_off);
-    a.mass = reinterpret_cast<unsigned long long *>(ws + L.mass_off);
-    a.cand = reinterpret_cast<unsigned long long *>(ws + L.cand_off);
-    a.kap = reinterpret_cast<uint32_t *>(ws + L.kap_off);
-    a.part_max = reinterpret_cast<uint32_t *>(ws + L.pmax_off);
-    a.part_best = reinterpret_cast<unsigned long long *>(ws + L.pbest_off);
+    a.cap = L.cap;
+    a.groups = L.groups;
+    a.gslots = L.gslots;
+    a.rec = reinterpret_cast<ChunkRec *>(ws + L.rec_off);
+    a.list = reinterpret_cast<unsigned long long *>(ws + L.list_off);
+    a.bins = reinterpret_cast<BinRec *>(ws + L.bins_off);
+    a.sorted = reinterpret_cast<SortedTok *>(ws + L.sorted_off);
+    a.tot = reinterpret_cast<RowTot *>(ws + L.tot_off);
+    a.cut = reinterpret_cast<RowCut *>(ws + L.cut_off);
     a.mask = mask;
     a.mstride = mask_stride;
     a.out_prob = out_prob;
@@ -1519,11 +1823,11 @@ hipError_t launch_sampler(int32_t *out_ids, const float *logits, int64_t logits_
                       (!mask || (reinterpret_cast<uintptr_t>(mask) % 4 == 0 && mask_stride % 4 == 0)) &&
                       vocab % 4 == 0;
     if (vec4)
-        a.mask ? launch_passes<true, true>(a, grid, flags, stream)
-               : launch_passes<true, false>(a, grid, flags, stream);
+        a.mask ? launch_passes<true, true>(a, grid, stream)
+               : launch_passes<true, false>(a, grid, stream);
     else
-        a.mask ? launch_passes<false, true>(a, grid, flags, stream)
-               : launch_passes<false, false>(a, grid, flags, stream);
+        a.mask ? launch_passes<false, true>(a, grid, stream)
+               : launch_passes<false, false>(a, grid, stream);
     return hipGetLastError();
 }
 

@@ -145,16 +145,16 @@ def test_sampler_validation():
 
     def call(**kw):
         a = dict(ids=FAKE, z=FAKE, zs=0, g=FAKE, gs=0, t=FAKE, p=FAKE, k=FAKE, B=8, V=1000,
-                 flags=3, ws=FAKE, wsb=need)
+                 ws=FAKE, wsb=need)
         a.update(kw)
         return L.pkv_sample_next_token(a["ids"], a["z"], a["zs"], a["g"], a["gs"], a["t"], a["p"],
-                                       a["k"], a["B"], a["V"], a["flags"], a["ws"], a["wsb"], None)
+                                       a["k"], a["B"], a["V"], a["ws"], a["wsb"], None)
 
     assert call(z=None) == _lib.PKV_ERR_INVALID_ARG
     assert call(t=FAKE + 2) == _lib.PKV_ERR_INVALID_ARG
     assert call(V=0) == _lib.PKV_ERR_UNSUPPORTED
     assert call(V=(1 << 24) + 1) == _lib.PKV_ERR_UNSUPPORTED
-    assert call(flags=4) == _lib.PKV_ERR_INVALID_ARG
+    assert call(B=65536) == _lib.PKV_ERR_INVALID_ARG
     assert call(zs=999) == _lib.PKV_ERR_INVALID_ARG
     assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
     assert call(B=0, ids=None, z=None, g=None) == _lib.PKV_OK
@@ -245,16 +245,15 @@ def test_sampler_ex_validation():
 
     def call(**kw):
         a = dict(ids=FAKE, z=FAKE, g=FAKE, m=None, ms=0, t=FAKE, p=FAKE, k=FAKE, B=4, V=1000,
-                 flags=3, prob=None, tid=None, tpr=None, ws=FAKE, wsb=need)
+                 prob=None, tid=None, tpr=None, ws=FAKE, wsb=need)
         a.update(kw)
         return L.pkv_sample_next_token_ex(a["ids"], a["z"], 0, a["g"], 0, a["m"], a["ms"], a["t"],
-                                          a["p"], a["k"], a["B"], a["V"], a["flags"], a["prob"],
-                                          a["tid"], a["tpr"], a["ws"], a["wsb"], None)
+                                          a["p"], a["k"], a["B"], a["V"], a["prob"], a["tid"],
+                                          a["tpr"], a["ws"], a["wsb"], None)
 
     assert call(m=FAKE, ms=999) == _lib.PKV_ERR_INVALID_ARG     # mask stride below vocab
     assert call(prob=FAKE + 2) == _lib.PKV_ERR_INVALID_ARG      # misaligned output
     assert call(tid=FAKE + 1) == _lib.PKV_ERR_INVALID_ARG
-    assert call(flags=4) == _lib.PKV_ERR_INVALID_ARG
     assert call(z=None) == _lib.PKV_ERR_INVALID_ARG
     assert call(wsb=need - 1) == _lib.PKV_ERR_WORKSPACE
     assert call(B=0, ids=None, z=None, g=None, t=None, p=None, k=None) == _lib.PKV_OK

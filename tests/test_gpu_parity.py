@@ -250,26 +250,11 @@ def test_decode_step_long_sampled_heads():
 
 # ---------------------------------------------------------------- sampler --
 
-def _flags(t, p, k, V):
-    f = 0
-    if np.any((k > 0) & (k < V)):
-        f |= pkv.PKV_SAMPLE_TOPK
-    if np.any(p < 1):
-        f |= pkv.PKV_SAMPLE_TOPP
-    return f
-
-
-def _sample_and_compare(z, g, t, p, k, flags=None):
-    B, V = z.shape
-    if flags is None:
-        flags = _flags(t, p, k, V)
-    ids = pkv.sample_next_token(dev_f32(z), dev_f32(g), dev_f32(t), dev_f32(p), dev_i32(k),
-                                flags=flags).cpu().numpy()
+def _sample_and_compare(z, g, t, p, k):
+    ids = pkv.sample_next_token(dev_f32(z), dev_f32(g), dev_f32(t), dev_f32(p),
+                                dev_i32(k)).cpu().numpy()
     torch.cuda.synchronize()
-    # the oracle sees the filters that the flags leave on
-    p_eff = p if flags & pkv.PKV_SAMPLE_TOPP else np.ones_like(p)
-    k_eff = k if flags & pkv.PKV_SAMPLE_TOPK else np.zeros_like(k)
-    ref, infos = oracle.sample(z, g, t, p_eff, k_eff)
+    ref, infos = oracle.sample(z, g, t, p, k)
     bad, amb = compare_ids(ids, ref, infos)
     return bad, amb, infos
 
@@ -302,17 +287,20 @@ def test_sampler_mixed_rows_and_edges():
     assert amb == 0
 
 
-def test_sampler_flags_turn_filters_off():
+def test_sampler_filters_follow_each_rows_settings():
+    """Each row's own top_k and top_p decide its filters: k <= 0 or k >= V
+    and p >= 1 turn a filter off for that row only, next to rows that use
+    it, in one call."""
     rng = np.random.default_rng(56)
-    B, V = 8, 9000
+    B, V = 10, 9000
     z = (rng.standard_normal((B, V), dtype=np.float32) * 2).astype(np.float32)
     g = rng.gumbel(size=(B, V)).astype(np.float32)
     t = np.full(B, 0.9, np.float32)
-    p = np.full(B, 0.5, np.float32)
-    k = np.full(B, 10, np.int32)
-    for flags in (0, pkv.PKV_SAMPLE_TOPK, pkv.PKV_SAMPLE_TOPP, 3):
-        bad, amb, _ = _sample_and_compare(z, g, t, p, k, flags=flags)
-        assert not bad and amb == 0, flags
+    p = np.array([0.5, 1.0, 1.5, 0.5, 1.0, 0.5, 0.999, 1.0, 0.5, 0.0], np.float32)
+    k = np.array([10, 10, 0, 0, -3, V, V + 5, 0, 1, 10], np.int32)
+    bad, amb, infos = _sample_and_compare(z, g, t, p, k)
+    assert not bad and amb == 0, bad
+    assert [i.kept for i in infos[1:3]] == [10, V]    # top-k alone; nothing
 
 
 def test_sampler_tiny_vocab_and_single_row():

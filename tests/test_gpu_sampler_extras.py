@@ -30,18 +30,8 @@ def _gpu():
     torch.cuda.init()
 
 
-def _flags(p, k, V):
-    f = 0
-    if np.any((k > 0) & (k < V)):
-        f |= pkv.PKV_SAMPLE_TOPK
-    if np.any(p < 1):
-        f |= pkv.PKV_SAMPLE_TOPP
-    return f
-
-
 def _run(z, g, t, p, k, mask=None, mask_stride_pad=0):
     B, V = z.shape
-    flags = _flags(p, k, V)
     mdev = None
     if mask is not None:
         if mask_stride_pad:
@@ -52,9 +42,9 @@ def _run(z, g, t, p, k, mask=None, mask_stride_pad=0):
         else:
             mdev = torch.from_numpy(np.ascontiguousarray(mask, np.uint8)).cuda()
     ids, prob, tid, tpr = pkv.sample_next_token_ex(dev_f32(z), dev_f32(g), dev_f32(t), dev_f32(p),
-                                                   dev_i32(k), mask=mdev, flags=flags)
+                                                   dev_i32(k), mask=mdev)
     plain_ids = pkv.sample_next_token_ex(dev_f32(z), dev_f32(g), dev_f32(t), dev_f32(p),
-                                         dev_i32(k), mask=mdev, flags=flags, extras=False)
+                                         dev_i32(k), mask=mdev, extras=False)
     torch.cuda.synchronize()
     out = (ids.cpu().numpy(), prob.cpu().numpy(), tid.cpu().numpy(), tpr.cpu().numpy())
     assert np.array_equal(out[0], plain_ids.cpu().numpy())

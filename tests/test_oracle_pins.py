@@ -336,10 +336,12 @@ def test_nucleus_closed_forms():
     # uniform logits: every token has mass 1/V; the nucleus keeps all ties
     info = oracle.sample_row(np.zeros(64, np.float32), g, 1.0, 0.5, 0)
     assert info.kept == 64
-    # p <= 0 keeps only the maxima
+    # p <= 0 keeps only the maxima; no mass is compared, so no rounding can
+    # move that cut: its margin is infinite (never excused as ambiguous)
     z3 = np.arange(64, dtype=np.float32) % 7
     info = oracle.sample_row(z3, g, 1.0, 0.0, 0)
     assert info.kept == int(np.sum(z3 == z3.max()))
+    assert info.margin == float("inf")
 
 
 def test_temperature_applies_before_nucleus():
