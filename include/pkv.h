@@ -86,6 +86,38 @@ uint32_t *pkv_get_error_word(void);
  * never depend on the wait, so the launch still stays inside its buffers. */
 int pkv_set_wait_limit(uint32_t polls);
 
+/* ---- measurement helpers -----------------------------------------------------
+ * Not part of the decode path: what the benchmark holds the kernels against
+ * (the nanochat page's inference benchmark reports model bandwidth
+ * utilisation against the device's bandwidth; these give the device's own
+ * figures).
+ *
+ * Streaming-read probe: reads `bytes` of device memory at buf once, with the
+ * 16-byte non-temporal vector loads the attention kernels stream K/V with,
+ * grid-stride over `workgroups` workgroups of 256 threads (0: 16 per compute
+ * unit).  sink: device uint32 [64], practically never written (it keeps the
+ * loads from being optimised out).  Timing is the caller's (HIP events on
+ * `stream`).  bytes: a multiple of 16; buf and sink 16- and 4-byte aligned. */
+int pkv_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t workgroups,
+                          hipStream_t stream);
+
+/* Properties of a device, from the HIP runtime (hipGetDeviceProperties). */
+typedef struct {
+    char name[256];
+    char arch[64];                  /* e.g. "gfx950:sramecc+:xnack-" */
+    int32_t compute_units;
+    int32_t clock_khz;              /* peak shader clock */
+    int32_t memory_clock_khz;
+    int32_t memory_bus_width_bits;
+    int32_t l2_cache_bytes;
+    int32_t lds_per_workgroup_bytes;
+    int32_t wavefront_size;
+    int32_t pad;
+    uint64_t total_memory_bytes;
+} pkv_device_info;
+
+int pkv_get_device_info(int32_t device, pkv_device_info *out);
+
 /* ---- slot mapping ---------------------------------------------------------
  * Decode-step slot of each row's new token (nano-vllm "Model Runner" page,
  * sections "allocated kv cache" and "prefill and decode"): a row whose

@@ -9,6 +9,7 @@ GPU, but every call does.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
@@ -68,6 +69,28 @@ def _dev(t: torch.Tensor, name: str, dtype) -> int:
 def _packed(t: torch.Tensor, name: str):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0) -> None:
+    """Streaming-read probe over the bytes of `buf` (a multiple of 16); sink:
+    int32 [64] on the same device.  Timing is the caller's."""
+    if not buf.is_cuda:
+        raise ValueError("buf must be a GPU tensor")
+    _packed(buf, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    _lib.check(_lib.lib().pkv_probe_stream_read(
+        buf.data_ptr(), nbytes, _dev(sink, "sink", torch.int32), workgroups, _stream()),
+        "probe_stream_read")
+
+
+def device_info(device: int = 0) -> dict:
+    """Properties of a device as the HIP runtime reports them."""
+    info = _lib.DeviceInfo()
+    _lib.check(_lib.lib().pkv_get_device_info(device, ctypes.byref(info)), "device_info")
+    out = {f: getattr(info, f) for f, _ in _lib.DeviceInfo._fields_ if f != "pad"}
+    out["name"] = info.name.decode(errors="replace")
+    out["arch"] = info.arch.decode(errors="replace")
+    return out
 
 
 def slot_mapping(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,

@@ -37,6 +37,8 @@ PROTOTYPES = {
     "pkv_set_error_word": (ctypes.c_int, [_P]),
     "pkv_get_error_word": (_P, []),
     "pkv_set_wait_limit": (ctypes.c_int, [_U32]),
+    "pkv_probe_stream_read": (ctypes.c_int, [_P, _SZ, _P, _I32, _P]),
+    "pkv_get_device_info": (ctypes.c_int, [_I32, _P]),
     "pkv_slot_mapping": (ctypes.c_int, [_P, _P, _I32, _P, _I32, _I32, _P]),
     "pkv_kv_store": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I64, _P]),
     "pkv_decode_split_tokens": (_I32, [_I32, _I32, _I32, _I32, _I32]),
@@ -76,6 +78,17 @@ PROTOTYPES = {
     "pkv_sample_next_token_ex": (ctypes.c_int, [_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _I32,
                                                 _I32, _P, _P, _P, _P, _SZ, _P]),
 }
+
+
+
+class DeviceInfo(ctypes.Structure):
+    """pkv_device_info (include/pkv.h)."""
+    _fields_ = [("name", ctypes.c_char * 256), ("arch", ctypes.c_char * 64),
+                ("compute_units", _I32), ("clock_khz", _I32), ("memory_clock_khz", _I32),
+                ("memory_bus_width_bits", _I32), ("l2_cache_bytes", _I32),
+                ("lds_per_workgroup_bytes", _I32), ("wavefront_size", _I32), ("pad", _I32),
+                ("total_memory_bytes", ctypes.c_uint64)]
+
 
 _lib = None
 

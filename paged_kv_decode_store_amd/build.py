@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 DEVICE_SOURCES = ["slot_store.hip", "decode_attention.hip", "decode_attention_mfma.hip",
-                  "varlen_attention.hip", "sampler.hip", "static_scratch.hip"]
+                  "varlen_attention.hip", "sampler.hip", "static_scratch.hip", "probe.hip"]
 HOST_SOURCES = ["api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include")]
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",

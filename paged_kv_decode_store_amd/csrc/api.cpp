@@ -178,6 +178,47 @@ int pkv_set_wait_limit(uint32_t polls)
     return PKV_OK;
 }
 
+int pkv_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t workgroups,
+                          hipStream_t stream)
+{
+    REQUIRE(bytes % 16 == 0, PKV_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+    if (bytes == 0) return PKV_OK;
+    REQUIRE(buf && sink, PKV_ERR_INVALID_ARG, "null pointer");
+    REQUIRE(aligned(buf, 16) && aligned(sink, 4), PKV_ERR_INVALID_ARG, "misaligned buffer");
+    REQUIRE(workgroups >= 0, PKV_ERR_INVALID_ARG, "workgroups must be >= 0");
+    if (workgroups == 0) {
+        int dev = 0, cus = 0;
+        int rc = hip_status(hipGetDevice(&dev), "hipGetDevice");
+        if (rc != PKV_OK) return rc;
+        rc = hip_status(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+                        "compute unit count");
+        if (rc != PKV_OK) return rc;
+        workgroups = 16 * cus;
+    }
+    return hip_status(pkv::launch_stream_read(buf, bytes, sink, workgroups, stream),
+                      "stream read probe launch");
+}
+
+int pkv_get_device_info(int32_t device, pkv_device_info *out)
+{
+    REQUIRE(out, PKV_ERR_INVALID_ARG, "null pointer");
+    hipDeviceProp_t p;
+    const int rc = hip_status(hipGetDeviceProperties(&p, device), "hipGetDeviceProperties");
+    if (rc != PKV_OK) return rc;
+    memset(out, 0, sizeof(*out));
+    snprintf(out->name, sizeof(out->name), "%s", p.name);
+    snprintf(out->arch, sizeof(out->arch), "%s", p.gcnArchName);
+    out->compute_units = p.multiProcessorCount;
+    out->clock_khz = p.clockRate;
+    out->memory_clock_khz = p.memoryClockRate;
+    out->memory_bus_width_bits = p.memoryBusWidth;
+    out->l2_cache_bytes = p.l2CacheSize;
+    out->lds_per_workgroup_bytes = (int32_t)p.sharedMemPerBlock;
+    out->wavefront_size = p.warpSize;
+    out->total_memory_bytes = (uint64_t)p.totalGlobalMem;
+    return PKV_OK;
+}
+
 int pkv_slot_mapping(int32_t *slot_mapping, const int32_t *block_tables,
                      int32_t block_table_stride, const int32_t *context_lens, int32_t batch,
                      int32_t block_size, hipStream_t stream)

@@ -125,6 +125,11 @@ hipError_t launch_varlen_slot_mapping(int32_t *slot_mapping, const int32_t *bloc
 // kernel is ALU-bound beyond group 2 on MI355X).
 constexpr int32_t kMfmaMinGroup = 3;
 
+// Streaming-read probe over `bytes` (a multiple of 16) of device memory with
+// `workgroups` workgroups of 256 threads; sink: 64 uint32, almost never written.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t workgroups,
+                              hipStream_t stream);
+
 // The library's fixed device scratch array (PKV_STATIC_SCRATCH_BYTES) on
 // the current device: its device address, resolved on first use per device.
 hipError_t static_scratch(void **out);

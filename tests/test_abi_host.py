@@ -26,10 +26,22 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.PROTOTYPES)
+
+
+def test_probe_arguments_are_checked_before_any_launch():
+    """The streaming-read probe refuses a length that is not a multiple of 16,
+    misaligned buffers and a negative workgroup count (no kernel runs here)."""
+    L = _lib.lib()
+    assert L.pkv_probe_stream_read(FAKE, 24, FAKE, 0, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_probe_stream_read(FAKE + 8, 32, FAKE, 0, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_probe_stream_read(FAKE, 32, FAKE + 2, 0, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_probe_stream_read(FAKE, 32, FAKE, -1, None) == _lib.PKV_ERR_INVALID_ARG
+    assert L.pkv_probe_stream_read(None, 0, None, 0, None) == _lib.PKV_OK
+    assert L.pkv_get_device_info(0, None) == _lib.PKV_ERR_INVALID_ARG
 
 
 def test_error_word_setting_is_per_thread_and_checked():
