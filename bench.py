@@ -291,6 +291,21 @@ def main():
         del lcopies
         log(f"[bench] sampler graph replay: {graph_samp_us:.2f} us per draw "
             f"({samp_copies} logits copies)")
+    # The reduce's floor: one launch, with the reduce's grid (one wave per row
+    # and query head, four per workgroup), that only streams the workspace
+    # holding the split partials (all splits; the reduce reads a row's used
+    # ones), as a graph of L launches like the reduce's.
+    reduce_floor = None
+    if not args.no_graph and not cascade:
+        pbytes = (ws.numel() // 16) * 16
+        sink = torch.zeros(64, dtype=torch.int32, device=dev)
+        fl_us = 1e3 * graph_time_ms(
+            lambda c: pkv.probe_stream_read(ws[:pbytes], sink, workgroups=(B * Hq + 3) // 4),
+            ncalls=L)
+        reduce_floor = {"us": round(fl_us, 3), "bytes": pbytes,
+                        "what": "pkv_probe_stream_read over the partials workspace with the "
+                                "reduce's grid, graph replay"}
+        log(f"[bench] reduce floor: {fl_us:.2f} us per launch")
     warm_attn_us = None
     if R > 1 and not args.no_graph:
         # the same pools every time: what a cache-resident workload reaches
@@ -362,6 +377,9 @@ def main():
         "attention_us_per_layer": round(attn_us_layer, 3),
         "attention_timing": "hip_graph_replay" if graph_attn_us is not None else "hip_events",
         "eager_event_us_per_layer": {"partial": round(part_ev_us, 3), "reduce": round(red_ev_us, 3)},
+        "reduce_us_per_layer": None if graph_attn_us is None or graph_part_us is None else
+        round(graph_attn_us - graph_part_us, 3),
+        "reduce_floor": reduce_floor,
         "sampler_us": round(samp_avg_us, 3),
         "sampler_timing": (f"hip_graph_replay over {samp_copies} logits copies"
                            if graph_samp_us is not None else "hip_events in the eager step"),

@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
     for (int j = 0; j < DPL; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int k = 0; k < kSpec; ++k) {
-        const float mk = __shfl(mv, k);   // split k's max, held by lane k
+        const float mk = read_lane(mv, k);   // split k's max, held by lane k
         if (k < ns) {
             const float w = __builtin_amdgcn_exp2f(mk - M);
 #pragma unroll

@@ -66,16 +66,28 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// Lane `lane`'s value, as a scalar.
+__device__ __forceinline__ float read_lane(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Max and sum over the whole wave: the four 16-lane rows reduce by DPP, then
+// the row results are read as scalars and combined in a fixed order.  Every
+// lane of the wave must be active; every lane gets the result.
 __device__ __forceinline__ float wave_max(float v)
 {
-    for (int x = 32; x >= 1; x >>= 1) v = fmaxf(v, __shfl_xor(v, x));
-    return v;
+    v = fmaxf(v, dpp_mov<DPP_QUAD_XOR1>(v));
+    v = fmaxf(v, dpp_mov<DPP_QUAD_XOR2>(v));
+    v = fmaxf(v, dpp_mov<DPP_ROW_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp_mov<DPP_ROW_MIRROR>(v));
+    return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v)
 {
-    for (int x = 32; x >= 1; x >>= 1) v += __shfl_xor(v, x);
-    return v;
+    v = group_sum<16>(v);
+    return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
