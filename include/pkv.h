@@ -433,19 +433,23 @@ int pkv_varlen_paged_attention(void *out, int64_t out_stride, const void *q,
  *            arithmetic); p <= 0 keeps only the maxima (p >= 1: off)
  *     id = argmax over kept i of fl32(s_i + gumbel_i), ties to lower index
  * The Gumbel noise is an input (standard Gumbel, fp32), so the draw is
- * reproducible.  Only the ids are written.  Two launches: one pass over the
- * logits (per-chunk maxima and candidate lists), then one workgroup per row
- * that selects the cut exactly from the candidates, or, when they cannot be
- * shown to hold the cut (e.g. k larger than the candidate lists, or many
- * tokens tied at the cut), from the whole row read again (exact, slower).
+ * reproducible.  Only the ids are written.  Three launches: one pass over
+ * the logits (per-chunk maxima and candidate lists), a few workgroups per
+ * row that bin the candidates below the row max (counts, exact masses, best
+ * Gumbel keys), then one workgroup per row that resolves the cut exactly
+ * inside its bin, or, when the candidates cannot be shown to hold the cut
+ * (e.g. k larger than the candidate lists, or many tokens tied at the cut),
+ * from the whole row read again (exact, slower).
  * out_ids      int32 [batch]
  * logits       fp32 [batch][vocab], row b at b*logits_stride (elements)
- * gumbel       fp32 [batch][vocab], row b at b*gumbel_stride; only read
+ * gumbel       fp32 [batch][vocab], row b at b*gumbel_stride; read for the
+ *              candidates (about one token in eight of a nucleus row) and
  *              where a token is eligible (unused for greedy rows)
  * temperature, top_p  fp32 [batch];  top_k  int32 [batch]
  * vocab        1 .. 2^24;  batch <= 65535
  * workspace    >= pkv_sampler_workspace_bytes(batch, vocab), 256-B aligned;
- *              about 3 bytes per logit; contents on entry are ignored */
+ *              about 3 bytes per logit plus ~200 KB per filtered row
+ *              (4.5 B per logit at 151,936); contents on entry are ignored */
 size_t pkv_sampler_workspace_bytes(int32_t batch, int32_t vocab);
 
 int pkv_sample_next_token(int32_t *out_ids, const float *logits,

@@ -1,5 +1,5 @@
 // Next-token sampler: temperature, top-k, nucleus (top-p) and a Gumbel-max
-// draw, on fp32 logits [B][V], in two launches.
+// draw, on fp32 logits [B][V], in three launches.
 //
 // scan   (one 256-thread workgroup per (chunk, row); the one pass over the
 //        logits).  Greedy and unfiltered rows reduce their chunk to a best
@@ -12,24 +12,37 @@
 //        than every unlisted one, so the chunk also records the largest
 //        value it left out and, for nucleus rows, the mass of what it left
 //        out (relative to M_c).
-// finish (one 1024-thread workgroup per row).  With T* the largest value
-//        left out by any chunk, the lists hold every token of the row with
-//        s > T*.  Their exact masses exp(s - M) (fp64, then 2^-38 fixed
-//        point: sums are order independent and bit-reproducible) plus the
-//        left-out masses give Z.  The top-k cut is a radix select on (s,
-//        then index) among the tokens above T*; the nucleus cut a radix
-//        select by mass on s (the smallest value whose strictly-greater
-//        mass is within p of the kept mass); both are exact.  They are
-//        valid when the cut lies above T* (checked: at least k tokens above
-//        T*, or more than p of the mass above T*); otherwise the same
-//        selections run over the whole row, read again from memory, which
-//        is slow but exact.  The Gumbel argmax over the kept tokens reads
-//        their noise only.
+// hist   (up to kGroups 256-thread workgroups per filtered row, each over a
+//        contiguous group of chunks).  With T* the largest value left out
+//        by any chunk, the lists hold every token of the row with s > T*.
+//        Each group bins its listed tokens above T* below the row max M
+//        (1024 bins of width 1/32, the last one taking the rest): counts,
+//        exact masses exp(s - M) (fp64, then 2^-38 fixed point: sums are
+//        order independent and bit-reproducible) for nucleus rows, and the
+//        best Gumbel key per bin (the noise of these tokens is read here);
+//        prefix scans over the bins give each bin's offset and the best key
+//        of the bins before it, and the tokens are written in bin order
+//        with their noise.  The group's listed masses plus its chunks'
+//        left-out masses give its share of Z.  Nothing is shared between
+//        workgroups: each writes its own bins and totals.
+// finish (one 1024-thread workgroup per row).  The groups' bins added up
+//        give the bin holding the cut: the k-th largest (top-k) or the
+//        deepest bin whose strictly-greater mass is within p of Z
+//        (nucleus).  Every token in the bins before it is kept, and the
+//        groups' prefix best keys give the best among them; only the cut
+//        bin's tokens are read (from the groups' bin-sorted arrays) and the
+//        exact cut among them is found in LDS.  This is valid when the cut
+//        lies above T* (checked: at least k tokens above T*, or more than p
+//        of the mass above T*).  Otherwise, and for top-k followed by a
+//        nucleus, p <= 0 or a crowded cut bin, general selections (bins,
+//        then radix selects by rank or by mass) run over the lists, or over
+//        the whole row read again from memory when the cut may lie below
+//        T* (slow but exact).
 //
-// Workgroups communicate only through the kernel boundary: no workgroup
-// waits for or fences against another one, and no workspace memory needs
-// clearing (every per-chunk record and list is fully written by its scan
-// workgroup; the finish workgroup builds its row's buffers itself).
+// Workgroups communicate only through kernel boundaries: no workgroup waits
+// for or fences against another one, and no workspace memory needs clearing
+// (every record, list, bin range and sorted array that a later launch reads
+// is fully written earlier in the same call).
 #include <math.h>
 
 #include <type_traits>
