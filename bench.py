@@ -291,20 +291,20 @@ def main():
         del lcopies
         log(f"[bench] sampler graph replay: {graph_samp_us:.2f} us per draw "
             f"({samp_copies} logits copies)")
-    # The reduce's floor: one launch, with the reduce's grid (one wave per row
-    # and query head, four per workgroup), that only streams the workspace
-    # holding the split partials (all splits; the reduce reads a row's used
-    # ones), as a graph of L launches like the reduce's.
+    # The reduce's floor: one launch that only streams the workspace holding
+    # the split partials (all splits; the reduce reads a row's used ones),
+    # timed as a graph of at least 64 such launches (fewer would time the
+    # host's replay calls, not the device).
     reduce_floor = None
     if not args.no_graph and not cascade:
         pbytes = (ws.numel() // 16) * 16
         sink = torch.zeros(64, dtype=torch.int32, device=dev)
         fl_us = 1e3 * graph_time_ms(
-            lambda c: pkv.probe_stream_read(ws[:pbytes], sink, workgroups=(B * Hq + 3) // 4),
-            ncalls=L)
+            lambda c: pkv.probe_stream_read(ws[:pbytes], sink), ncalls=max(L, 64))
         reduce_floor = {"us": round(fl_us, 3), "bytes": pbytes,
-                        "what": "pkv_probe_stream_read over the partials workspace with the "
-                                "reduce's grid, graph replay"}
+                        "what": "pkv_probe_stream_read over the partials workspace (16 "
+                                "workgroups per CU), graph replay: a launch that only reads "
+                                "what the reduce reads"}
         log(f"[bench] reduce floor: {fl_us:.2f} us per launch")
     warm_attn_us = None
     if R > 1 and not args.no_graph:

@@ -317,7 +317,9 @@ int pkv_decode_attention_partial_store(const void *q, int64_t q_stride,
  * only the order of the work differs: the shared prefix, positions
  * [0, num_prefix_blocks*block_size), is read once per KV head for all the
  * rows (through prefix_blocks), each row's own positions after it through
- * its block table, and the two are merged by log-sum-exp.
+ * its block table, and the two are merged by log-sum-exp.  Two launches:
+ * one grid on the matrix cores for both parts (16 (row, query head) pairs
+ * per prefix workgroup), then the split-KV reduce.
  *
  * prefix_blocks      int32 [num_prefix_blocks]: block ids of the shared
  *                    prefix, in position order.  Every row's first

@@ -727,19 +727,16 @@ int pkv_cascade_decode_attention(void *out, int64_t out_stride, const void *q, i
     REQUIRE(aligned(out, 16), PKV_ERR_INVALID_ARG, "out must be 16-byte aligned");
     REQUIRE(aligned(prefix_blocks, 4), PKV_ERR_INVALID_ARG, "prefix_blocks must be 4-byte aligned");
 
-    // prefix launch: shared blocks, one workgroup per (prefix split, KV head, query chunk)
-    pkv::PartialArgs pa = a;
-    pa.prefix_blocks = prefix_blocks;
-    pa.prefix_len = cg.prefix_len;
-    pa.split_tokens = cg.prefix_split;
-    pa.vq_per_kv = batch * (num_q_heads / num_kv_heads);
-    pa.vchunks = cg.vchunks;
-    rc = hip_status(pkv::launch_decode_prefix_mfma(pa, head_dim, stream), "cascade prefix launch");
-    if (rc) return rc;
-    // tail launch: each row's positions after the prefix
+    // one launch: the shared blocks, one workgroup per (prefix split, KV
+    // head, query chunk), then each row's positions after the prefix
+    a.prefix_blocks = prefix_blocks;
+    a.prefix_len = cg.prefix_len;
+    a.prefix_split = cg.prefix_split;
+    a.vq_per_kv = batch * (num_q_heads / num_kv_heads);
+    a.vchunks = cg.vchunks;
     a.pos_base = cg.prefix_len;
     a.split_base = cg.prefix_splits;
-    rc = hip_status(pkv::launch_decode_partial(a, head_dim, stream), "cascade tail launch");
+    rc = hip_status(pkv::launch_decode_cascade_mfma(a, head_dim, stream), "cascade launch");
     if (rc) return rc;
     pkv::ReduceArgs r;
     r.out = static_cast<uint16_t *>(out);

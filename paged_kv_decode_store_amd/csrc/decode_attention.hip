@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
     // together with the row length, before it is known how many are in use
     // (slots past the row's count hold stale data inside the workspace and
     // are masked below): one memory round trip instead of three.
-    constexpr int kSpec = 8;
+    constexpr int kSpec = 24;
     const int S = a.num_splits;
     const int64_t base = ((int64_t)b * a.num_q_heads + h) * S;
     const float *ml = a.part_ml + 2 * base;

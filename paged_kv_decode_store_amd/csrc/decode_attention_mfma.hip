@@ -76,16 +76,18 @@ __device__ __forceinline__ uint32_t pair_of(uint32_t x, uint32_t y)
     return __builtin_amdgcn_perm(y, x, H ? 0x07060302u : 0x05040100u);
 }
 
-// Launch modes of the kernel: the decode partial step and the cascade's
-// prefix step.
-enum : int { kDecode = 0, kPrefix = 1 };
+// Launch modes of the kernel: the decode partial step, and the cascade's
+// prefix and tail steps in one grid (prefix workgroups first).
+enum : int { kDecode = 0, kCascade = 1 };
 
 template <int D, bool FUSED, int MODE>
 __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const PartialArgs a)
 {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(!FUSED || MODE == kDecode, "only the decode step stores");
-    constexpr bool PREFIX = MODE == kPrefix;
+    // this workgroup runs the cascade's prefix step (always false, at compile
+    // time, in the decode step)
+    const bool PREFIX = MODE == kCascade && (int)blockIdx.x < a.prefix_wgs;
     constexpr int KD = D / 4;       // K dims per lane (one position)
     constexpr int KW = KD / 2;      // their packed words
     constexpr int KP = KD / 8;      // their 16-byte pieces: piece w is dims 8*(4*w + kb) + [0, 8)
@@ -98,9 +100,9 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
     const int ln = lane & 15;       // query (S^T column) / position (K row) / dim block
     const int kb = lane >> 4;
 
-    int x = blockIdx.x;
+    int x = (MODE == kCascade && !PREFIX) ? (int)blockIdx.x - a.prefix_wgs : (int)blockIdx.x;
     int hc, kvh, b, s;
-    if constexpr (PREFIX) {
+    if (PREFIX) {
         hc = x % a.vchunks;
         x /= a.vchunks;
         kvh = x % a.num_kv_heads;
@@ -119,9 +121,9 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
     }
 
     int n, t_begin, t_end, pos_new = -1;
-    if constexpr (PREFIX) {
-        t_begin = s * a.split_tokens;
-        t_end = min(a.prefix_len, t_begin + a.split_tokens);
+    if (PREFIX) {
+        t_begin = s * a.prefix_split;
+        t_end = min(a.prefix_len, t_begin + a.prefix_split);
         n = t_end;
     } else {
         const int n_row = a.context_lens[b];
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
     const int qv = hc * kMQ + ln;
     const bool qreal = PREFIX ? qv < a.vq_per_kv : qv < a.group;
     int qrow, qhead, lim;
-    if constexpr (PREFIX) {
+    if (PREFIX) {
         qrow = qreal ? qv / a.group : 0;
         qhead = kvh * a.group + (qreal ? qv % a.group : 0);
         lim = qreal ? min(t_end, min(max(a.context_lens[qrow], 0), a.max_len)) : 0;
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(kMWaves * 64) void decode_partial_mfma_kernel(const
             continue;
         }
         int64_t pidx;
-        if constexpr (PREFIX) {
+        if (PREFIX) {
             const int rb = v / a.group, rh = kvh * a.group + v % a.group;
             pidx = ((int64_t)rb * a.num_q_heads + rh) * a.num_splits + s;
         } else {
@@ -355,11 +357,17 @@ template <int D, int MODE>
 hipError_t launch_mfma_d(const PartialArgs &a, hipStream_t stream)
 {
     PartialArgs m = a;
-    if constexpr (MODE == kPrefix) {
+    if constexpr (MODE == kCascade) {
         m.vchunks = (a.vq_per_kv + kMQ - 1) / kMQ;
-        const int64_t grid = (int64_t)((a.prefix_len + a.split_tokens - 1) / a.split_tokens) *
-                             a.num_kv_heads * m.vchunks;
-        decode_partial_mfma_kernel<D, false, kPrefix><<<(unsigned)grid, kMWaves * 64, 0, stream>>>(m);
+        m.head_chunks = (a.group + kMQ - 1) / kMQ;
+        m.out = nullptr;
+        const int64_t pre = (int64_t)((a.prefix_len + a.prefix_split - 1) / a.prefix_split) *
+                            a.num_kv_heads * m.vchunks;
+        const int64_t tail = (int64_t)(a.num_splits - a.split_base) * a.batch * a.num_kv_heads *
+                             m.head_chunks;
+        m.prefix_wgs = (int32_t)pre;
+        decode_partial_mfma_kernel<D, false, kCascade>
+            <<<(unsigned)(pre + tail), kMWaves * 64, 0, stream>>>(m);
     } else {
         m.head_chunks = (a.group + kMQ - 1) / kMQ;
         const int64_t grid = (int64_t)(a.num_splits - a.split_base) * a.batch * a.num_kv_heads *
@@ -405,11 +413,11 @@ hipError_t launch_decode_partial_mfma(const PartialArgs &a, int32_t head_dim, hi
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_prefix_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream)
+hipError_t launch_decode_cascade_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream)
 {
     if (a.batch == 0 || a.prefix_len <= 0) return hipSuccess;
-    if (head_dim == 128) return launch_mfma_d<128, kPrefix>(a, stream);
-    if (head_dim == 64) return launch_mfma_d<64, kPrefix>(a, stream);
+    if (head_dim == 128) return launch_mfma_d<128, kCascade>(a, stream);
+    if (head_dim == 64) return launch_mfma_d<64, kCascade>(a, stream);
     return hipErrorInvalidValue;
 }
 

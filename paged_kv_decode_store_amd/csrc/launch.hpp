@@ -68,12 +68,17 @@ struct PartialArgs {
     // where the virtual queries of a KV head are the (row, query head) pairs
     // that use it, vq_per_kv = batch * group; positions [0, prefix_len) are
     // read once through prefix_blocks.
+    // Cascade launch (both in one grid): the first prefix_wgs workgroups
+    // are the prefix step with prefix_split positions per split, the rest
+    // the tail step.
     int32_t pos_base;
     int32_t split_base;
     const int32_t *prefix_blocks;
     int32_t prefix_len;
     int32_t vq_per_kv;
     int32_t vchunks;        // virtual-query chunks per KV head
+    int32_t prefix_split;   // positions per prefix split
+    int32_t prefix_wgs;
     // varlen multi-query attention: sequence b's new tokens are rows
     // [cu_q[b], cu_q[b+1]) of q and out, its cache holds cu_k[b+1] - cu_k[b]
     // tokens (the new ones last); one workgroup per (chunk of 16 (token,
@@ -107,12 +112,15 @@ struct ReduceArgs {
 };
 
 hipError_t launch_decode_partial(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
+// Shared-prefix decode in one launch: the prefix step (prefix_blocks,
+// prefix_len, prefix_split, vq_per_kv set) and the tail step (pos_base,
+// split_base set) on the matrix cores, partials only.
+hipError_t launch_decode_cascade_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
 hipError_t launch_decode_reduce(const ReduceArgs &a, int32_t head_dim, hipStream_t stream);
 // Matrix-core partial step (up to 16 query heads per workgroup; head_chunks
-// is derived), and the prefix step of the cascade decode on the same kernel
-// (`a` describes the prefix launch; 16 virtual queries per workgroup).
+// is derived).  The cascade decode runs on the same kernel
+// (launch_decode_cascade_mfma; 16 virtual queries per prefix workgroup).
 hipError_t launch_decode_partial_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
-hipError_t launch_decode_prefix_mfma(const PartialArgs &a, int32_t head_dim, hipStream_t stream);
 // Varlen multi-query paged attention on the matrix-core kernel.
 hipError_t launch_varlen_attention(const PartialArgs &a, int32_t head_dim, int32_t max_seqlen_q,
                                    hipStream_t stream);
