@@ -542,8 +542,9 @@ def partial_kernel_name(cfg, D, fused, cascade):
 
 def stream_read_ceiling(dev, nbytes=1 << 31, launches=10):
     """Achieved rate of the library's streaming-read probe (16-byte
-    non-temporal loads, 16 workgroups per CU) over a fresh buffer far larger
-    than the caches, timed with HIP events on the current stream."""
+    non-temporal loads, 16 workgroups per CU, each over a contiguous share)
+    over a fresh buffer far larger than the caches, timed with HIP events on
+    the current stream."""
     import torch
 
     import paged_kv_decode_store_amd as pkv
@@ -562,8 +563,9 @@ def stream_read_ceiling(dev, nbytes=1 << 31, launches=10):
     del buf
     return {"GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes, "us_per_launch":
             round(us, 2), "launches": launches,
-            "how": "pkv_probe_stream_read: 16-byte non-temporal loads, grid-stride, "
-                   "16 workgroups of 256 threads per CU, HIP events"}
+            "how": "pkv_probe_stream_read: 16-byte non-temporal loads, each of 16 "
+                   "workgroups of 256 threads per CU over a contiguous share, 8 loads in "
+                   "flight per thread, HIP events"}
 
 
 def read_traffic(name, fused, mfma):

@@ -94,8 +94,8 @@ int pkv_set_wait_limit(uint32_t polls);
  *
  * Streaming-read probe: reads `bytes` of device memory at buf once, with the
  * 16-byte non-temporal vector loads the attention kernels stream K/V with,
- * grid-stride over `workgroups` workgroups of 256 threads (0: 16 per compute
- * unit).  sink: device uint32 [64], practically never written (it keeps the
+ * over `workgroups` workgroups of 256 threads (0: 16 per compute unit), each
+ * reading a contiguous share with eight loads in flight per thread.  sink: device uint32 [64], practically never written (it keeps the
  * loads from being optimised out).  Timing is the caller's (HIP events on
  * `stream`).  bytes: a multiple of 16; buf and sink 16- and 4-byte aligned. */
 int pkv_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t workgroups,

@@ -22,6 +22,8 @@
 // O = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, and writes bf16.
 #include <math.h>
 
+#include <type_traits>
+
 #include "launch.hpp"
 #include "pkv_device.hpp"
 
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(const Parti
     }
 }
 
-template <int D>
+template <int D, int SPEC>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
 {
     constexpr int DPL = D / 64;  // output dims per lane
@@ -285,8 +287,10 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
     // The first kSpec slots' partials and every lane's (m, l) are requested
     // together with the row length, before it is known how many are in use
     // (slots past the row's count hold stale data inside the workspace and
-    // are masked below): one memory round trip instead of three.
-    constexpr int kSpec = 24;
+    // are masked below): one memory round trip instead of three.  kSpec is
+    // chosen by the launcher to cover the workspace's slots (8, 24 or 48):
+    // more unrolled slots than there are cost time.
+    constexpr int kSpec = SPEC;
     const int S = a.num_splits;
     const int64_t base = ((int64_t)b * a.num_q_heads + h) * S;
     const float *ml = a.part_ml + 2 * base;
@@ -329,18 +333,18 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const ReduceArgs a)
             for (int j = 0; j < DPL; ++j) acc[j] += w * v[k][j];
         }
     }
-    // the remaining splits, four per step so that their loads are in flight together
+    // the remaining splits, eight per step so that their loads are in flight together
     int s = kSpec;
-    for (; s + 4 <= ns; s += 4) {
-        float w[4], u[4][DPL];
+    for (; s + 8 <= ns; s += 8) {
+        float w[8], u[8][DPL];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 8; ++k) {
             w[k] = __builtin_amdgcn_exp2f(ml[2 * (s + k)] - M);
 #pragma unroll
             for (int j = 0; j < DPL; ++j) u[k][j] = po[(int64_t)(s + k) * D + j];
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < 8; ++k)
 #pragma unroll
             for (int j = 0; j < DPL; ++j) acc[j] += w[k] * u[k][j];
     }
@@ -447,10 +451,19 @@ hipError_t launch_decode_reduce(const ReduceArgs &a, int32_t head_dim, hipStream
     if (a.batch == 0) return hipSuccess;
     const int64_t waves = (int64_t)a.batch * a.num_q_heads;
     const unsigned grid = (unsigned)((waves + 3) / 4);
+    auto go = [&](auto d) {
+        constexpr int D = decltype(d)::value;
+        if (a.num_splits <= 8)
+            decode_reduce_kernel<D, 8><<<grid, 256, 0, stream>>>(a);
+        else if (a.num_splits <= 24)
+            decode_reduce_kernel<D, 24><<<grid, 256, 0, stream>>>(a);
+        else
+            decode_reduce_kernel<D, 48><<<grid, 256, 0, stream>>>(a);
+    };
     if (head_dim == 128)
-        decode_reduce_kernel<128><<<grid, 256, 0, stream>>>(a);
+        go(std::integral_constant<int, 128>{});
     else if (head_dim == 64)
-        decode_reduce_kernel<64><<<grid, 256, 0, stream>>>(a);
+        go(std::integral_constant<int, 64>{});
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
