@@ -103,7 +103,8 @@ struct alignas(32) RowTot {
     unsigned long long Z;    // mass of its tokens (2^-38 units of the row max's)
     unsigned long long mu;   // mass of its listed tokens above T*
     uint32_t nu;             // its listed tokens above T*
-    uint32_t pad[3];
+    uint32_t kmax, tout;     // the row max's key and T*'s (the same in every group)
+    uint32_t pad;
 };
 static_assert(sizeof(RowTot) == 32, "row totals");
 
@@ -987,6 +988,8 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
             r.mu += s_sum[1][w];
             r.nu += (uint32_t)s_sum[2][w];
         }
+        r.kmax = kmax;
+        r.tout = tout;
         a.tot[part] = r;
     }
 }
@@ -1537,30 +1540,25 @@ __global__ __launch_bounds__(kFThreads) void samp_finish_kernel(const SampArgs a
 
     // ---- one round of loads: the groups' records of this thread's bin
     // (requested blind: bins past the last one written hold stale data,
-    // dropped once T* is known), the groups' totals, the chunk records.
+    // dropped once T* is known) and the groups' totals, which also carry the
+    // row max and T*.  Rows without a histogram take those from the chunk
+    // records.
     static_assert(kHBins == kFThreads, "one finish bin per thread");
     BinRec grp[kGroups];
+    uint32_t kmax, tout;
+    RowTot tot = {};
     if (use_hist) {
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)   // (a missing group reads group 0, dropped below)
             grp[g] = a.bins[((int64_t)b * a.groups + (g < a.groups ? g : 0)) * kHBins + threadIdx.x];
+        const RowTot t0 = a.tot[(int64_t)b * a.groups];
         if (threadIdx.x < (unsigned)a.groups) sh.gtot[threadIdx.x] = a.tot[(int64_t)b * a.groups + threadIdx.x];
-    }
-    uint32_t km = 0, to = 0;
-    for (int c = threadIdx.x; c < nch; c += kFThreads) {
-        const ChunkRec r = rec[c];
-        km = max(km, r.mkey);
-        to = max(to, r.outkey);
-        sh.nlist[c] = r.n;
-    }
-    if (threadIdx.x < 64) sh.tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
-    uint32_t kmax, tout;
-    block_max2<kFThreads>(km, to, sh.red, kmax, tout);   // (its barrier orders the LDS fills)
-    const float Mf = key_float(kmax);
-    const double M = (double)Mf;
-    RowTot tot = {};
-    if (use_hist) {   // the groups' bins and totals added up
-        const bool in = (int)threadIdx.x < bins_above(tout, Mf);
+        if (threadIdx.x < 64) sh.tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+        kmax = t0.kmax;
+        tout = t0.tout;
+        __syncthreads();
+        // the groups' bins and totals added up
+        const bool in = (int)threadIdx.x < bins_above(tout, key_float(kmax));
         uint32_t cnt = 0;
         unsigned long long mass = 0;
 #pragma unroll
@@ -1582,7 +1580,19 @@ __global__ __launch_bounds__(kFThreads) void samp_finish_kernel(const SampArgs a
             tot.nu += sh.gtot[g].nu;
         }
         __syncthreads();
+    } else {
+        uint32_t km = 0, to = 0;
+        for (int c = threadIdx.x; c < nch; c += kFThreads) {
+            const ChunkRec r = rec[c];
+            km = max(km, r.mkey);
+            to = max(to, r.outkey);
+            sh.nlist[c] = r.n;
+        }
+        if (threadIdx.x < 64) sh.tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+        block_max2<kFThreads>(km, to, sh.red, kmax, tout);   // (its barrier orders the LDS fills)
     }
+    const float Mf = key_float(kmax);
+    const double M = (double)Mf;
     // The lists hold every token above T*; the cut must lie above T*.
     bool ok;
     if (mode & MODE_TOPK) ok = tot.nu >= (uint32_t)a.top_k[b];
@@ -1590,6 +1600,10 @@ __global__ __launch_bounds__(kFThreads) void samp_finish_kernel(const SampArgs a
     else ok = tout < kmax;   // p <= 0: every maximum must be above T*
     if (ok && single && one_pass_draw(a, sh, grp, b, mode, kmax, tot.Z)) return;
     if (ok) {
+        if (use_hist) {   // the lists' sizes (rows without a histogram have them)
+            for (int c = threadIdx.x; c < nch; c += kFThreads) sh.nlist[c] = rec[c].n;
+            __syncthreads();
+        }
         ListSource src;
         src.lrow = a.list + (int64_t)b * nch * a.cap;
         src.nlist = sh.nlist;
