@@ -67,7 +67,8 @@ constexpr int kDigits = 4096;           // radix digits per level (<= 12 bits)
 constexpr int kHBins = 1024;            // finish-side value bins (the last one takes the rest)
 constexpr int kGroups = 8;              // histogram workgroups per row (at most)
 constexpr int kGroupChunks = kMaxChunks / kGroups;   // chunks of one group (at most)
-constexpr int kHBatch = 16;             // list slots per thread whose loads are issued together
+constexpr int kHThreads = 512;          // histogram kernel
+constexpr int kHBatch = 8;              // list slots per thread whose loads are issued together
 constexpr double kMassUnit = 0x1p38;    // fixed-point masses: 2^-38 of the row max's
 
 enum : uint32_t {
@@ -692,12 +693,17 @@ __device__ __forceinline__ void scan_chunk(const SampArgs &a, Tile<VEC4> &t, int
     float omax = -__builtin_huge_valf();
     float zx = 0.f;
     bool any_nan_out = false;
+    // bin_of(s, Mc) < jc reads (Mc - s) * kBinsPerUnit < jc for jc < kBins
+    // (the truncated bin index of a non-negative d is below an integer jc
+    // exactly when d is; NaN lands in the last bin either way)
+    const bool all_listed = jc >= kBins;
+    const float jcf = (float)jc;
     auto classify = [&](auto with_mass) {
         const double Md = (double)Mc;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const float s = t.v[j];
-            const bool lj = in(j) && bin_of(s, Mc) < jc;
+            const bool lj = in(j) && (all_listed || (Mc - s) * kBinsPerUnit < jcf);
             const bool oj = in(j) && !lj;
             listed |= (lj ? 1u : 0u) << j;
             const float so = oj ? s : -__builtin_huge_valf();
@@ -794,18 +800,18 @@ __device__ __forceinline__ int bins_above(uint32_t tout, float M)
 // The first kHBatch list slots of each thread are requested together with
 // the row's records, before anything is known of them (slots past a
 // chunk's count hold stale data and are dropped once the counts arrive).
-__global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
+__global__ __launch_bounds__(kHThreads) void samp_hist_kernel(const SampArgs a)
 {
     const int b = blockIdx.y;
     const int g = blockIdx.x;
     const uint32_t mode = row_mode(a, b);
     if (!(mode & (MODE_TOPK | MODE_TOPP))) return;   // greedy, plain, maxima: not needed
-    __shared__ unsigned long long s_red[kThreads / 64];
+    __shared__ unsigned long long s_red[kHThreads / 64];
     __shared__ double s_tab[64];
     __shared__ uint32_t s_cnt[kHBins];
     __shared__ unsigned long long s_mass[kHBins];
     __shared__ unsigned long long s_best[kHBins];
-    __shared__ unsigned long long s_sum[3][kThreads / 64];
+    __shared__ unsigned long long s_sum[3][kHThreads / 64];
     __shared__ uint32_t s_n[kGroupChunks], s_mk[kGroupChunks];
     __shared__ double s_zx[kGroupChunks];
     const int c0 = (int)((int64_t)g * a.nchunks / a.groups);
@@ -817,12 +823,12 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
     unsigned long long v[kHBatch];
 #pragma unroll
     for (int j = 0; j < kHBatch; ++j) {
-        const int f = (int)threadIdx.x + j * kThreads;
+        const int f = (int)threadIdx.x + j * kHThreads;
         v[j] = lgrp[f < nslots ? f : 0];
     }
     const ChunkRec *rec = a.rec + (int64_t)b * a.nchunks;
     uint32_t km = 0, to = 0;
-    for (int c = threadIdx.x; c < a.nchunks; c += kThreads) {
+    for (int c = threadIdx.x; c < a.nchunks; c += kHThreads) {
         const ChunkRec r = rec[c];
         km = max(km, r.mkey);
         to = max(to, r.outkey);
@@ -833,13 +839,13 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
         }
     }
     if (threadIdx.x < 64) s_tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
-    for (int d = threadIdx.x; d < kHBins; d += kThreads) {
+    for (int d = threadIdx.x; d < kHBins; d += kHThreads) {
         s_cnt[d] = 0;
         s_mass[d] = 0;
         s_best[d] = 0;
     }
     uint32_t kmax, tout;
-    block_max2<kThreads>(km, to, s_red, kmax, tout);   // (its barrier orders the fills)
+    block_max2<kHThreads>(km, to, s_red, kmax, tout);   // (its barrier orders the fills)
     const float Mf = key_float(kmax);
     const double M = (double)Mf;
     const bool nucleus = (mode & MODE_TOPP) && !(mode & MODE_TOPK);
@@ -851,20 +857,23 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
     auto live = [&](int f, unsigned long long p) { return listed(f) && (uint32_t)(p >> 32) > tout; };
     unsigned long long zl = 0, mu = 0, nu = 0;
     float gv[kHBatch];
-    for (int f0 = threadIdx.x; f0 < nslots; f0 += kHBatch * kThreads) {
+    for (int f0 = threadIdx.x; f0 < nslots; f0 += kHBatch * kHThreads) {
         if (f0 != (int)threadIdx.x) {   // later batches
 #pragma unroll
             for (int j = 0; j < kHBatch; ++j) {
-                const int f = f0 + j * kThreads;
+                const int f = f0 + j * kHThreads;
                 v[j] = lgrp[f < nslots ? f : 0];
             }
         }
 #pragma unroll
-        for (int j = 0; j < kHBatch; ++j)
-            gv[j] = gn[live(f0 + j * kThreads, v[j]) ? unpack_index(v[j]) : 0u];
+        for (int j = 0; j < kHBatch; ++j) {   // (lanes with nothing to read issue no load)
+            float gj = 0.f;
+            if (live(f0 + j * kHThreads, v[j])) gj = gn[unpack_index(v[j])];
+            gv[j] = gj;
+        }
 #pragma unroll
         for (int j = 0; j < kHBatch; ++j) {
-            const int f = f0 + j * kThreads;
+            const int f = f0 + j * kHThreads;
             if (!listed(f)) continue;
             const float s = value_of(v[j]);
             const unsigned long long m = nucleus ? mass_fixed(s, M, s_tab) : 0ull;
@@ -881,7 +890,7 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
         }
     }
     if (nucleus)   // the chunks' left-out masses, brought from M_c to M
-        for (int c = threadIdx.x; c < c1 - c0; c += kThreads)
+        for (int c = threadIdx.x; c < c1 - c0; c += kHThreads)
             if (s_zx[c] > 0.0)
                 zl += (unsigned long long)(s_zx[c] * exp_below((double)key_float(s_mk[c]) - M, s_tab) *
                                            kMassUnit + 0.5);
@@ -898,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
 
     // Exclusive prefix count and prefix max over the bins: thread t owns
     // bins [kPB t, kPB t + kPB).
-    constexpr int kPB = kHBins / kThreads;
+    constexpr int kPB = kHBins / kHThreads;
     const int d0 = kPB * (int)threadIdx.x;
     uint32_t cnt[kPB];
     unsigned long long bst[kPB];
@@ -922,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
             imax = max(imax, um);
         }
     }
-    __shared__ unsigned long long s_wmax[kThreads / 64];
+    __shared__ unsigned long long s_wmax[kHThreads / 64];
     if (lane == 63) {   // (s_red is free: its last use was behind a barrier)
         s_red[wave] = isum;
         s_wmax[wave] = imax;
@@ -958,20 +967,23 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
     __syncthreads();
     // the tokens in bin order, with their noise
     SortedTok *out = a.sorted + part * a.gslots;
-    for (int f0 = threadIdx.x; f0 < nslots; f0 += kHBatch * kThreads) {
-        if (nslots > kHBatch * kThreads) {   // several batches: read again
+    for (int f0 = threadIdx.x; f0 < nslots; f0 += kHBatch * kHThreads) {
+        if (nslots > kHBatch * kHThreads) {   // several batches: read again
 #pragma unroll
             for (int j = 0; j < kHBatch; ++j) {
-                const int f = f0 + j * kThreads;
+                const int f = f0 + j * kHThreads;
                 v[j] = lgrp[f < nslots ? f : 0];
             }
 #pragma unroll
-            for (int j = 0; j < kHBatch; ++j)
-                gv[j] = gn[live(f0 + j * kThreads, v[j]) ? unpack_index(v[j]) : 0u];
+            for (int j = 0; j < kHBatch; ++j) {
+                float gj = 0.f;
+                if (live(f0 + j * kHThreads, v[j])) gj = gn[unpack_index(v[j])];
+                gv[j] = gj;
+            }
         }
 #pragma unroll
         for (int j = 0; j < kHBatch; ++j) {
-            if (!live(f0 + j * kThreads, v[j])) continue;
+            if (!live(f0 + j * kHThreads, v[j])) continue;
             const uint32_t pos = atomicAdd(&s_cnt[hbin_of(value_of(v[j]), Mf)], 1u);
             SortedTok st;
             st.packed = v[j];
@@ -983,7 +995,7 @@ __global__ __launch_bounds__(kThreads) void samp_hist_kernel(const SampArgs a)
     if (threadIdx.x == 0) {
         RowTot r = {};
 #pragma unroll
-        for (int w = 0; w < kThreads / 64; ++w) {
+        for (int w = 0; w < kHThreads / 64; ++w) {
             r.Z += s_sum[0][w];
             r.mu += s_sum[1][w];
             r.nu += (uint32_t)s_sum[2][w];
@@ -1793,7 +1805,7 @@ void launch_passes(const SampArgs &a, const dim3 grid, hipStream_t stream)
     case 8: samp_scan_kernel<VEC4, MASK, 8><<<grid, kThreads, 0, stream>>>(a); break;
     default: samp_scan_kernel<VEC4, MASK, 4><<<grid, kThreads, 0, stream>>>(a); break;
     }
-    samp_hist_kernel<<<dim3(a.groups, a.batch), kThreads, 0, stream>>>(a);
+    samp_hist_kernel<<<dim3(a.groups, a.batch), kHThreads, 0, stream>>>(a);
     samp_finish_kernel<<<a.batch, kFThreads, 0, stream>>>(a);
     if (a.out_prob || a.out_top_ids || a.out_top_probs)
         samp_extras_kernel<<<a.batch, kRThreads, 0, stream>>>(a);
