@@ -57,8 +57,9 @@ namespace {
 constexpr int kThreads = 256;           // scan kernel
 constexpr int kFThreads = 1024;         // finish kernel: one workgroup per row
 constexpr int kRThreads = 512;          // extra outputs: one workgroup per row
-constexpr int kBins = 2048;             // value bins below the chunk max
-constexpr float kBinsPerUnit = 32.f;    // bin width: 1/32 of a logit unit
+constexpr int kBins = 512;              // scan: value bins below the chunk max ...
+constexpr float kBinsPerUnit = 8.f;     // ... 1/8 of a logit unit wide
+constexpr float kHBinsPerUnit = 32.f;   // finish-side bins: 1/32 of a unit
 constexpr int kMaxPer = 16;             // logits per thread per chunk (more: register spills)
 constexpr int kMinGroups = 256;         // scan workgroups wanted (one per CU)
 constexpr int kListDiv = 8;             // list capacity per chunk: chunk / kListDiv
@@ -233,7 +234,7 @@ __device__ __forceinline__ int bin_of(float s, float M)
 // in the last one.
 __device__ __forceinline__ int hbin_of(float s, float M)
 {
-    const float d = (M - s) * kBinsPerUnit;
+    const float d = (M - s) * kHBinsPerUnit;
     return d < (float)(kHBins - 1) ? (int)d : kHBins - 1;
 }
 
@@ -345,7 +346,7 @@ __device__ __forceinline__ T wave_max_t(T v)
 }
 
 template <typename T, int NT>
-__device__ T block_sum(T v, T *scratch)
+__device__ __forceinline__ T block_sum(T v, T *scratch)
 {
     v = wave_sum_t(v);
     __syncthreads();
@@ -359,7 +360,7 @@ __device__ T block_sum(T v, T *scratch)
 }
 
 template <typename T, int NT>
-__device__ T block_max(T v, T *scratch)
+__device__ __forceinline__ T block_max(T v, T *scratch)
 {
     v = wave_max_t(v);
     __syncthreads();
@@ -395,22 +396,64 @@ __device__ __forceinline__ void block_max2(uint32_t x, uint32_t y, unsigned long
     __syncthreads();
 }
 
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_shift_t(T v)   // lanes with no source read 0
+{
+    if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+    } else {
+        const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+        const unsigned long long lo =
+            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+        const unsigned long long hi =
+            (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+        return __builtin_bit_cast(T, (hi << 32) | lo);
+    }
+}
+
+// Inclusive sum over the lanes of a wave in ascending order: row shifts by
+// 1, 2, 4 and 8 within each row of 16 lanes, then the rows' totals read as
+// scalars.  Every lane of the wave must be active.
+template <typename T>
+__device__ __forceinline__ T wave_scan_incl(T v)
+{
+    v += dpp_shift_t<0x111>(v);   // row_shr:1
+    v += dpp_shift_t<0x112>(v);   // row_shr:2
+    v += dpp_shift_t<0x114>(v);   // row_shr:4
+    v += dpp_shift_t<0x118>(v);   // row_shr:8
+    const T r0 = readlane_t(v, 15), r1 = readlane_t(v, 31), r2 = readlane_t(v, 47);
+    const int lane = threadIdx.x & 63;
+    T add = 0;
+    if (lane >= 16) add += r0;
+    if (lane >= 32) add += r1;
+    if (lane >= 48) add += r2;
+    return v + add;
+}
+
 template <typename T, int NT, bool REV = false>
-__device__ T block_scan_inclusive(T v, T *scratch)
+__device__ __forceinline__ T block_scan_inclusive(T v, T *scratch)
 {
     const int tid = REV ? NT - 1 - (int)threadIdx.x : (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     // lanes of a wave in scan order: REV reverses the lane order too
+    if constexpr (REV) {
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const T u = REV ? __shfl_down(v, (unsigned)off) : __shfl_up(v, (unsigned)off);
-        if (lane >= off) v += u;
+        for (int off = 1; off < 64; off <<= 1) {
+            const T u = __shfl_down(v, (unsigned)off);
+            if (lane >= off) v += u;
+        }
+    } else {
+        v = wave_scan_incl(v);
     }
     __syncthreads();
     if (lane == 63) scratch[wave] = v;
     __syncthreads();
     T base = 0;
-    for (int w = 0; w < wave; ++w) base += scratch[w];
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {   // (all reads issued together)
+        const T s = scratch[w];
+        base += w < wave ? s : T(0);
+    }
     __syncthreads();
     return v + base;
 }
@@ -1009,24 +1052,34 @@ __global__ __launch_bounds__(kHThreads) void samp_hist_kernel(const SampArgs a)
 // ---- finish ----------------------------------------------------------------
 
 constexpr int kCand = 1024;   // tokens of a threshold bin resolved in LDS
+constexpr int kSmallCand = 128;   // up to this many, compared one by one directly
+constexpr int kSubBins = 256;     // above: sub-ranges of their values ...
+constexpr int kSubCand = 256;     // ... and candidates of one sub-range compared directly
 // the counting cut gives each candidate q >= 1 lanes: at most one per thread
 static_assert(kCand <= kFThreads, "cand_rank / cand_cut need a lane per candidate");
 constexpr int kBatch = 8;     // list entries per thread whose loads are issued together
 
+constexpr int kCutBins = 2048;   // the radix cut's widest level: 11 bits
+static_assert(kHBins <= kCutBins, "finish bins fit the radix arrays");
+
 struct FinishShared {
     double tab[64];                       // 2^(j/64)
     uint32_t nlist[kMaxChunks];           // list sizes of the chunks
-    uint32_t bcnt[kBins];                 // value bins below the row max (the first
-    unsigned long long bmass[kBins];      // kHBins): counts and masses (2^-38 units)
+    uint32_t bcnt[kCutBins];              // value bins below the row max (kHBins) or
+    unsigned long long bmass[kCutBins];   // one radix level: counts, masses (2^-38 units)
     unsigned long long ckey[kCand];       // one bin's tokens: packed keys ...
     unsigned long long cmass[kCand];      // ... masses
     float cgum[kCand];                    // ... and noise (one-pass draw)
     RowTot gtot[kGroups];                 // the histogram groups' totals
-    uint32_t goff[kGroups], gcnt[kGroups], gstart[kGroups + 1];   // the cut bin, per group
+    uint32_t goff[kGroups], gstart[kGroups + 1];   // the cut bin, per group
+    uint32_t scnt[kSubBins];              // candidate sub-ranges: counts, masses,
+    unsigned long long smass[kSubBins];
+    unsigned long long skey[kSubCand], smas[kSubCand];   // ... the chosen one's tokens
     uint32_t hcnt[kDigits];               // radix digits (slow path)
     unsigned long long red[kFThreads / 64];
-    uint32_t nc, sel;
+    uint32_t nc, sel, ssel, snc;
     unsigned long long up, pick;
+    unsigned long long sup;               // sub-range search: what lies above it
 };
 
 // The row's listed tokens above T*, streamed from memory.  Thread t takes
@@ -1197,24 +1250,26 @@ __device__ __forceinline__ uint32_t compact_bin(const Src &src, FinishShared &sh
     return n;
 }
 
-// Exact cut among n <= kCand candidates in LDS by counting: q consecutive
-// lanes (q a power of two) share one candidate and split the comparisons.
-// Top-k: the packed key of rank `rank` (1 = largest, by value then index).
-__device__ __forceinline__ unsigned long long cand_rank(FinishShared &sh, uint32_t n, uint32_t rank)
+// Exact cut among n <= kCand candidates (keys, masses in LDS) by counting:
+// q consecutive lanes (q a power of two) share one candidate and split the
+// comparisons.  Top-k: the packed key of rank `rank` (1 = largest, by value
+// then index).
+__device__ __forceinline__ unsigned long long count_rank(FinishShared &sh, const unsigned long long *keys,
+                                                         uint32_t n, uint32_t rank)
 {
     uint32_t np = 1;
     while (np < n) np <<= 1;
     const uint32_t q = min(64u, (uint32_t)kFThreads / np);
     const uint32_t e = threadIdx.x / q, part = threadIdx.x % q;
     const bool real = e < n;
-    const unsigned long long ke = real ? sh.ckey[e] : 0ull;
+    const unsigned long long ke = real ? keys[e] : 0ull;
     uint32_t larger = 0;
     uint32_t j = part;
     for (; j + 7 * q < n; j += 8 * q) {   // eight LDS reads in flight
 #pragma unroll
-        for (int u = 0; u < 8; ++u) larger += sh.ckey[j + u * q] > ke ? 1u : 0u;
+        for (int u = 0; u < 8; ++u) larger += keys[j + u * q] > ke ? 1u : 0u;
     }
-    for (; j < n; j += q) larger += sh.ckey[j] > ke ? 1u : 0u;
+    for (; j < n; j += q) larger += keys[j] > ke ? 1u : 0u;
     for (uint32_t m = 1; m < q; m <<= 1) larger += __shfl_xor(larger, (int)m);
     if (real && part == 0 && larger + 1 == rank) sh.pick = ke;
     __syncthreads();
@@ -1224,29 +1279,175 @@ __device__ __forceinline__ unsigned long long cand_rank(FinishShared &sh, uint32
 }
 
 // Nucleus: the smallest candidate value whose strictly-greater mass (A from
-// the bins above plus the candidates above) is <= limit.
-__device__ __forceinline__ uint32_t cand_cut(FinishShared &sh, uint32_t n, unsigned long long A, double limit)
+// what lies above plus the candidates above) is <= limit.
+__device__ __forceinline__ uint32_t count_cut(FinishShared &sh, const unsigned long long *keys,
+                                              const unsigned long long *mass, uint32_t n,
+                                              unsigned long long A, double limit)
 {
     uint32_t np = 1;
     while (np < n) np <<= 1;
     const uint32_t q = min(64u, (uint32_t)kFThreads / np);
     const uint32_t e = threadIdx.x / q, part = threadIdx.x % q;
     const bool real = e < n;
-    const uint32_t ke = real ? (uint32_t)(sh.ckey[e] >> 32) : 0u;
+    const uint32_t ke = real ? (uint32_t)(keys[e] >> 32) : 0u;
     unsigned long long above = 0;
     uint32_t j = part;
     for (; j + 7 * q < n; j += 8 * q) {   // eight LDS reads in flight
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-            above += (uint32_t)(sh.ckey[j + u * q] >> 32) > ke ? sh.cmass[j + u * q] : 0ull;
+            above += (uint32_t)(keys[j + u * q] >> 32) > ke ? mass[j + u * q] : 0ull;
     }
-    for (; j < n; j += q) above += (uint32_t)(sh.ckey[j] >> 32) > ke ? sh.cmass[j] : 0ull;
+    for (; j < n; j += q) above += (uint32_t)(keys[j] >> 32) > ke ? mass[j] : 0ull;
     for (uint32_t m = 1; m < q; m <<= 1) above += __shfl_xor(above, (int)m);
     const bool fits = real && (double)(A + above) <= limit;
     // the smallest qualifying key: a max over complemented keys
     const uint32_t t =
         (uint32_t)block_max<unsigned long long, kFThreads>(fits ? (unsigned long long)(~ke) : 0ull, sh.red);
     return ~t;
+}
+
+// More than kSmallCand candidates: their value keys' range is cut into
+// kSubBins sub-ranges; counts (and masses) per sub-range locate the one
+// holding the cut, and only its candidates are compared one by one (all of
+// them again if it holds more than kSubCand, e.g. many ties).  Sub-range of
+// a value key: monotone in the key, so tied values share one.
+__device__ __forceinline__ int sub_of(uint32_t k, uint32_t kmin, unsigned long long span)
+{
+    return (int)(((unsigned long long)(k - kmin) * kSubBins) / span);
+}
+
+// Fills sh.scnt (and sh.smass) over the candidates' sub-ranges; returns the
+// key range through kmin / span.
+__device__ __forceinline__ void sub_hist(FinishShared &sh, uint32_t n, bool with_mass, uint32_t &kmin,
+                                         unsigned long long &span)
+{
+    if (threadIdx.x < kSubBins) {
+        sh.scnt[threadIdx.x] = 0;
+        sh.smass[threadIdx.x] = 0;
+    }
+    if (threadIdx.x == 0) sh.snc = 0;
+    const bool real = threadIdx.x < n;
+    const uint32_t k = real ? (uint32_t)(sh.ckey[threadIdx.x] >> 32) : 0u;
+    uint32_t hi, nlo;
+    block_max2<kFThreads>(real ? k : 0u, real ? ~k : 0u, sh.red, hi, nlo);   // (orders the clears)
+    kmin = ~nlo;
+    span = (unsigned long long)(hi - kmin) + 1;
+    if (real) {
+        const int s = sub_of(k, kmin, span);
+        atomicAdd(&sh.scnt[s], 1u);
+        if (with_mass) atomicAdd(&sh.smass[s], sh.cmass[threadIdx.x]);
+    }
+    __syncthreads();
+}
+
+// Copies the candidates of sub-range ssel (at most kSubCand) into sh.skey /
+// sh.smas; returns their number.
+__device__ __forceinline__ uint32_t sub_compact(FinishShared &sh, uint32_t n, uint32_t kmin,
+                                                unsigned long long span)
+{
+    if (threadIdx.x < n) {
+        const uint32_t k = (uint32_t)(sh.ckey[threadIdx.x] >> 32);
+        if (sub_of(k, kmin, span) == (int)sh.ssel) {
+            const uint32_t slot = atomicAdd(&sh.snc, 1u);
+            if (slot < (uint32_t)kSubCand) {
+                sh.skey[slot] = sh.ckey[threadIdx.x];
+                sh.smas[slot] = sh.cmass[threadIdx.x];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t m = sh.snc;
+    __syncthreads();
+    return m;
+}
+
+// Top-k: the packed key of rank `rank` among the n candidates in LDS.
+__device__ __forceinline__ unsigned long long cand_rank(FinishShared &sh, uint32_t n, uint32_t rank)
+{
+    if (n <= (uint32_t)kSmallCand) return count_rank(sh, sh.ckey, n, rank);
+    uint32_t kmin;
+    unsigned long long span;
+    sub_hist(sh, n, false, kmin, span);
+    if (threadIdx.x < 64) {   // wave 0: sub-ranges from the top, lane l owning 4
+        const int lane = threadIdx.x;
+        uint32_t c4[4], own = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            c4[u] = sh.scnt[kSubBins - 1 - 4 * lane - u];
+            own += c4[u];
+        }
+        uint32_t incl = own;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t v = (uint32_t)__shfl_up((int)incl, (unsigned)o);
+            if (lane >= o) incl += v;
+        }
+        uint32_t before = incl - own;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (before < rank && rank <= before + c4[u]) {
+                sh.ssel = (uint32_t)(kSubBins - 1 - 4 * lane - u);
+                sh.sup = before;   // candidates in the sub-ranges above
+            }
+            before += c4[u];
+        }
+    }
+    __syncthreads();
+    const uint32_t r2 = rank - (uint32_t)sh.sup;
+    const uint32_t m = sub_compact(sh, n, kmin, span);
+    if (m > (uint32_t)kSubCand) return count_rank(sh, sh.ckey, n, rank);
+    return count_rank(sh, sh.skey, m, r2);
+}
+
+// Nucleus: the smallest candidate value whose strictly-greater mass (A from
+// the bins above plus the candidates above) is <= limit.
+__device__ __forceinline__ uint32_t cand_cut(FinishShared &sh, uint32_t n, unsigned long long A, double limit)
+{
+    if (n <= (uint32_t)kSmallCand) return count_cut(sh, sh.ckey, sh.cmass, n, A, limit);
+    uint32_t kmin;
+    unsigned long long span;
+    sub_hist(sh, n, true, kmin, span);
+    if (threadIdx.x < 64) {   // wave 0: sub-ranges from the top, lane l owning 4
+        const int lane = threadIdx.x;
+        uint32_t c4[4];
+        unsigned long long m4[4], own = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            c4[u] = sh.scnt[kSubBins - 1 - 4 * lane - u];
+            m4[u] = sh.smass[kSubBins - 1 - 4 * lane - u];
+            own += m4[u];
+        }
+        unsigned long long incl = own;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long v = __shfl_up(incl, (unsigned)o);
+            if (lane >= o) incl += v;
+        }
+        unsigned long long above = A + incl - own;
+        // the deepest non-empty sub-range whose strictly-greater mass fits
+        int deep = kSubBins;
+        unsigned long long deep_a = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (c4[u] && (double)above <= limit) {
+                deep = kSubBins - 1 - 4 * lane - u;
+                deep_a = above;
+            }
+            above += m4[u];
+        }
+        const int best = -wave_max_t(-deep);
+        if (deep == best && best < kSubBins) {
+            sh.ssel = (uint32_t)best;
+            sh.sup = deep_a;
+        }
+        if (lane == 0 && best == kSubBins) sh.ssel = 0xffffffffu;   // (none: cannot happen)
+    }
+    __syncthreads();
+    if (sh.ssel == 0xffffffffu) return count_cut(sh, sh.ckey, sh.cmass, n, A, limit);
+    const unsigned long long A2 = sh.sup;
+    const uint32_t m = sub_compact(sh, n, kmin, span);
+    if (m > (uint32_t)kSubCand) return count_cut(sh, sh.ckey, sh.cmass, n, A, limit);
+    return count_cut(sh, sh.skey, sh.smas, m, A2, limit);
 }
 
 // Slow path of a bin with more than kCand tokens: radix select over the
@@ -1450,37 +1651,81 @@ __device__ __forceinline__ void select_and_draw(const SampArgs &a, FinishShared 
     }
 }
 
-// Top-k alone or nucleus alone, from the groups' bins of the tokens above
-// T* (added up in sh.bcnt, sh.bmass; this thread's bin's group records in
-// grp): the cut bin jc follows from the bins; every token in the bins
-// before it is kept, and their best Gumbel key is the groups' prefix best at
-// jc; only bin jc's tokens are read (from the groups' bin-sorted arrays,
-// with their noise) and resolved in LDS.  Returns false, having written
-// nothing, when bin jc holds more than kCand tokens.
+// Fast path of a row with one filter (top-k or nucleus): wave 0 finds the
+// cut bin from the summed bins (16 per lane, a wave scan), the thread of
+// that bin publishes where the bin's tokens lie in each group, and wave 0
+// alone resolves the bin's tokens (at most kWaveCand) and draws, with no
+// block-wide barrier after the publication (a larger bin, up to kCand
+// tokens, is resolved by the whole workgroup).  False (the same in every
+// thread) when the bin is empty or holds more than kCand tokens; then
+// nothing has been written.
+constexpr int kWaveCand = 64;              // cut-bin tokens one wave resolves (one per lane)
+constexpr int kWBins = kHBins / 64;        // bins per lane of that wave
+static_assert(kHBins % 64 == 0 && kWaveCand <= kCand, "wave fast path shape");
+
 __device__ __forceinline__ bool one_pass_draw(const SampArgs &a, FinishShared &sh, const BinRec (&grp)[kGroups],
                                               int b, uint32_t mode, uint32_t kmax, unsigned long long Z)
 {
     const float M = key_float(kmax);
     const bool topk = (mode & MODE_TOPK) != 0;
-    if (threadIdx.x == 0) sh.gstart[kGroups] = 0u;   // (no cut bin found: nothing to resolve)
-    int jc;
-    uint32_t r = 0;
-    unsigned long long A = 0;
-    double limit = 0.0;
-    if (topk) {
-        bin_by_count(sh, (uint32_t)a.top_k[b], jc, r);
-    } else {
-        limit = (double)a.top_p[b] * (double)Z;
-        bin_by_mass(sh, limit, jc, A);
+    const uint32_t k = topk ? (uint32_t)a.top_k[b] : 0u;
+    const double limit = topk ? 0.0 : (double)a.top_p[b] * (double)Z;
+    if (threadIdx.x < 64) {
+        const int lane = (int)threadIdx.x;
+        const int d0 = lane * kWBins;
+        uint32_t c[kWBins];
+        unsigned long long m[kWBins];
+        uint32_t csum = 0;
+        unsigned long long msum = 0;
+#pragma unroll
+        for (int j = 0; j < kWBins; ++j) {
+            c[j] = sh.bcnt[d0 + j];
+            m[j] = topk ? 0ull : sh.bmass[d0 + j];
+            csum += c[j];
+            msum += m[j];
+        }
+        int found = -1;
+        unsigned long long aux = 0;   // top-k: tokens in the bins before; nucleus: their mass
+        if (topk) {
+            uint32_t above = wave_scan_incl(csum) - csum;
+#pragma unroll
+            for (int j = 0; j < kWBins; ++j) {   // the bin holding rank k (one at most)
+                if (above < k && k <= above + c[j]) {
+                    found = d0 + j;
+                    aux = above;
+                }
+                above += c[j];
+            }
+        } else {
+            unsigned long long above = wave_scan_incl(msum) - msum;
+#pragma unroll
+            for (int j = 0; j < kWBins; ++j) {   // the deepest non-empty bin that fits
+                if (c[j] && (double)above <= limit) {
+                    found = d0 + j;
+                    aux = above;
+                }
+                above += m[j];
+            }
+        }
+        const int jc = wave_max_t(found);
+        const unsigned long long own = __ballot(found == jc && jc >= 0);
+        if (own) aux = readlane_t(aux, __ffsll((long long)own) - 1);
+        if (lane == 0) {
+            sh.sel = (uint32_t)jc;
+            sh.pick = aux;
+            sh.gstart[kGroups] = 0u;   // (no cut bin: nothing to resolve)
+        }
     }
-    if ((int)threadIdx.x == jc) {
+    __syncthreads();
+    const int jc = (int)sh.sel;
+    const unsigned long long aux = sh.pick;
+    if ((int)threadIdx.x == jc) {   // the bin's tokens, group by group
         unsigned long long up = 0;
         uint32_t start = 0;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
             const bool in = g < a.groups;
             sh.goff[g] = in ? grp[g].off : 0u;
-            sh.gcnt[g] = in ? grp[g].cnt : 0u;
             sh.gstart[g] = start;
             start += in ? grp[g].cnt : 0u;
             up = in ? max(up, grp[g].above) : up;
@@ -1491,34 +1736,88 @@ __device__ __forceinline__ bool one_pass_draw(const SampArgs &a, FinishShared &s
     __syncthreads();
     const uint32_t n = sh.gstart[kGroups];
     if (n == 0u || n > (uint32_t)kCand) return false;   // (uniform)
-    // bin jc's tokens: thread t < n takes the t-th, group by group
-    if (threadIdx.x < n) {
+    if (n > (uint32_t)kWaveCand) {   // a larger bin: every thread takes a token
+        if (threadIdx.x < n) {
+            int g = 0;
+#pragma unroll
+            for (int h = 1; h < kGroups; ++h) g = threadIdx.x >= sh.gstart[h] ? h : g;
+            const SortedTok st = a.sorted[((int64_t)b * a.groups + g) * a.gslots + sh.goff[g] +
+                                          (threadIdx.x - sh.gstart[g])];
+            sh.ckey[threadIdx.x] = st.packed;
+            sh.cgum[threadIdx.x] = st.g;
+            sh.cmass[threadIdx.x] = topk ? 0ull : mass_fixed(value_of(st.packed), (double)M, sh.tab);
+        }
+        __syncthreads();
+        unsigned long long kpack = 0;
+        uint32_t tau = 0;
+        if (topk)
+            kpack = cand_rank(sh, n, k - (uint32_t)aux);
+        else
+            tau = cand_cut(sh, n, aux, limit);
+        unsigned long long best = threadIdx.x == 0 ? sh.up : 0ull;
+        if (threadIdx.x < n) {
+            const unsigned long long v = sh.ckey[threadIdx.x];
+            const bool keep = topk ? v >= kpack : (uint32_t)(v >> 32) >= tau;
+            if (keep)
+                best = max(best, pack_key_index(float_key(value_of(v) + sh.cgum[threadIdx.x]), unpack_index(v)));
+        }
+        best = block_max<unsigned long long, kFThreads>(best, sh.red);
+        if (threadIdx.x == 0) {
+            a.out_ids[b] = (int32_t)unpack_index(best);
+            RowCut cut;
+            cut.mode = mode;
+            cut.tau = tau;
+            cut.kpack = kpack;
+            a.cut[b] = cut;
+        }
+        return true;
+    }
+    if (threadIdx.x >= 64) return true;
+
+    // ---- wave 0 alone from here: lane e holds token e of the bin ----
+    const int lane = (int)threadIdx.x;
+    const bool real = (uint32_t)lane < n;
+    unsigned long long key = 0, mass = 0;
+    float gum = 0.f;
+    if (real) {
         int g = 0;
 #pragma unroll
-        for (int h = 1; h < kGroups; ++h) g = threadIdx.x >= sh.gstart[h] ? h : g;
-        const SortedTok st = a.sorted[((int64_t)b * a.groups + g) * a.gslots + sh.goff[g] +
-                                      (threadIdx.x - sh.gstart[g])];
-        sh.ckey[threadIdx.x] = st.packed;
-        sh.cgum[threadIdx.x] = st.g;
-        sh.cmass[threadIdx.x] = topk ? 0ull : mass_fixed(value_of(st.packed), (double)M, sh.tab);
+        for (int h = 1; h < kGroups; ++h) g = (uint32_t)lane >= sh.gstart[h] ? h : g;
+        const SortedTok st =
+            a.sorted[((int64_t)b * a.groups + g) * a.gslots + sh.goff[g] + ((uint32_t)lane - sh.gstart[g])];
+        key = st.packed;
+        gum = st.g;
+        mass = topk ? 0ull : mass_fixed(value_of(st.packed), (double)M, sh.tab);
     }
-    __syncthreads();
+    // Each token against every token of the bin, read across lanes: top-k
+    // counts the larger packed keys (rank inside the bin: k - aux), nucleus
+    // adds the masses of strictly larger values (A = aux from the bins
+    // before).
     unsigned long long kpack = 0;
     uint32_t tau = 0;
-    if (topk)
-        kpack = cand_rank(sh, n, r);
-    else
-        tau = cand_cut(sh, n, A, limit);
-    // the best of the bins before jc and of bin jc's kept tokens
-    unsigned long long best = threadIdx.x == 0 ? sh.up : 0ull;
-    if (threadIdx.x < n) {
-        const unsigned long long v = sh.ckey[threadIdx.x];
-        const bool keep = topk ? v >= kpack : (uint32_t)(v >> 32) >= tau;
-        if (keep) best = max(best, pack_key_index(float_key(value_of(v) + sh.cgum[threadIdx.x]),
-                                                  unpack_index(v)));
+    if (topk) {
+        uint32_t larger = 0;
+        for (uint32_t j = 0; j < n; ++j) larger += readlane_t(key, (int)j) > key ? 1u : 0u;
+        const uint32_t rank = k - (uint32_t)aux;
+        kpack = wave_max_t(real && larger + 1 == rank ? key : 0ull);   // (exactly one token has that rank)
+    } else {
+        const uint32_t vk = (uint32_t)(key >> 32);
+        unsigned long long above = 0;
+        for (uint32_t j = 0; j < n; ++j) {
+            const uint32_t vj = readlane_t(vk, (int)j);
+            const unsigned long long mj = readlane_t(mass, (int)j);
+            above += vj > vk ? mj : 0ull;
+        }
+        // the smallest qualifying value: a max over complemented keys
+        const bool fits = real && (double)(aux + above) <= limit;
+        tau = ~wave_max_t(fits ? ~vk : 0u);
     }
-    best = block_max<unsigned long long, kFThreads>(best, sh.red);
-    if (threadIdx.x == 0) {
+    // the best of the bins before jc and of bin jc's kept tokens
+    unsigned long long best = lane == 0 ? sh.up : 0ull;
+    if (real && (topk ? key >= kpack : (uint32_t)(key >> 32) >= tau))
+        best = max(best, pack_key_index(float_key(value_of(key) + gum), unpack_index(key)));
+    best = wave_max_t(best);
+    if (lane == 0) {
         a.out_ids[b] = (int32_t)unpack_index(best);
         RowCut cut;
         cut.mode = mode;
