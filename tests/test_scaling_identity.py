@@ -35,3 +35,25 @@ def test_double_reciprocal_product_equals_fp32_division():
             assert np.array_equal(div.view(np.uint32), prod.view(np.uint32)), float(T)
             checked += zz.size
     assert checked > 10_000_000
+
+
+def test_double_reciprocal_product_exhaustive_at_workload_temperature(tmp_path):
+    """Every non-NaN fp32 z (all 2^32 bit patterns) at T = 0.8, the
+    temperature of the Qwen3-shaped workload's draw: the identity holds for
+    the whole range, subnormal ties included (tests/scaling_exhaustive.c; run
+    it by hand with other temperatures as arguments).  ~10 s of host time."""
+    import os
+    import shutil
+    import subprocess
+
+    import pytest
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "scaling_exhaustive.c")
+    exe = str(tmp_path / "scaling_exhaustive")
+    subprocess.run([cc, "-O2", "-o", exe, src], check=True)
+    r = subprocess.run([exe, "0.8"], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 mismatches" in r.stdout
