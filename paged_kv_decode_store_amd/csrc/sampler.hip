@@ -1059,7 +1059,14 @@ constexpr int kSubCand = 256;     // ... and candidates of one sub-range compare
 static_assert(kCand <= kFThreads, "cand_rank / cand_cut need a lane per candidate");
 constexpr int kBatch = 8;     // list entries per thread whose loads are issued together
 
+constexpr int kWaveCandMax = 256;  // cut-bin tokens one wave resolves (four per lane)
 constexpr int kCutBins = 2048;   // the radix cut's widest level: 11 bits
+
+// A token of a cut bin resolved by one wave (top-k: a = packed key;
+// nucleus: a = value key, b = mass).
+struct alignas(16) CandRec {
+    unsigned long long a, b;
+};
 static_assert(kHBins <= kCutBins, "finish bins fit the radix arrays");
 
 struct FinishShared {
@@ -1070,6 +1077,9 @@ struct FinishShared {
     unsigned long long ckey[kCand];       // one bin's tokens: packed keys ...
     unsigned long long cmass[kCand];      // ... masses
     float cgum[kCand];                    // ... and noise (one-pass draw)
+    CandRec crec[kWaveCandMax];           // a cut bin resolved by one wave: its
+    uint32_t wcnt[64];                    // sub-ranges' counts and masses, and the
+    unsigned long long wmass[64];         // chosen sub-range's tokens (crec)
     RowTot gtot[kGroups];                 // the histogram groups' totals
     uint32_t goff[kGroups], gstart[kGroups + 1];   // the cut bin, per group
     uint32_t scnt[kSubBins];              // candidate sub-ranges: counts, masses,
@@ -1659,7 +1669,17 @@ __device__ __forceinline__ void select_and_draw(const SampArgs &a, FinishShared 
 // tokens, is resolved by the whole workgroup).  False (the same in every
 // thread) when the bin is empty or holds more than kCand tokens; then
 // nothing has been written.
-constexpr int kWaveCand = 64;              // cut-bin tokens one wave resolves (one per lane)
+// The calling wave's LDS writes are complete before its later reads (LDS
+// serves one wave's instructions in order): a wave-scope fence pair.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kWaveCand = kWaveCandMax;
+constexpr int kWPer = kWaveCand / 64;      // tokens per lane
 constexpr int kWBins = kHBins / 64;        // bins per lane of that wave
 static_assert(kHBins % 64 == 0 && kWaveCand <= kCand, "wave fast path shape");
 
@@ -1774,48 +1794,150 @@ __device__ __forceinline__ bool one_pass_draw(const SampArgs &a, FinishShared &s
     }
     if (threadIdx.x >= 64) return true;
 
-    // ---- wave 0 alone from here: lane e holds token e of the bin ----
+    // ---- wave 0 alone from here: lane l holds tokens l + 64 r of the bin ----
     const int lane = (int)threadIdx.x;
-    const bool real = (uint32_t)lane < n;
-    unsigned long long key = 0, mass = 0;
-    float gum = 0.f;
-    if (real) {
-        int g = 0;
+    unsigned long long key[kWPer], mass[kWPer];
+    float gum[kWPer];
+    uint32_t vlo = 0xffffffffu, vhi = 0u;
 #pragma unroll
-        for (int h = 1; h < kGroups; ++h) g = (uint32_t)lane >= sh.gstart[h] ? h : g;
-        const SortedTok st =
-            a.sorted[((int64_t)b * a.groups + g) * a.gslots + sh.goff[g] + ((uint32_t)lane - sh.gstart[g])];
-        key = st.packed;
-        gum = st.g;
-        mass = topk ? 0ull : mass_fixed(value_of(st.packed), (double)M, sh.tab);
+    for (int r = 0; r < kWPer; ++r) {
+        const uint32_t e = (uint32_t)(lane + 64 * r);
+        key[r] = 0;
+        mass[r] = 0;
+        gum[r] = 0.f;
+        if (e < n) {
+            int g = 0;
+#pragma unroll
+            for (int h = 1; h < kGroups; ++h) g = e >= sh.gstart[h] ? h : g;
+            const SortedTok st =
+                a.sorted[((int64_t)b * a.groups + g) * a.gslots + sh.goff[g] + (e - sh.gstart[g])];
+            key[r] = st.packed;
+            gum[r] = st.g;
+            mass[r] = topk ? 0ull : mass_fixed(value_of(st.packed), (double)M, sh.tab);
+            vlo = min(vlo, (uint32_t)(st.packed >> 32));
+            vhi = max(vhi, (uint32_t)(st.packed >> 32));
+        }
     }
-    // Each token against every token of the bin, read across lanes: top-k
-    // counts the larger packed keys (rank inside the bin: k - aux), nucleus
-    // adds the masses of strictly larger values (A = aux from the bins
-    // before).
+    // Up to 16 tokens are compared directly.  Above that the bin's value
+    // range is cut into 64 sub-ranges, lane l owning the (63 - l)-th so that
+    // lanes run from the largest values down; their counts (and masses) in
+    // LDS locate the sub-range holding the cut, and only its tokens are
+    // compared one by one.  Tied values share a sub-range.
+    const bool small = n <= 16u;
+    uint32_t sub[kWPer] = {};
+    uint32_t sel = 0;
+    unsigned long long base = topk ? 0ull : aux;   // top-k: tokens in the sub-ranges above; nucleus: A plus their mass
+    if (!small) {
+        vlo = ~wave_max_t(~vlo);
+        vhi = wave_max_t(vhi);
+        const unsigned long long span = (unsigned long long)(vhi - vlo) + 1;
+        sh.wcnt[lane] = 0;
+        sh.wmass[lane] = 0;
+        wave_lds_sync();
+#pragma unroll
+        for (int r = 0; r < kWPer; ++r) {
+            if ((uint32_t)(lane + 64 * r) < n) {
+                sub[r] = (uint32_t)(((unsigned long long)((uint32_t)(key[r] >> 32) - vlo) * 64) / span);
+                atomicAdd(&sh.wcnt[sub[r]], 1u);
+                if (!topk) atomicAdd(&sh.wmass[sub[r]], mass[r]);
+            }
+        }
+        wave_lds_sync();
+        const uint32_t cnt = sh.wcnt[63 - lane];
+        if (topk) {
+            const uint32_t rank = k - (uint32_t)aux;
+            const uint32_t before = wave_scan_incl(cnt) - cnt;
+            const unsigned long long bal = __ballot(before < rank && rank <= before + cnt);
+            const int src = bal ? __ffsll((long long)bal) - 1 : 0;   // (one lane: rank <= n)
+            sel = 63u - (uint32_t)src;
+            base = readlane_t(before, src);
+        } else {
+            const unsigned long long ms = sh.wmass[63 - lane];
+            const unsigned long long before = wave_scan_incl(ms) - ms;
+            // the deepest non-empty sub-range whose strictly-greater mass fits
+            // (the bin's top token always fits: its strictly-greater mass is A)
+            const unsigned long long bal = __ballot(cnt != 0u && (double)(aux + before) <= limit);
+            const int src = bal ? 63 - __clzll((long long)bal) : 0;
+            sel = 63u - (uint32_t)src;
+            base = aux + readlane_t(before, src);
+        }
+    }
+    // the chosen sub-range's tokens, compacted into LDS records (top-k: the
+    // packed key; nucleus: the value key and the mass)
+    uint32_t m = 0;
+    bool in[kWPer];
+#pragma unroll
+    for (int r = 0; r < kWPer; ++r) in[r] = (uint32_t)(lane + 64 * r) < n && (small || sub[r] == sel);
+    if (!small) {
+#pragma unroll
+        for (int r = 0; r < kWPer; ++r) {
+            const unsigned long long bal = __ballot(in[r]);
+            const uint32_t pos = m + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (in[r]) sh.crec[pos] = topk ? CandRec{key[r], 0ull} : CandRec{key[r] >> 32, mass[r]};
+            m += (uint32_t)__popcll(bal);
+        }
+        wave_lds_sync();
+    }
+    // each of them against every token of the sub-range (every lane reads
+    // the same record: a broadcast), eight records in flight; a small bin's
+    // tokens against each other through cross-lane reads
+    uint32_t larger[kWPer] = {};
+    unsigned long long above[kWPer] = {};
+    uint32_t j = 0;
+    auto visit = [&](const CandRec &rc) {
+#pragma unroll
+        for (int r = 0; r < kWPer; ++r) {
+            if (topk)
+                larger[r] += rc.a > key[r] ? 1u : 0u;
+            else
+                above[r] += rc.a > (key[r] >> 32) ? rc.b : 0ull;
+        }
+    };
+    if (small) {   // one token per lane (lane < n), read across lanes
+        for (; j < n; ++j) {
+            if (topk) {
+                larger[0] += readlane_t(key[0], (int)j) > key[0] ? 1u : 0u;
+            } else {
+                const uint32_t vj = readlane_t((uint32_t)(key[0] >> 32), (int)j);
+                above[0] += vj > (uint32_t)(key[0] >> 32) ? readlane_t(mass[0], (int)j) : 0ull;
+            }
+        }
+    } else {
+        for (; j + 8 <= m; j += 8) {
+            CandRec rc[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) rc[u] = sh.crec[j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) visit(rc[u]);
+        }
+        for (; j < m; ++j) visit(sh.crec[j]);
+    }
     unsigned long long kpack = 0;
     uint32_t tau = 0;
     if (topk) {
-        uint32_t larger = 0;
-        for (uint32_t j = 0; j < n; ++j) larger += readlane_t(key, (int)j) > key ? 1u : 0u;
-        const uint32_t rank = k - (uint32_t)aux;
-        kpack = wave_max_t(real && larger + 1 == rank ? key : 0ull);   // (exactly one token has that rank)
+        const uint32_t rank_in = k - (uint32_t)aux - (uint32_t)base;
+        unsigned long long pick = 0;
+#pragma unroll
+        for (int r = 0; r < kWPer; ++r)
+            if (in[r] && larger[r] + 1 == rank_in) pick = key[r];
+        kpack = wave_max_t(pick);   // (exactly one token has that rank)
     } else {
-        const uint32_t vk = (uint32_t)(key >> 32);
-        unsigned long long above = 0;
-        for (uint32_t j = 0; j < n; ++j) {
-            const uint32_t vj = readlane_t(vk, (int)j);
-            const unsigned long long mj = readlane_t(mass, (int)j);
-            above += vj > vk ? mj : 0ull;
-        }
         // the smallest qualifying value: a max over complemented keys
-        const bool fits = real && (double)(aux + above) <= limit;
-        tau = ~wave_max_t(fits ? ~vk : 0u);
+        uint32_t nk = 0;
+#pragma unroll
+        for (int r = 0; r < kWPer; ++r)
+            if (in[r] && (double)(base + above[r]) <= limit) nk = max(nk, ~(uint32_t)(key[r] >> 32));
+        tau = ~wave_max_t(nk);
     }
     // the best of the bins before jc and of bin jc's kept tokens
     unsigned long long best = lane == 0 ? sh.up : 0ull;
-    if (real && (topk ? key >= kpack : (uint32_t)(key >> 32) >= tau))
-        best = max(best, pack_key_index(float_key(value_of(key) + gum), unpack_index(key)));
+#pragma unroll
+    for (int r = 0; r < kWPer; ++r) {
+        const unsigned long long v = key[r];
+        if ((uint32_t)(lane + 64 * r) < n && (topk ? v >= kpack : (uint32_t)(v >> 32) >= tau))
+            best = max(best, pack_key_index(float_key(value_of(v) + gum[r]), unpack_index(v)));
+    }
     best = wave_max_t(best);
     if (lane == 0) {
         a.out_ids[b] = (int32_t)unpack_index(best);
