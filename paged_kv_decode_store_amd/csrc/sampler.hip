@@ -565,16 +565,31 @@ __device__ __forceinline__ uint32_t in_chunk_bits(int i0, int i1, int per)
 
 // What a row needs, from its own settings: 0 < k < V turns top-k on, p < 1
 // the nucleus (p <= 0: the maxima only), T <= 0 (or NaN) means greedy.
-__device__ __forceinline__ uint32_t row_mode(const SampArgs &a, int b)
+struct RowSettings {
+    uint32_t mode;
+    int32_t k;
+    float p;
+};
+
+__device__ __forceinline__ RowSettings row_settings(const SampArgs &a, int b)
 {
     const float T = a.temperature[b];
-    if (!(T > 0.f)) return MODE_GREEDY;
     const int32_t k = a.top_k[b];
     const float p = a.top_p[b];
     uint32_t mode = 0;
-    if (k > 0 && k < a.vocab) mode |= MODE_TOPK;
-    if (p < 1.f) mode |= (p > 0.f) ? MODE_TOPP : MODE_TOPP_MAX;
-    return mode ? mode : MODE_PLAIN;
+    if (!(T > 0.f)) {
+        mode = MODE_GREEDY;
+    } else {
+        if (k > 0 && k < a.vocab) mode |= MODE_TOPK;
+        if (p < 1.f) mode |= (p > 0.f) ? MODE_TOPP : MODE_TOPP_MAX;
+        if (!mode) mode = MODE_PLAIN;
+    }
+    return RowSettings{mode, k, p};
+}
+
+__device__ __forceinline__ uint32_t row_mode(const SampArgs &a, int b)
+{
+    return row_settings(a, b).mode;
 }
 
 // ---- scan ------------------------------------------------------------------
@@ -1684,12 +1699,13 @@ constexpr int kWBins = kHBins / 64;        // bins per lane of that wave
 static_assert(kHBins % 64 == 0 && kWaveCand <= kCand, "wave fast path shape");
 
 __device__ __forceinline__ bool one_pass_draw(const SampArgs &a, FinishShared &sh, const BinRec (&grp)[kGroups],
-                                              int b, uint32_t mode, uint32_t kmax, unsigned long long Z)
+                                              int b, const RowSettings &rs, uint32_t kmax, unsigned long long Z)
 {
+    const uint32_t mode = rs.mode;
     const float M = key_float(kmax);
     const bool topk = (mode & MODE_TOPK) != 0;
-    const uint32_t k = topk ? (uint32_t)a.top_k[b] : 0u;
-    const double limit = topk ? 0.0 : (double)a.top_p[b] * (double)Z;
+    const uint32_t k = topk ? (uint32_t)rs.k : 0u;
+    const double limit = topk ? 0.0 : (double)rs.p * (double)Z;
     if (threadIdx.x < 64) {
         const int lane = (int)threadIdx.x;
         const int d0 = lane * kWBins;
@@ -1954,7 +1970,8 @@ __global__ __launch_bounds__(kFThreads) void samp_finish_kernel(const SampArgs a
 {
     __shared__ FinishShared sh;
     const int b = blockIdx.x;
-    const uint32_t mode = row_mode(a, b);
+    const RowSettings rs = row_settings(a, b);   // (read once, before any barrier)
+    const uint32_t mode = rs.mode;
     const ChunkRec *rec = a.rec + (int64_t)b * a.nchunks;
     const int nch = a.nchunks;
     if (mode & (MODE_GREEDY | MODE_PLAIN)) {
@@ -2028,10 +2045,10 @@ __global__ __launch_bounds__(kFThreads) void samp_finish_kernel(const SampArgs a
     const double M = (double)Mf;
     // The lists hold every token above T*; the cut must lie above T*.
     bool ok;
-    if (mode & MODE_TOPK) ok = tot.nu >= (uint32_t)a.top_k[b];
-    else if (mode & MODE_TOPP) ok = (double)tot.mu > (double)a.top_p[b] * (double)tot.Z;
+    if (mode & MODE_TOPK) ok = tot.nu >= (uint32_t)rs.k;
+    else if (mode & MODE_TOPP) ok = (double)tot.mu > (double)rs.p * (double)tot.Z;
     else ok = tout < kmax;   // p <= 0: every maximum must be above T*
-    if (ok && single && one_pass_draw(a, sh, grp, b, mode, kmax, tot.Z)) return;
+    if (ok && single && one_pass_draw(a, sh, grp, b, rs, kmax, tot.Z)) return;
     if (ok) {
         if (use_hist) {   // the lists' sizes (rows without a histogram have them)
             for (int c = threadIdx.x; c < nch; c += kFThreads) sh.nlist[c] = rec[c].n;
