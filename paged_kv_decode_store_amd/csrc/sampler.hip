@@ -568,7 +568,7 @@ __device__ __forceinline__ uint32_t in_chunk_bits(int i0, int i1, int per)
 struct RowSettings {
     uint32_t mode;
     int32_t k;
-    float p;
+    float p, T;
 };
 
 __device__ __forceinline__ RowSettings row_settings(const SampArgs &a, int b)
@@ -584,7 +584,7 @@ __device__ __forceinline__ RowSettings row_settings(const SampArgs &a, int b)
         if (p < 1.f) mode |= (p > 0.f) ? MODE_TOPP : MODE_TOPP_MAX;
         if (!mode) mode = MODE_PLAIN;
     }
-    return RowSettings{mode, k, p};
+    return RowSettings{mode, k, p, T};
 }
 
 __device__ __forceinline__ uint32_t row_mode(const SampArgs &a, int b)
@@ -606,8 +606,9 @@ __device__ __forceinline__ int elem_index(int i0, int j)
 // chunk lies inside the row (no per-element range checks).
 template <bool VEC4, bool MASK, int PER, bool FULL>
 __device__ __forceinline__ void scan_chunk(const SampArgs &a, Tile<VEC4> &t, int b, int c, int i0,
-                                           int i1, uint32_t mode)
+                                           int i1, const RowSettings &rs)
 {
+    const uint32_t mode = rs.mode;
     __shared__ unsigned long long s_red[kThreads / 64];
     __shared__ uint32_t s_cnt[kBins];
     __shared__ uint32_t s_wkey[kThreads / 64];
@@ -627,7 +628,7 @@ __device__ __forceinline__ void scan_chunk(const SampArgs &a, Tile<VEC4> &t, int
                 if (in(j)) best = max(best, pack_key_index(float_key(t.raw(j)), (uint32_t)elem_index<VEC4>(i0, j)));
         } else {
             // every token is eligible: stream the noise too
-            const Scaler sc(a.temperature[b]);
+            const Scaler sc(rs.T);
             Tile<VEC4> gt;
             gt.template load_range<0, PER>(a.gumbel + (int64_t)b * a.gstride, i0, i1, PER);
 #pragma unroll
@@ -651,8 +652,7 @@ __device__ __forceinline__ void scan_chunk(const SampArgs &a, Tile<VEC4> &t, int
     // meaning).
     for (int d = threadIdx.x; d < kBins; d += kThreads) s_cnt[d] = 0;
     if (threadIdx.x == 0) s_nlist = 0;
-    const float T = a.temperature[b];
-    const Scaler sc(T);
+    const Scaler sc(rs.T);
     // s = z / T by the double product for every element; a wave that holds
     // a logit small enough for a subnormal tie redoes those by division
     unsigned long long tiny = 0;
@@ -715,7 +715,7 @@ __device__ __forceinline__ void scan_chunk(const SampArgs &a, Tile<VEC4> &t, int
         for (int w = 0; w < wave; ++w) cum += s_wtot[w];
         const uint32_t cap = (uint32_t)a.cap;
         uint32_t need = cap;                               // nucleus: as many as fit
-        if (mode & MODE_TOPK) need = min((uint32_t)a.top_k[b], cap);
+        if (mode & MODE_TOPK) need = min((uint32_t)rs.k, cap);
         else if (mode & MODE_TOPP_MAX) need = 1;
         int fit = 0, nd = kBins;
 #pragma unroll
@@ -832,11 +832,11 @@ __global__ __launch_bounds__(kThreads) void samp_scan_kernel(const SampArgs a)
     Tile<VEC4> t;
     t.template load_range<0, PER, true>(a.logits + (int64_t)b * a.lstride, i0, i1, PER);
     t.load_mask(MASK ? a.mask + (int64_t)b * a.mstride : nullptr, i0, i1, PER);
-    const uint32_t mode = row_mode(a, b);
+    const RowSettings rs = row_settings(a, b);
     if (i1 - i0 == PER * kThreads)
-        scan_chunk<VEC4, MASK, PER, true>(a, t, b, c, i0, i1, mode);
+        scan_chunk<VEC4, MASK, PER, true>(a, t, b, c, i0, i1, rs);
     else
-        scan_chunk<VEC4, MASK, PER, false>(a, t, b, c, i0, i1, mode);
+        scan_chunk<VEC4, MASK, PER, false>(a, t, b, c, i0, i1, rs);
 }
 
 // ---- histogram -------------------------------------------------------------
@@ -2006,8 +2006,8 @@ __global__ __launch_bounds__(kFThreads) void samp_finish_kernel(const SampArgs a
         if (threadIdx.x < 64) sh.tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
         kmax = t0.kmax;
         tout = t0.tout;
-        __syncthreads();
-        // the groups' bins and totals added up
+        // the groups' bins and totals added up (the totals once the barrier
+        // below has made them visible)
         const bool in = (int)threadIdx.x < bins_above(tout, key_float(kmax));
         uint32_t cnt = 0;
         unsigned long long mass = 0;
@@ -2024,12 +2024,12 @@ __global__ __launch_bounds__(kFThreads) void samp_finish_kernel(const SampArgs a
         }
         sh.bcnt[threadIdx.x] = cnt;
         sh.bmass[threadIdx.x] = mass;
+        __syncthreads();
         for (int g = 0; g < a.groups; ++g) {
             tot.Z += sh.gtot[g].Z;
             tot.mu += sh.gtot[g].mu;
             tot.nu += sh.gtot[g].nu;
         }
-        __syncthreads();
     } else {
         uint32_t km = 0, to = 0;
         for (int c = threadIdx.x; c < nch; c += kFThreads) {
