@@ -414,20 +414,26 @@ __device__ __forceinline__ T dpp_shift_t(T v)   // lanes with no source read 0
 // Inclusive sum over the lanes of a wave in ascending order: row shifts by
 // 1, 2, 4 and 8 within each row of 16 lanes, then the rows' totals read as
 // scalars.  Every lane of the wave must be active.
-template <typename T>
-__device__ __forceinline__ T wave_scan_incl(T v)
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_scan_op(T v, Op op)   // (op(x, 0) = x)
 {
-    v += dpp_shift_t<0x111>(v);   // row_shr:1
-    v += dpp_shift_t<0x112>(v);   // row_shr:2
-    v += dpp_shift_t<0x114>(v);   // row_shr:4
-    v += dpp_shift_t<0x118>(v);   // row_shr:8
+    v = op(v, dpp_shift_t<0x111>(v));   // row_shr:1
+    v = op(v, dpp_shift_t<0x112>(v));   // row_shr:2
+    v = op(v, dpp_shift_t<0x114>(v));   // row_shr:4
+    v = op(v, dpp_shift_t<0x118>(v));   // row_shr:8
     const T r0 = readlane_t(v, 15), r1 = readlane_t(v, 31), r2 = readlane_t(v, 47);
     const int lane = threadIdx.x & 63;
     T add = 0;
-    if (lane >= 16) add += r0;
-    if (lane >= 32) add += r1;
-    if (lane >= 48) add += r2;
-    return v + add;
+    if (lane >= 16) add = op(add, r0);
+    if (lane >= 32) add = op(add, r1);
+    if (lane >= 48) add = op(add, r2);
+    return op(v, add);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_scan_incl(T v)
+{
+    return wave_scan_op(v, [](T x, T y) { return x + y; });
 }
 
 template <typename T, int NT, bool REV = false>
@@ -978,17 +984,9 @@ __global__ __launch_bounds__(kHThreads) void samp_hist_kernel(const SampArgs a)
         csum += cnt[j];
         cmax = max(cmax, bst[j]);
     }
-    uint32_t isum = csum;
-    unsigned long long imax = cmax;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t us = (uint32_t)__shfl_up((int)isum, (unsigned)o);
-        const unsigned long long um = __shfl_up(imax, (unsigned)o);
-        if (lane >= o) {
-            isum += us;
-            imax = max(imax, um);
-        }
-    }
+    const uint32_t isum = wave_scan_incl(csum);
+    const unsigned long long imax =
+        wave_scan_op(cmax, [](unsigned long long x, unsigned long long y) { return max(x, y); });
     __shared__ unsigned long long s_wmax[kHThreads / 64];
     if (lane == 63) {   // (s_red is free: its last use was behind a barrier)
         s_red[wave] = isum;
@@ -1001,9 +999,14 @@ __global__ __launch_bounds__(kHThreads) void samp_hist_kernel(const SampArgs a)
         const unsigned long long prev = __shfl_up(imax, 1u);
         rmax = lane > 0 ? prev : 0ull;
     }
-    for (int w = 0; w < wave; ++w) {
-        run += (uint32_t)s_red[w];
-        rmax = max(rmax, s_wmax[w]);
+#pragma unroll
+    for (int w = 0; w < kHThreads / 64; ++w) {   // (all reads issued together)
+        const uint32_t ws = (uint32_t)s_red[w];
+        const unsigned long long wm = s_wmax[w];
+        if (w < wave) {
+            run += ws;
+            rmax = max(rmax, wm);
+        }
     }
     const int nb = bins_above(tout, Mf);
     const int64_t part = (int64_t)b * a.groups + g;
