@@ -131,8 +131,11 @@ def kv_store(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
 
 def decode_split_tokens(batch: int, num_q_heads: int, num_kv_heads: int, max_context_len: int,
                         split_tokens: int = 0) -> int:
-    return int(lib().pkv_decode_split_tokens(batch, num_q_heads, num_kv_heads, max_context_len,
-                                             split_tokens))
+    s = int(lib().pkv_decode_split_tokens(batch, num_q_heads, num_kv_heads, max_context_len,
+                                          split_tokens))
+    if s == 0 and split_tokens != 0:   # the library answers 0 for a split it rejects
+        raise _lib.PkvError(_lib.PKV_ERR_INVALID_ARG, "pkv_decode_split_tokens")
+    return s
 
 
 def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

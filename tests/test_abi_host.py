@@ -11,6 +11,7 @@ import re
 
 import pytest
 
+import paged_kv_decode_store_amd as pkv
 from paged_kv_decode_store_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -139,6 +140,11 @@ def test_workspace_and_split_queries():
         assert s >= 64 and s % 64 == 0
         assert L.pkv_decode_split_tokens(B, Hq, Hkv, ml, 128) == 128
     assert L.pkv_decode_split_tokens(4, 4, 4, 100, 100) == 0  # not a multiple of 64
+    # the binding turns that 0 into an error instead of passing it on (where
+    # 0 would mean the automatic split)
+    with pytest.raises(_lib.PkvError):
+        pkv.decode_split_tokens(64, 16, 8, 4096, 288)
+    assert pkv.decode_split_tokens(64, 16, 8, 4096, 320) == 320
     # workspace: [B][Hq][S][D] + [B][Hq][S][2] fp32, each 256-byte aligned
     B, Hq, Hkv, D, ml, split = 3, 4, 2, 64, 1000, 128
     S = (ml + split - 1) // split
