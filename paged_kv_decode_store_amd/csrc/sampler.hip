@@ -1077,7 +1077,7 @@ constexpr int kSubCand = 256;     // ... and candidates of one sub-range compare
 static_assert(kCand <= kFThreads, "cand_rank / cand_cut need a lane per candidate");
 constexpr int kBatch = 8;     // list entries per thread whose loads are issued together
 
-constexpr int kWaveCandMax = 256;  // cut-bin tokens one wave resolves (four per lane)
+constexpr int kWaveCand = 256;     // cut-bin tokens one wave resolves (four per lane)
 constexpr int kCutBins = 2048;   // the radix cut's widest level: 11 bits
 
 // A token of a cut bin resolved by one wave (top-k: a = packed key;
@@ -1095,7 +1095,7 @@ struct FinishShared {
     unsigned long long ckey[kCand];       // one bin's tokens: packed keys ...
     unsigned long long cmass[kCand];      // ... masses
     float cgum[kCand];                    // ... and noise (one-pass draw)
-    CandRec crec[kWaveCandMax];           // a cut bin resolved by one wave: its
+    CandRec crec[kWaveCand];              // a cut bin resolved by one wave: its
     uint32_t wcnt[64];                    // sub-ranges' counts and masses, and the
     unsigned long long wmass[64];         // chosen sub-range's tokens (crec)
     RowTot gtot[kGroups];                 // the histogram groups' totals
@@ -1679,14 +1679,6 @@ __device__ __forceinline__ void select_and_draw(const SampArgs &a, FinishShared 
     }
 }
 
-// Fast path of a row with one filter (top-k or nucleus): wave 0 finds the
-// cut bin from the summed bins (16 per lane, a wave scan), the thread of
-// that bin publishes where the bin's tokens lie in each group, and wave 0
-// alone resolves the bin's tokens (at most kWaveCand) and draws, with no
-// block-wide barrier after the publication (a larger bin, up to kCand
-// tokens, is resolved by the whole workgroup).  False (the same in every
-// thread) when the bin is empty or holds more than kCand tokens; then
-// nothing has been written.
 // The calling wave's LDS writes are complete before its later reads (LDS
 // serves one wave's instructions in order): a wave-scope fence pair.
 __device__ __forceinline__ void wave_lds_sync()
@@ -1696,10 +1688,18 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-constexpr int kWaveCand = kWaveCandMax;
-constexpr int kWPer = kWaveCand / 64;      // tokens per lane
+constexpr int kWPer = kWaveCand / 64;      // tokens per lane of the resolving wave
 constexpr int kWBins = kHBins / 64;        // bins per lane of that wave
-static_assert(kHBins % 64 == 0 && kWaveCand <= kCand, "wave fast path shape");
+static_assert(kHBins % 64 == 0 && kWaveCand % 64 == 0 && kWaveCand <= kCand, "wave fast path shape");
+
+// Fast path of a row with one filter (top-k or nucleus): wave 0 finds the
+// cut bin from the summed bins (16 per lane, a wave scan), the thread of
+// that bin publishes where the bin's tokens lie in each group, and wave 0
+// alone resolves the bin's tokens (at most kWaveCand) and draws, with no
+// block-wide barrier after the publication (a larger bin, up to kCand
+// tokens, is resolved by the whole workgroup).  False (the same in every
+// thread) when the bin is empty or holds more than kCand tokens; then
+// nothing has been written.
 
 __device__ __forceinline__ bool one_pass_draw(const SampArgs &a, FinishShared &sh, const BinRec (&grp)[kGroups],
                                               int b, const RowSettings &rs, uint32_t kmax, unsigned long long Z)
