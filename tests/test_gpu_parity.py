@@ -526,3 +526,46 @@ def test_sampler_maximum_vocab(B, V):
     bad, amb, infos = _sample_and_compare(z, g, t, p, k)
     assert not bad, bad
     assert amb == 0
+
+
+@pytest.mark.parametrize("n", [1, 16, 17, 63, 64, 65, 200, 256, 257, 300])
+def test_sampler_cut_bin_sizes_and_ties(n):
+    """Rows whose cut bin (1/32 of a unit below the row max) holds exactly n
+    tokens, with pairs of tied values among them: up to 16 are resolved by
+    one wave directly, up to 256 by one wave through value sub-ranges, more
+    by the whole workgroup.  One top-k row (rank in the middle of the bin
+    and on a tie) and one nucleus row per size; p sits halfway between two
+    strictly-greater-mass levels, so no row is near a boundary."""
+    rng = np.random.default_rng(7000 + n)
+    V = 40000
+    rows, ks, ps = [], [], []
+    for kind in ("topk", "topk_tie", "nucleus"):
+        z = np.minimum(rng.standard_normal(V), 4.0).astype(np.float32)
+        idx = rng.choice(V, n + 1, replace=False)
+        z[idx[0]] = 10.0                                     # the row max
+        u = rng.uniform(0.05, 0.95, n)
+        u[1::2] = u[0::2][:n // 2]                           # pairs of equal values
+        z[idx[1:]] = (10.0 - (10.0 + u) / 32.0).astype(np.float32)   # all in bin 10
+        rows.append(z)
+        vals = np.sort(z[idx[1:]].astype(np.float64))[::-1]
+        if kind == "topk":
+            ks.append(1 + max(1, n // 2)); ps.append(1.0)
+        elif kind == "topk_tie":
+            j = int(np.flatnonzero(vals[:-1] == vals[1:])[0]) if n > 1 else 0
+            ks.append(1 + j + 1); ps.append(1.0)             # rank on the first of a tie pair
+        else:
+            s64 = z.astype(np.float64)
+            Z = np.exp(s64 - 10.0).sum()
+            distinct = np.unique(vals)[::-1]                 # descending distinct values
+            above = [1.0 + np.exp(vals[vals > v] - 10.0).sum() for v in distinct]
+            j = len(distinct) // 2
+            hi = above[j + 1] if j + 1 < len(above) else above[j] + np.exp(distinct[j] - 10.0)
+            ks.append(0); ps.append(float((above[j] + hi) / 2.0 / Z))
+    z = np.stack(rows)
+    B = z.shape[0]
+    g = rng.gumbel(size=(B, V)).astype(np.float32)
+    t = np.ones(B, np.float32)
+    say(f"sampler cut bin of {n} tokens")
+    bad, amb, infos = _sample_and_compare(z, g, t, np.array(ps, np.float32), np.array(ks, np.int32))
+    assert not bad, bad
+    assert amb == 0
