@@ -61,7 +61,7 @@ constexpr int kBins = 512;              // scan: value bins below the chunk max 
 constexpr float kBinsPerUnit = 8.f;     // ... 1/8 of a logit unit wide
 constexpr float kHBinsPerUnit = 32.f;   // finish-side bins: 1/32 of a unit
 constexpr int kMaxPer = 16;             // logits per thread per chunk (more: register spills)
-constexpr int kMinGroups = 256;         // scan workgroups wanted (one per CU)
+constexpr int kMinGroups = 512;         // scan workgroups wanted (two per CU)
 constexpr int kListDiv = 8;             // list capacity per chunk: chunk / kListDiv
 constexpr int kMaxChunks = 4096;        // vocab <= 2^24 in chunks of 4096
 constexpr int kDigits = 4096;           // radix digits per level (<= 12 bits)
