@@ -117,8 +117,9 @@ __device__ __forceinline__ int load_block_id(const int32_t *table, int j)
 __device__ __forceinline__ uint32_t float_key(float f)
 {
     f = f + 0.0f;
-    uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f);
+    // negative: all bits flipped; otherwise the sign bit set
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float key_float(uint32_t k)
