@@ -244,8 +244,8 @@ __device__ __forceinline__ int hbin_of(float s, float M)
 // the fp32 exponential.  0 below 2^-200 (and for NaN).
 __device__ __forceinline__ float mass_approx(float s, double M)
 {
-    const double x = ((double)s - M) * 1.4426950408889634;
-    if (!(x > -200.0)) return 0.f;
+    // (-inf and NaN clamp to -200 too; 2^-200 and below round to 0 in fp32)
+    const double x = fmax(((double)s - M) * 1.4426950408889634, -200.0);
     const double fl = floor(x);
     return ldexpf(__builtin_amdgcn_exp2f((float)(x - fl)), (int)fl);
 }
